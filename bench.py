@@ -1,0 +1,282 @@
+"""Benchmark of the mixed-head attention hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic sequence of the workload:
+head regrouping (handle init), every prefill chunk (append/evict, retrieval causal
+attention, streaming sink + window attention) and every decode step (append/evict,
+split-K retrieval decode + streaming decode + merge).  Inputs (Q, K, V for every
+position) are generated on the device before timing and stay resident in HBM.
+
+Default workload: Llama-2-7B-shaped MHA layer (32 heads, head_dim 128, bf16, 8 of 32
+heads retrieval, sink 64 + recent 256), 32768-token prefill in 4096-token chunks, then
+128 decode steps.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DuoAttn layer decode µs/step & prefill tok/s at context L; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def esize(w):
+    return 4 if w.io_dtype == "f32" else 2
+
+
+def decode_bytes(w, t):
+    """Algorithmic HBM bytes of one decode-attention launch at query position t, one
+    layer: K+V of every visible key counted once per KV head (GQA sharing), plus Q and O.
+    int4 vectors cost 64 code bytes + 4 bytes of scale/zero."""
+    mask = w.mask(0)
+    nr = int(mask.sum())
+    ns = w.n_kv_heads - nr
+    vec = 68 if w.kv_format == "int4" else w.head_dim * esize(w)
+    kv = 2 * vec * (nr * (t + 1) + ns * min(t + 1, w.sink + w.recent))
+    qo = 2 * w.n_q_heads * w.head_dim * esize(w)
+    return kv + qo
+
+
+def prefill_flops(w, t0, T, retrieval=True):
+    """Algorithmic flops of one prefill chunk [t0, t0+T): 4*D per visible (query, key)
+    pair (QK^T and PV), retrieval heads over causal pairs, streaming heads over
+    min(i+1, sink+recent) pairs."""
+    mask = w.mask(0)
+    G = w.group
+    if retrieval:
+        pairs = T * t0 + T * (T + 1) // 2
+        return 4 * w.head_dim * pairs * int(mask.sum()) * G
+    cap = w.sink + w.recent
+    pairs = sum(min(i + 1, cap) for i in range(t0, t0 + T))
+    return 4 * w.head_dim * pairs * int((~mask).sum()) * G
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    io = B.DUO_DTYPE_F32 if w.io_dtype == "f32" else B.DUO_DTYPE_BF16
+    tdt = torch.float32 if w.io_dtype == "f32" else torch.bfloat16
+    has_prefill = w.prefill_chunk > 0
+    if not has_prefill:
+        raise SystemExit("bench.py times workloads with a chunked prefill; decode-only stacks use --workload with prefill")
+    total = w.context + w.decode_steps
+    chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
+    if sum(chunks) < w.context:
+        chunks.append(w.context - sum(chunks))
+
+    def synth(kind, H):
+        t = torch.empty((total, H, w.head_dim), dtype=tdt, device=dev)
+        B.duo_synth_fill(t, io, w.seed, I.KIND_STREAM[kind], 0, t.numel())
+        return t
+
+    Q, K, V = synth("q", w.n_q_heads), synth("k", w.n_kv_heads), synth("v", w.n_kv_heads)
+    out_pre = torch.empty((max(chunks), w.n_q_heads, w.head_dim), dtype=tdt, device=dev)
+    out_dec = torch.empty((w.n_q_heads, w.head_dim), dtype=tdt, device=dev)
+    cfg = B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent, w.max_context,
+                        io, B.DUO_KV_INT4_G128 if w.kv_format == "int4" else B.DUO_KV_SAME_AS_IO,
+                        w.masks().astype(np.uint8))
+    ws = torch.empty(B.duo_kv_bytes(cfg), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    handles = []
+
+    def step(profile=False):
+        h = B.duo_kv_init(cfg, ws)
+        handles.append(h)
+        if profile:
+            B.duo_profile_enable(h, True)
+        t = 0
+        for T in chunks:
+            B.duo_prefill(h, 0, Q[t:t + T], K[t:t + T], V[t:t + T], T, out_pre)
+            t += T
+        for _ in range(w.decode_steps):
+            B.duo_decode(h, 0, Q[t], K[t], V[t], out_dec)
+            t += 1
+        return h
+
+    for _ in range(args.warmup):
+        B.duo_kv_free(step())
+        handles.pop()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    totals = {c: [0.0, 0] for c in B.KERNEL_CLASSES}
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(profile=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    for h in handles:
+        for c, (ms, n) in B.duo_profile_collect(h).items():
+            totals[c][0] += ms
+            totals[c][1] += n
+        B.duo_kv_free(h)
+    handles.clear()
+    ms_per_step = ms_total / args.steps
+
+    tokens = w.context + w.decode_steps
+    # component figures (per step)
+    dec_ms = totals["decode"][0] / args.steps
+    app_ms = totals["append"][0] / args.steps
+    pre_r_ms = totals["prefill_retrieval"][0] / args.steps
+    pre_s_ms = totals["prefill_streaming"][0] / args.steps
+
+    # algorithmic work per step
+    dec_bytes = sum(decode_bytes(w, t) for t in range(w.context, total))
+    fl_r = fl_s = 0
+    t = 0
+    for T in chunks:
+        fl_r += prefill_flops(w, t, T, True)
+        fl_s += prefill_flops(w, t, T, False)
+        t += T
+
+    rooflines = []
+    if totals["decode"][1]:
+        a = dec_bytes / (dec_ms * 1e-3) / 1e9
+        rooflines.append({"kernel": "decode_attention", "bound": "hbm", "achieved": round(a, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                          "avg_launch_us": round(dec_ms * 1e3 / w.decode_steps, 3), "ms_per_step": round(dec_ms, 4),
+                          "traffic": None})
+    if totals["prefill_retrieval"][1]:
+        fl = fl_r if totals["prefill_streaming"][1] else fl_r + fl_s
+        a = fl / (pre_r_ms * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if w.io_dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+        rooflines.append({"kernel": "prefill_retrieval_attention", "bound": "mfma", "achieved": round(a, 2),
+                          "peak": peak, "unit": "TFLOP/s", "frac": round(a / peak, 4),
+                          "avg_launch_us": round(pre_r_ms * 1e3 / len(chunks), 2), "ms_per_step": round(pre_r_ms, 4),
+                          "traffic": None})
+    if totals["prefill_streaming"][1]:
+        a = fl_s / (pre_s_ms * 1e-3) / 1e12
+        rooflines.append({"kernel": "prefill_streaming_attention", "bound": "mfma", "achieved": round(a, 2),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "avg_launch_us": round(pre_s_ms * 1e3 / len(chunks), 2), "ms_per_step": round(pre_s_ms, 4),
+                          "traffic": None})
+    dominant = max(rooflines, key=lambda r: r["ms_per_step"]) if rooflines else None
+
+    prefill_ms = pre_r_ms + pre_s_ms + app_ms * len(chunks) / max(1, len(chunks) + w.decode_steps)
+    res = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": 1, "seq_len": w.context, "decode_steps": w.decode_steps,
+                   "prefill_chunk": w.prefill_chunk, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "retrieval_kv_heads": int(w.mask(0).sum()), "sink": w.sink,
+                   "recent": w.recent, "kv_format": w.kv_format, "parallelism": "single_gpu"},
+        "components": {
+            "decode_us_per_step": round(dec_ms * 1e3 / w.decode_steps, 3),
+            "decode_append_plus_attention_us_per_step": None,
+            "prefill_tok_s": round(w.context / (prefill_ms * 1e-3), 1) if prefill_ms > 0 else None,
+            "kernel_ms_per_step": {c: round(totals[c][0] / args.steps, 4) for c in totals},
+            "kernel_launches_per_step": {c: totals[c][1] // args.steps for c in totals},
+            "wall_s": round(wall, 3),
+        },
+        "roofline": dominant,
+        "roofline_all": rooflines,
+        "cpu_baseline": None,
+    }
+    # decode step including its append, from the decode-phase share of append launches
+    n_app = totals["append"][1] / args.steps
+    if n_app:
+        per_app = app_ms / n_app
+        res["components"]["decode_append_plus_attention_us_per_step"] = round(
+            (dec_ms / w.decode_steps + per_app) * 1e3, 3)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, total, args.cpu_seconds)
+    return res
+
+
+def cpu_baseline(w, total, budget_s):
+    """The oracle on the host cores over a bounded, uniformly random sample of the step's
+    rows (prefill positions and decode positions alike, all heads), scaled to the whole
+    step by the row count.  Input generation is excluded from the timing."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixed_head_kv_amd import inputs as I
+    from oracle import attention as OA
+
+    t_gen = time.perf_counter()
+    K = OA.upcast(I.synth(w.seed, 0, "k", 0, total, w.n_kv_heads, w.head_dim, w.io_dtype), w.io_dtype)
+    V = OA.upcast(I.synth(w.seed, 0, "v", 0, total, w.n_kv_heads, w.head_dim, w.io_dtype), w.io_dtype)
+    log(f"cpu_baseline: host inputs generated in {time.perf_counter() - t_gen:.1f}s")
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(total)
+    HD = w.n_q_heads * w.head_dim
+    done = 0
+    elapsed = 0.0
+    batch = 32
+    while done < total and elapsed < budget_s:
+        rows = np.sort(order[done:done + batch])
+        counters = rows.astype(np.uint64)[:, None] * np.uint64(HD) + np.arange(HD, dtype=np.uint64)[None, :]
+        qb = I.values_f32(w.seed, I.KIND_STREAM["q"], counters)
+        if w.io_dtype == "bf16":
+            qb = I.f32_to_bf16_bits(qb)
+        qb = qb.reshape(len(rows), w.n_q_heads, w.head_dim)
+        t0 = time.perf_counter()
+        OA.layer_attention(OA.upcast(qb, w.io_dtype), rows, K, V, w.mask(0), w.sink, w.recent)
+        elapsed += time.perf_counter() - t0
+        done += len(rows)
+    est = elapsed * total / done
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    return {"value": round(total / est, 2), "unit": "tok/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{done} of {total} step rows drawn uniformly (all {w.n_q_heads} heads), "
+                      f"{elapsed:.1f}s, scaled by row count",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama2_7b_mha_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(run(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * duo_attn.h -- C ABI of the mixed-head (retrieval / streaming) KV attention library
+ * for AMD Instinct MI355X (gfx950).  Library: libduo_attn.so.
+ *
+ * What the library computes
+ * -------------------------
+ * Each transformer layer's KV heads are split into two kinds.  A retrieval head keeps
+ * a full KV cache and its queries attend causally to every token; a streaming head
+ * keeps a constant-length cache holding only the attention sinks and the most recent
+ * tokens, and its queries attend to exactly those.  Sources: hotpaper.ai page
+ * "DuoAttention: Efficient Long-Context LLM Inference with Retrieval and Streaming
+ * Heads", abstract (full KV cache for retrieval heads, light constant-length cache of
+ * recent tokens and sinks for streaming heads; applies to both decoding and
+ * pre-filling; MHA and GQA models) and its technical-approach section (two caches per
+ * layer); "What is DuoAttention" (nav.superapi.store), Technical principles.
+ *
+ * For a query at absolute position i (0-based) the visible keys are
+ *   retrieval head: { j : j <= i }
+ *   streaming head: { j : j <= i and (j < sink or i - j < recent) }
+ * scores are scale * <q_i, k_j> (scale = 1/sqrt(head_dim) unless set), softmax over
+ * the visible set, output sum_j p_ij v_j; accumulation in fp32, output in the I/O
+ * dtype rounded to nearest even.  Sinks are positions 0..sink-1; the recent window
+ * includes the current token, so a streaming cache holds exactly sink + recent tokens.
+ * Query head h uses KV head h / (n_q_heads / n_kv_heads) (MHA when equal, GQA
+ * otherwise) and takes that KV head's label.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Pointers named d_* or documented as device pointers are HIP device memory owned
+ *   by the caller.  The library never allocates device memory: the caller provides
+ *   one workspace (size from duo_kv_bytes) that holds every cache, table and scratch
+ *   buffer.  The library owns only the small host-side handle.
+ * - Work is enqueued on the caller's stream (hipStream_t passed as void*, NULL = the
+ *   default stream) and no call synchronises.  Buffers must stay valid until the
+ *   stream has run the work.  Calls on one handle must be ordered (same stream, or
+ *   the caller orders the streams): they share the workspace's scratch region.
+ * - Every call validates all arguments before enqueuing anything; a call that
+ *   returns an error has changed no state.  Device pointers must be 16-byte aligned.
+ * - Return codes: DUO_OK, or a negative DUO_E_* code with a message available from
+ *   duo_last_error() (thread-local).
+ * - A handle is not thread-safe.
+ *
+ * Tensor layouts (row-major, contiguous, batch B = cfg.batch):
+ *   Q, O for prefill : [B, T, n_q_heads, head_dim]      (token-major, as a fused QKV
+ *   K, V for prefill : [B, T, n_kv_heads, head_dim]      projection produces them)
+ *   Q, O for decode  : [B, n_q_heads, head_dim]
+ *   K, V for decode  : [B, n_kv_heads, head_dim]
+ * Element type: float32 (DUO_DTYPE_F32) or bfloat16 (DUO_DTYPE_BF16), cfg.io_dtype.
+ */
+#ifndef DUO_ATTN_H
+#define DUO_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DUO_OK             0
+#define DUO_E_INVALID     -1  /* null / misaligned pointer, value out of range        */
+#define DUO_E_UNSUPPORTED -2  /* valid request this build does not implement          */
+#define DUO_E_CAPACITY    -3  /* length + tokens > max_context, or workspace too small */
+#define DUO_E_STATE       -4  /* call not allowed in the handle's current state        */
+#define DUO_E_HIP         -5  /* a HIP runtime call or kernel launch failed            */
+
+/* I/O element types. */
+#define DUO_DTYPE_F32  0
+#define DUO_DTYPE_BF16 1
+
+/* KV cache formats. */
+#define DUO_KV_SAME_AS_IO 0  /* caches hold K/V in the I/O type, bit-exact copies   */
+#define DUO_KV_INT4_G128  1  /* 4-bit codes, one group per 128-value vector, fp16
+                                scale and zero (bf16 I/O, head_dim 128 only).  Format
+                                of one vector x: s = fp16(fp32(fp32(max-min)/15)),
+                                z = fp16(min), q = clamp(rint_even(fp32(fp32(x-z)/s)),
+                                0, 15) (q = 0 when s == 0); dequantised value
+                                fp32(q*s + z).  The pages only name a 4-bit KV cache
+                                (hotpaper.ai page, abstract and main results). */
+
+/* Limits of this build. */
+#define DUO_MAX_KV_HEADS 64
+#define DUO_MAX_GROUP    16   /* n_q_heads / n_kv_heads */
+
+typedef struct duo_config {
+  int32_t n_layers;     /* >= 1 */
+  int32_t batch;        /* >= 1; sequences of a batch share one length and one mask */
+  int32_t n_q_heads;    /* multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* 1..DUO_MAX_KV_HEADS */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t sink;         /* attention-sink tokens, >= 0 */
+  int32_t recent;       /* recent-window tokens including the current one, >= 1 */
+  int32_t io_dtype;     /* DUO_DTYPE_* */
+  int32_t kv_format;    /* DUO_KV_* */
+  int32_t reserved;     /* must be 0 */
+  int64_t max_context;  /* tokens per sequence the retrieval caches can hold, >= 1 */
+  float scale;          /* softmax scale; 0 means 1/sqrt(head_dim) */
+  /* Host pointer, [n_layers * n_kv_heads] bytes, 1 = retrieval head, 0 = streaming
+   * head (the per-head label that the method fixes before inference: hotpaper.ai
+   * page, abstract; cn.bg3.co article, DuoAttention 的创新设计).  Copied at init. */
+  const uint8_t* retrieval_mask;
+} duo_config;
+
+typedef struct duo_handle duo_handle;
+
+/* Size in bytes of the device workspace duo_kv_init needs for cfg.  Returns
+ * DUO_E_INVALID / DUO_E_UNSUPPORTED for a config init would reject. */
+int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes);
+
+/* Create a handle over a caller-allocated device workspace of `bytes` bytes
+ * (>= duo_kv_bytes, 256-byte aligned).  Lays out one retrieval cache per retrieval KV
+ * head and one constant-length (sink + recent slots) cache per streaming KV head, per
+ * layer and sequence, and clears the scratch counters (one small kernel on `stream`).
+ * Every layer starts with length 0.  The workspace must not be used by anything else
+ * while the handle lives. */
+int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream,
+                duo_handle** out);
+
+/* Causal attention of n_tokens new tokens of `layer` (positions len .. len+T-1) and
+ * append of their K/V (pre-filling; a prompt may be split into chunks, one call each,
+ * and the result equals one unchunked call).  q, k, v, out: device pointers in the
+ * prefill layouts above.  Retrieval heads attend to every earlier token of the
+ * sequence; streaming heads to the sinks and the recent window, read from their
+ * constant-length cache as it stood before the call plus the chunk itself.  After the
+ * call the layer's length is len + T.  int4 caches: DUO_E_UNSUPPORTED (decode-only
+ * format in this build).  Errors: DUO_E_INVALID (T <= 0, bad layer, null or
+ * misaligned pointer), DUO_E_CAPACITY (len + T > max_context). */
+int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v,
+                int32_t n_tokens, void* out, void* hip_stream);
+
+/* Append n_tokens K/V rows (prefill layout, no attention) at positions len .. len+T-1:
+ * retrieval heads store every row, streaming heads keep the sinks and the last
+ * `recent` tokens (evicting older ones); int4 caches quantise on the way in.  Used to
+ * fill long contexts.  Errors as duo_prefill. */
+int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, int32_t n_tokens,
+                  void* hip_stream);
+
+/* One decoding step of `layer`: appends k_new / v_new (decode layout) at position
+ * t = len, then the query q (decode layout) at position t attends to the visible keys
+ * (so the new token sees itself), writing out.  If k_new and v_new are both NULL
+ * nothing is appended and the query attends at t = len - 1 (its K/V were appended
+ * earlier, e.g. by duo_kv_append).  Retrieval heads use split-K flash decoding over
+ * the full cache with a log-sum-exp merge; streaming heads read their sink + recent
+ * slots.  Errors: DUO_E_INVALID, DUO_E_CAPACITY (append past max_context),
+ * DUO_E_STATE (NULL k_new/v_new with an empty layer, or only one of them NULL). */
+int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new,
+               void* out, void* hip_stream);
+
+/* Tokens currently held for `layer` (the position of the next appended token). */
+int duo_kv_length(const duo_handle* h, int32_t layer, int64_t* out_len);
+
+/* Free the host handle (the workspace stays the caller's).  NULL is allowed. */
+void duo_kv_free(duo_handle* h);
+
+/* Message of the last error on this thread ("" if none). */
+const char* duo_last_error(void);
+
+/* ---- Inspection (used by tests to check the caches) --------------------------- */
+
+/* Copy the stored K (which = 0) or V (which = 1) vectors of one sequence `b`, KV head
+ * `kv_head` of `layer`, for absolute positions pos0 .. pos0+n-1, into d_out
+ * ([n, head_dim] float32, device), dequantised for int4 caches with the same device
+ * code the attention kernels use.  Positions must be held: < len for retrieval heads,
+ * visible from position len-1 for streaming heads; otherwise DUO_E_INVALID. */
+int duo_kv_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which,
+                int64_t pos0, int32_t n, float* d_out, void* hip_stream);
+
+/* int4 caches only: copy the packed codes (n * 64 bytes, byte k = code 2k in the low
+ * nibble and code 2k+1 in the high nibble, element order) and the fp16 scale and zero
+ * bit patterns (n * 2 uint16: scale, zero) of the same vectors as duo_kv_read. */
+int duo_kv_read_int4(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which,
+                     int64_t pos0, int32_t n, uint8_t* d_codes, uint16_t* d_meta, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_ATTN_H */

@@ -1,0 +1,43 @@
+/*
+ * duo_profile.h -- per-kernel timing of a duo_handle (tracing).  Exported by
+ * libduo_attn.so.
+ *
+ * While profiling is enabled on a handle, every kernel launch the handle makes is
+ * bracketed by two hipEvents recorded on the stream of that launch, so the measured
+ * interval is the kernel's own execution on that stream.  duo_profile_collect waits
+ * for the recorded events, adds up elapsed milliseconds and launch counts per kernel
+ * class, and clears the record.  Event objects are pooled by the handle (host-side
+ * HIP resources; no device memory is allocated).  Recording adds one event pair per
+ * launch on the stream.
+ *
+ * Errors: DUO_E_INVALID (NULL handle or output array), DUO_E_HIP (event failure).
+ */
+#ifndef DUO_PROFILE_H
+#define DUO_PROFILE_H
+
+#include <stdint.h>
+
+#include "duo_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUO_KERNEL_APPEND             0  /* fused append / evict (and int4 quantise) */
+#define DUO_KERNEL_PREFILL_RETRIEVAL  1  /* causal prefill attention, retrieval heads */
+#define DUO_KERNEL_PREFILL_STREAMING  2  /* sink + window prefill attention, streaming heads */
+#define DUO_KERNEL_DECODE             3  /* split-K decode attention with merge, all heads */
+#define DUO_KERNEL_CLASSES            4
+
+/* on != 0 starts recording, on == 0 stops (recorded events stay until collected). */
+int duo_profile_enable(duo_handle* h, int32_t on);
+
+/* total_ms[DUO_KERNEL_CLASSES], launches[DUO_KERNEL_CLASSES]: filled with the sums
+ * since the last collect.  Synchronises on the recorded events. */
+int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_PROFILE_H */

@@ -1,0 +1,247 @@
+"""ctypes binding of libduo_attn.so (include/duo_attn.h, include/duo_synth.h).
+
+Argument marshalling only: the functions below carry the C names and pass device
+pointers, sizes and the current HIP stream through; every step of the attention path
+runs in the library's HIP kernels.  PyTorch supplies device memory and streams.  If the
+built library is missing this module raises on first use; there is no fallback.
+
+``DuoKV`` is a small convenience owner of one handle and its workspace tensor.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libduo_attn.so")
+
+DUO_OK = 0
+DUO_E_INVALID = -1
+DUO_E_UNSUPPORTED = -2
+DUO_E_CAPACITY = -3
+DUO_E_STATE = -4
+DUO_E_HIP = -5
+DUO_DTYPE_F32 = 0
+DUO_DTYPE_BF16 = 1
+DUO_KV_SAME_AS_IO = 0
+DUO_KV_INT4_G128 = 1
+
+EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
+           "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
+           "duo_profile_enable", "duo_profile_collect"]
+KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode"]
+
+
+class DuoError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class duo_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("sink", ctypes.c_int32),
+        ("recent", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("max_context", ctypes.c_int64), ("scale", ctypes.c_float),
+        ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libduo_attn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mixed_head_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    cfgp = ctypes.POINTER(duo_config)
+    sig = {
+        "duo_kv_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(u64)]),
+        "duo_kv_init": (ctypes.c_int, [cfgp, vp, u64, vp, ctypes.POINTER(vp)]),
+        "duo_prefill": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp]),
+        "duo_kv_append": (ctypes.c_int, [vp, i32, vp, vp, i32, vp]),
+        "duo_decode": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
+        "duo_kv_length": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64)]),
+        "duo_kv_free": (None, [vp]),
+        "duo_last_error": (ctypes.c_char_p, []),
+        "duo_kv_read": (ctypes.c_int, [vp, i32, i32, i32, i32, i64, i32, vp, vp]),
+        "duo_kv_read_int4": (ctypes.c_int, [vp, i32, i32, i32, i32, i64, i32, vp, vp, vp]),
+        "duo_synth_fill": (ctypes.c_int, [vp, i32, u64, ctypes.c_uint32, u64, u64, vp]),
+        "duo_profile_enable": (ctypes.c_int, [vp, i32]),
+        "duo_profile_collect": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != DUO_OK:
+        raise DuoError(rc, lib().duo_last_error().decode())
+
+
+def make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, sink, recent, max_context, io_dtype,
+                kv_format, retrieval_mask, scale=0.0):
+    """Build a duo_config; `retrieval_mask` is any [n_layers, n_kv_heads] 0/1 array.
+    The returned object keeps the mask buffer alive."""
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(retrieval_mask, dtype=np.uint8).reshape(-1))
+    cfg = duo_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, sink, recent,
+                     io_dtype, kv_format, 0, max_context, scale,
+                     m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    cfg._mask_keepalive = m
+    return cfg
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---- the C entry points, same names ------------------------------------------------
+
+def duo_kv_bytes(cfg) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().duo_kv_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def duo_kv_init(cfg, workspace, stream=None):
+    h = ctypes.c_void_p()
+    _check(lib().duo_kv_init(ctypes.byref(cfg), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def duo_prefill(h, layer, q, k, v, n_tokens, out, stream=None):
+    _check(lib().duo_prefill(h, layer, _ptr(q), _ptr(k), _ptr(v), n_tokens, _ptr(out), _stream(stream)))
+
+
+def duo_kv_append(h, layer, k, v, n_tokens, stream=None):
+    _check(lib().duo_kv_append(h, layer, _ptr(k), _ptr(v), n_tokens, _stream(stream)))
+
+
+def duo_decode(h, layer, q, k_new, v_new, out, stream=None):
+    _check(lib().duo_decode(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _stream(stream)))
+
+
+def duo_kv_length(h, layer) -> int:
+    out = ctypes.c_int64()
+    _check(lib().duo_kv_length(h, layer, ctypes.byref(out)))
+    return out.value
+
+
+def duo_kv_free(h):
+    lib().duo_kv_free(h)
+
+
+def duo_last_error() -> str:
+    return lib().duo_last_error().decode()
+
+
+def duo_kv_read(h, layer, b, kv_head, which, pos0, n, out, stream=None):
+    _check(lib().duo_kv_read(h, layer, b, kv_head, which, pos0, n, _ptr(out), _stream(stream)))
+
+
+def duo_kv_read_int4(h, layer, b, kv_head, which, pos0, n, codes, meta, stream=None):
+    _check(lib().duo_kv_read_int4(h, layer, b, kv_head, which, pos0, n, _ptr(codes), _ptr(meta), _stream(stream)))
+
+
+def duo_synth_fill(out, dtype, seed, stream_id, counter0, n, stream=None):
+    _check(lib().duo_synth_fill(_ptr(out), dtype, seed, stream_id, counter0, n, _stream(stream)))
+
+
+def duo_profile_enable(h, on: bool):
+    _check(lib().duo_profile_enable(h, 1 if on else 0))
+
+
+def duo_profile_collect(h) -> dict:
+    """{class name: (total_ms, launches)} since the last collect."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().duo_profile_collect(h, ms, cnt))
+    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+# ---- convenience owner -------------------------------------------------------------
+
+class DuoKV:
+    """One handle plus its workspace (a torch uint8 tensor on the current device)."""
+
+    def __init__(self, n_layers, n_q_heads, n_kv_heads, head_dim, sink, recent, max_context, retrieval_mask,
+                 io_dtype="bf16", kv_format="same", batch=1, scale=0.0, device="cuda"):
+        import torch
+        self.io = DUO_DTYPE_F32 if io_dtype == "f32" else DUO_DTYPE_BF16
+        self.torch_dtype = torch.float32 if io_dtype == "f32" else torch.bfloat16
+        self.cfg = make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, sink, recent, max_context,
+                               self.io, DUO_KV_INT4_G128 if kv_format == "int4" else DUO_KV_SAME_AS_IO,
+                               retrieval_mask, scale)
+        self.nbytes = duo_kv_bytes(self.cfg)
+        self.workspace = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.h = duo_kv_init(self.cfg, self.workspace)
+        self.B, self.Hq, self.Hkv, self.D = batch, n_q_heads, n_kv_heads, head_dim
+
+    @classmethod
+    def for_workload(cls, w, **kw):
+        return cls(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent, w.max_context,
+                   w.masks().astype("uint8"), io_dtype=w.io_dtype, kv_format=w.kv_format, **kw)
+
+    def close(self):
+        if self.h:
+            duo_kv_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def length(self, layer):
+        return duo_kv_length(self.h, layer)
+
+    def prefill(self, layer, q, k, v, out=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        duo_prefill(self.h, layer, q, k, v, q.shape[-3], out)
+        return out
+
+    def append(self, layer, k, v):
+        duo_kv_append(self.h, layer, k, v, k.shape[-3])
+
+    def decode(self, layer, q, k_new=None, v_new=None, out=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        duo_decode(self.h, layer, q, k_new, v_new, out)
+        return out
+
+    def read(self, layer, kv_head, which, pos0, n, b=0):
+        import torch
+        out = torch.empty((n, self.D), dtype=torch.float32, device=self.workspace.device)
+        duo_kv_read(self.h, layer, b, kv_head, which, pos0, n, out)
+        return out
+
+    def read_int4(self, layer, kv_head, which, pos0, n, b=0):
+        import torch
+        codes = torch.empty((n, 64), dtype=torch.uint8, device=self.workspace.device)
+        meta = torch.empty((n, 2), dtype=torch.int16, device=self.workspace.device)
+        duo_kv_read_int4(self.h, layer, b, kv_head, which, pos0, n, codes, meta)
+        return codes, meta

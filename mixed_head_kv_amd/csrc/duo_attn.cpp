@@ -1,0 +1,513 @@
+// Host side of libduo_attn.so: argument validation, workspace layout, head regrouping,
+// per-layer lengths and kernel launches.  The C ABI is declared in include/duo_attn.h.
+//
+// Head regrouping: the per-KV-head retrieval / streaming label (fixed before inference,
+// hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with Retrieval
+// and Streaming Heads", abstract; cn.bg3.co article, DuoAttention 的创新设计) splits
+// each layer's KV heads into a dense list of retrieval heads and a dense list of
+// streaming heads, so each kind launches as one batch of workgroups and owns one
+// contiguous cache region.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/duo_attn.h"
+#include "../../include/duo_profile.h"
+#include "../../include/duo_synth.h"
+#include "duo_kernels.h"
+
+using duo::CacheRegion;
+using duo::Geom;
+using duo::LayerView;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DUO_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DUO_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+struct LayerLayout {
+  int n_ret = 0, n_str = 0;
+  uint64_t ret_k = 0, ret_v = 0, ret_km = 0, ret_vm = 0;
+  uint64_t str_k = 0, str_v = 0, str_km = 0, str_vm = 0;
+};
+
+struct Layout {
+  int64_t cap = 0;   // retrieval rows per cache
+  int64_t nslot = 0; // streaming slots per cache
+  std::vector<LayerLayout> layers;
+  uint64_t partials = 0, counters = 0, total = 0;
+};
+
+int validate_config(const duo_config* c) {
+  if (!c) return fail(DUO_E_INVALID, "config is NULL");
+  if (c->n_layers < 1) return fail(DUO_E_INVALID, "n_layers must be >= 1");
+  if (c->batch < 1) return fail(DUO_E_INVALID, "batch must be >= 1");
+  if (c->n_kv_heads < 1 || c->n_kv_heads > DUO_MAX_KV_HEADS)
+    return fail(DUO_E_INVALID, "n_kv_heads must be in 1..64");
+  if (c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads)
+    return fail(DUO_E_INVALID, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (c->n_q_heads / c->n_kv_heads > DUO_MAX_GROUP)
+    return fail(DUO_E_UNSUPPORTED, "n_q_heads / n_kv_heads above 16 is not supported");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(DUO_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->sink < 0) return fail(DUO_E_INVALID, "sink must be >= 0");
+  if (c->recent < 1) return fail(DUO_E_INVALID, "recent must be >= 1");
+  if (c->max_context < 1 || c->max_context > (int64_t(1) << 40)) return fail(DUO_E_INVALID, "max_context out of range");
+  if (c->io_dtype != DUO_DTYPE_F32 && c->io_dtype != DUO_DTYPE_BF16) return fail(DUO_E_INVALID, "unknown io_dtype");
+  if (c->kv_format != DUO_KV_SAME_AS_IO && c->kv_format != DUO_KV_INT4_G128)
+    return fail(DUO_E_INVALID, "unknown kv_format");
+  if (c->kv_format == DUO_KV_INT4_G128 && (c->io_dtype != DUO_DTYPE_BF16 || c->head_dim != 128))
+    return fail(DUO_E_UNSUPPORTED, "int4 KV needs bf16 I/O and head_dim 128");
+  if (c->reserved != 0) return fail(DUO_E_INVALID, "reserved must be 0");
+  if (!(c->scale >= 0.0f) || !std::isfinite(c->scale)) return fail(DUO_E_INVALID, "scale must be finite and >= 0");
+  if (!c->retrieval_mask) return fail(DUO_E_INVALID, "retrieval_mask is NULL");
+  const int64_t n = int64_t(c->n_layers) * c->n_kv_heads;
+  for (int64_t i = 0; i < n; ++i)
+    if (c->retrieval_mask[i] > 1) return fail(DUO_E_INVALID, "retrieval_mask entries must be 0 or 1");
+  return DUO_OK;
+}
+
+// Byte layout of the workspace.  Returns false on arithmetic overflow.
+bool make_layout(const duo_config* c, Layout* L) {
+  const uint64_t B = c->batch, D = c->head_dim;
+  L->cap = int64_t(align_up(uint64_t(c->max_context), duo::kRowAlign));
+  L->nslot = int64_t(align_up(uint64_t(c->sink) + uint64_t(c->recent), duo::kRowAlign));
+  const bool int4 = c->kv_format == DUO_KV_INT4_G128;
+  const uint64_t esize = c->io_dtype == DUO_DTYPE_F32 ? 4 : 2;
+  // bytes per stored vector (codes or values) and per meta entry
+  const uint64_t vec = int4 ? D / 2 : D * esize;
+  const uint64_t meta = int4 ? 4 : 0;
+  uint64_t off = 0;
+  const long double limit = 1.0e18L;
+  L->layers.assign(c->n_layers, LayerLayout());
+  for (int l = 0; l < c->n_layers; ++l) {
+    LayerLayout& y = L->layers[l];
+    for (int h = 0; h < c->n_kv_heads; ++h)
+      (c->retrieval_mask[l * c->n_kv_heads + h] ? y.n_ret : y.n_str)++;
+    const long double ret_rows = (long double)B * y.n_ret * L->cap;
+    const long double str_rows = (long double)B * y.n_str * L->nslot;
+    if (ret_rows * vec * 2 + str_rows * vec * 2 + (ret_rows + str_rows) * meta * 2 + (long double)off > limit)
+      return false;
+    const uint64_t rr = B * y.n_ret * uint64_t(L->cap), sr = B * y.n_str * uint64_t(L->nslot);
+    y.ret_k = off; off = align_up(off + rr * vec, kAlign);
+    y.ret_v = off; off = align_up(off + rr * vec, kAlign);
+    y.str_k = off; off = align_up(off + sr * vec, kAlign);
+    y.str_v = off; off = align_up(off + sr * vec, kAlign);
+    if (int4) {
+      y.ret_km = off; off = align_up(off + rr * meta, kAlign);
+      y.ret_vm = off; off = align_up(off + rr * meta, kAlign);
+      y.str_km = off; off = align_up(off + sr * meta, kAlign);
+      y.str_vm = off; off = align_up(off + sr * meta, kAlign);
+    }
+  }
+  L->partials = off;
+  off = align_up(off + B * c->n_q_heads * uint64_t(duo::kMaxSplits) * (D + 2) * 4, kAlign);
+  L->counters = off;
+  off = align_up(off + B * c->n_kv_heads * 4, kAlign);
+  L->total = off;
+  return true;
+}
+
+}  // namespace
+
+struct duo_handle {
+  duo_config cfg;
+  std::vector<uint8_t> mask;
+  char* ws = nullptr;
+  uint64_t ws_bytes = 0;
+  Layout layout;
+  Geom geom;
+  std::vector<LayerView> views;
+  std::vector<int64_t> len;
+  float* partials = nullptr;
+  int* counters = nullptr;
+  int num_cu = 256;
+  int chunk_override = 0;
+  bool use_mfma = false;
+  // kernel timing (duo_profile.h)
+  bool profiling = false;
+  struct Mark { int cls; hipEvent_t start, stop; };
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> event_pool;
+  ~duo_handle() {
+    for (Mark& m : marks) { event_pool.push_back(m.start); event_pool.push_back(m.stop); }
+    for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+hipEvent_t take_event(duo_handle* h) {
+  if (!h->event_pool.empty()) {
+    hipEvent_t e = h->event_pool.back();
+    h->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when the handle is profiling.
+struct KernelMark {
+  duo_handle* h;
+  int cls;
+  hipStream_t st;
+  hipEvent_t start = nullptr;
+  KernelMark(duo_handle* h_, int cls_, hipStream_t st_) : h(h_), cls(cls_), st(st_) {
+    if (h->profiling && (start = take_event(h)) != nullptr) (void)hipEventRecord(start, st);
+  }
+  ~KernelMark() {
+    if (!start) return;
+    hipEvent_t stop = take_event(h);
+    if (stop && hipEventRecord(stop, st) == hipSuccess) {
+      h->marks.push_back(duo_handle::Mark{cls, start, stop});
+    } else {
+      h->event_pool.push_back(start);
+      if (stop) h->event_pool.push_back(stop);
+    }
+  }
+};
+
+int check_layer(const duo_handle* h, int32_t layer) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  if (layer < 0 || layer >= h->cfg.n_layers) return fail(DUO_E_INVALID, "layer out of range");
+  return DUO_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(DUO_E_INVALID, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(DUO_E_INVALID, std::string(name) + " is not 16-byte aligned");
+  return DUO_OK;
+}
+
+duo::DecodePlan make_plan(const duo_handle* h, int64_t t) {
+  duo::DecodePlan p;
+  p.t = t;
+  p.partials = h->partials;
+  p.counters = h->counters;
+  const int64_t nkeys = t + 1;
+  const int B = h->cfg.batch;
+  const LayerView& lv = h->views[0];
+  (void)lv;
+  // Retrieval: enough splits for ~4 workgroups per CU over all retrieval heads, at
+  // least 256 keys per split, a multiple of 64, and never above kMaxSplits.
+  int64_t heads = 0;
+  for (const LayerLayout& y : h->layout.layers) heads = y.n_ret > heads ? y.n_ret : heads;
+  heads *= B;
+  int64_t chunk = 256;
+  if (heads > 0) {
+    const int64_t target_wg = int64_t(h->num_cu) * 4;
+    const int64_t per_head = (target_wg + heads - 1) / heads;
+    const int64_t want = (nkeys + per_head - 1) / per_head;
+    if (want > chunk) chunk = want;
+  }
+  const int64_t min_chunk = (nkeys + duo::kMaxSplits - 1) / duo::kMaxSplits;
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
+  chunk = int64_t(align_up(uint64_t(chunk), 64));
+  p.chunk_r = int(chunk);
+  p.nsplit_r = int((nkeys + chunk - 1) / chunk);
+  const int64_t nslots = nkeys < h->cfg.sink + h->cfg.recent ? nkeys : int64_t(h->cfg.sink) + h->cfg.recent;
+  p.chunk_s = 128;
+  p.nsplit_s = int((nslots + p.chunk_s - 1) / p.chunk_s);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* duo_last_error(void) { return g_last_error.c_str(); }
+
+int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!out_bytes) return fail(DUO_E_INVALID, "out_bytes is NULL");
+  Layout L;
+  if (!make_layout(cfg, &L)) return fail(DUO_E_INVALID, "workspace size overflows");
+  *out_bytes = L.total;
+  return ok();
+}
+
+int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream, duo_handle** out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(DUO_E_INVALID, "out is NULL");
+  if (!d_workspace) return fail(DUO_E_INVALID, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign) return fail(DUO_E_INVALID, "workspace is not 256-byte aligned");
+  Layout L;
+  if (!make_layout(cfg, &L)) return fail(DUO_E_INVALID, "workspace size overflows");
+  if (bytes < L.total) return fail(DUO_E_CAPACITY, "workspace smaller than duo_kv_bytes()");
+
+  duo_handle* h = new duo_handle();
+  h->cfg = *cfg;
+  h->mask.assign(cfg->retrieval_mask, cfg->retrieval_mask + size_t(cfg->n_layers) * cfg->n_kv_heads);
+  h->cfg.retrieval_mask = h->mask.data();
+  h->ws = static_cast<char*>(d_workspace);
+  h->ws_bytes = bytes;
+  h->layout = L;
+  Geom& g = h->geom;
+  g.B = cfg->batch;
+  g.Hq = cfg->n_q_heads;
+  g.Hkv = cfg->n_kv_heads;
+  g.G = cfg->n_q_heads / cfg->n_kv_heads;
+  g.D = cfg->head_dim;
+  g.S = cfg->sink;
+  g.R = cfg->recent;
+  g.io = cfg->io_dtype;
+  g.kvfmt = cfg->kv_format;
+  g.scale = cfg->scale > 0.0f ? cfg->scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  g.scale_log2 = g.scale * 1.4426950408889634f;
+  const bool int4 = cfg->kv_format == DUO_KV_INT4_G128;
+  h->views.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const LayerLayout& y = L.layers[l];
+    LayerView& v = h->views[l];
+    std::memset(&v, 0, sizeof(v));
+    v.n_ret = y.n_ret;
+    v.n_str = y.n_str;
+    v.ret = CacheRegion{h->ws + y.ret_k, h->ws + y.ret_v,
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.ret_km) : nullptr,
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.ret_vm) : nullptr, L.cap};
+    v.str = CacheRegion{h->ws + y.str_k, h->ws + y.str_v,
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.str_km) : nullptr,
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.str_vm) : nullptr, L.nslot};
+    int nr = 0, ns = 0;
+    for (int kv = 0; kv < cfg->n_kv_heads; ++kv) {
+      if (h->mask[size_t(l) * cfg->n_kv_heads + kv]) {
+        v.kind[kv] = duo::kKindRetrieval;
+        v.slot[kv] = nr;
+        v.ret_kv[nr++] = kv;
+      } else {
+        v.kind[kv] = duo::kKindStreaming;
+        v.slot[kv] = ns;
+        v.str_kv[ns++] = kv;
+      }
+    }
+  }
+  h->len.assign(cfg->n_layers, 0);
+  h->partials = reinterpret_cast<float*>(h->ws + L.partials);
+  h->counters = reinterpret_cast<int*>(h->ws + L.counters);
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) h->num_cu = n;
+  }
+  if (const char* e = std::getenv("DUO_DECODE_CHUNK")) h->chunk_override = std::atoi(e);
+  h->use_mfma = false;
+  hipError_t e = duo::launch_zero_i32(h->counters, int64_t(cfg->batch) * cfg->n_kv_heads, as_stream(hip_stream));
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "clearing counters");
+  }
+  *out = h;
+  return ok();
+}
+
+void duo_kv_free(duo_handle* h) { delete h; }
+
+int duo_kv_length(const duo_handle* h, int32_t layer, int64_t* out_len) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (!out_len) return fail(DUO_E_INVALID, "out_len is NULL");
+  *out_len = h->len[layer];
+  return ok();
+}
+
+static int check_tokens(const duo_handle* h, int32_t layer, int32_t n_tokens) {
+  if (n_tokens <= 0) return fail(DUO_E_INVALID, "n_tokens must be > 0");
+  if (h->len[layer] + n_tokens > h->cfg.max_context)
+    return fail(DUO_E_CAPACITY, "length + n_tokens exceeds max_context");
+  return DUO_OK;
+}
+
+int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v, int32_t n_tokens,
+                void* out, void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) || (rc = check_ptr(out, "out")))
+    return rc;
+  if (h->cfg.kv_format == DUO_KV_INT4_G128) return fail(DUO_E_UNSUPPORTED, "prefill with an int4 cache");
+  if ((rc = check_tokens(h, layer, n_tokens))) return rc;
+  const LayerView& lv = h->views[layer];
+  const int64_t t0 = h->len[layer];
+  hipStream_t st = as_stream(hip_stream);
+  hipError_t e;
+  {
+    KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+    e = duo::launch_prefill_valu(h->geom, lv, q, k, v, out, n_tokens, t0, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill attention");
+  {
+    KernelMark m(h, DUO_KERNEL_APPEND, st);
+    e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 3, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill append");
+  h->len[layer] = t0 + n_tokens;
+  return ok();
+}
+
+int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, int32_t n_tokens, void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if ((rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
+  if ((rc = check_tokens(h, layer, n_tokens))) return rc;
+  const int64_t t0 = h->len[layer];
+  hipError_t e;
+  {
+    KernelMark m(h, DUO_KERNEL_APPEND, as_stream(hip_stream));
+    e = duo::launch_append(h->geom, h->views[layer], k, v, n_tokens, t0, 3, as_stream(hip_stream));
+  }
+  if (e != hipSuccess) return hip_fail(e, "append");
+  h->len[layer] = t0 + n_tokens;
+  return ok();
+}
+
+int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
+               void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(out, "out"))) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(DUO_E_STATE, "k_new and v_new must both be set or both NULL");
+  const bool append = k_new != nullptr;
+  if (append && ((rc = check_ptr(k_new, "k_new")) || (rc = check_ptr(v_new, "v_new")))) return rc;
+  const int64_t len = h->len[layer];
+  if (append && len + 1 > h->cfg.max_context) return fail(DUO_E_CAPACITY, "decode append exceeds max_context");
+  if (!append && len < 1) return fail(DUO_E_STATE, "decode without new K/V on an empty layer");
+  const LayerView& lv = h->views[layer];
+  hipStream_t st = as_stream(hip_stream);
+  const int64_t t = append ? len : len - 1;
+  hipError_t e;
+  if (append) {
+    KernelMark m(h, DUO_KERNEL_APPEND, st);
+    e = duo::launch_append(h->geom, lv, k_new, v_new, 1, t, 3, st);
+    if (e != hipSuccess) return hip_fail(e, "decode append");
+  }
+  const duo::DecodePlan p = make_plan(h, t);
+  {
+    KernelMark m(h, DUO_KERNEL_DECODE, st);
+    e = duo::launch_decode_valu(h->geom, lv, p, q, out, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode attention");
+  if (append) h->len[layer] = len + 1;
+  return ok();
+}
+
+static int check_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,
+                      int32_t n, bool* streaming, int64_t* cache) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (b < 0 || b >= h->cfg.batch) return fail(DUO_E_INVALID, "sequence index out of range");
+  if (kv_head < 0 || kv_head >= h->cfg.n_kv_heads) return fail(DUO_E_INVALID, "kv_head out of range");
+  if (which != 0 && which != 1) return fail(DUO_E_INVALID, "which must be 0 (K) or 1 (V)");
+  if (n < 0) return fail(DUO_E_INVALID, "n must be >= 0");
+  const LayerView& lv = h->views[layer];
+  *streaming = lv.kind[kv_head] == duo::kKindStreaming;
+  *cache = int64_t(b) * (*streaming ? lv.n_str : lv.n_ret) + lv.slot[kv_head];
+  const int64_t len = h->len[layer];
+  if (pos0 < 0 || pos0 + n > len) return fail(DUO_E_INVALID, "positions not yet appended");
+  if (*streaming && n > 0) {
+    const int64_t last = len - 1;
+    for (int64_t p = pos0; p < pos0 + n; ++p)
+      if (!(p < h->cfg.sink || last - p < h->cfg.recent))
+        return fail(DUO_E_INVALID, "position evicted from the streaming cache");
+  }
+  return DUO_OK;
+}
+
+int duo_kv_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,
+                int32_t n, float* d_out, void* hip_stream) {
+  bool streaming;
+  int64_t cache;
+  int rc = check_read(h, layer, b, kv_head, which, pos0, n, &streaming, &cache);
+  if (rc) return rc;
+  if ((rc = check_ptr(d_out, "out"))) return rc;
+  if (n == 0) return ok();
+  const LayerView& lv = h->views[layer];
+  hipError_t e = duo::launch_read(h->geom, streaming ? lv.str : lv.ret, cache, streaming, pos0, n, which, d_out,
+                                  as_stream(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "read");
+  return ok();
+}
+
+int duo_kv_read_int4(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,
+                     int32_t n, uint8_t* d_codes, uint16_t* d_meta, void* hip_stream) {
+  bool streaming;
+  int64_t cache;
+  int rc = check_read(h, layer, b, kv_head, which, pos0, n, &streaming, &cache);
+  if (rc) return rc;
+  if (h->cfg.kv_format != DUO_KV_INT4_G128) return fail(DUO_E_STATE, "cache is not int4");
+  if ((rc = check_ptr(d_codes, "codes")) || (rc = check_ptr(d_meta, "meta"))) return rc;
+  if (n == 0) return ok();
+  const LayerView& lv = h->views[layer];
+  hipError_t e = duo::launch_read_int4(h->geom, streaming ? lv.str : lv.ret, cache, streaming, pos0, n, which,
+                                       d_codes, d_meta, as_stream(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "read_int4");
+  return ok();
+}
+
+int duo_profile_enable(duo_handle* h, int32_t on) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  h->profiling = on != 0;
+  return ok();
+}
+
+int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  if (!total_ms || !launches) return fail(DUO_E_INVALID, "output array is NULL");
+  for (int c = 0; c < DUO_KERNEL_CLASSES; ++c) {
+    total_ms[c] = 0.0;
+    launches[c] = 0;
+  }
+  int rc = DUO_OK;
+  for (duo_handle::Mark& m : h->marks) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(m.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, m.start, m.stop);
+    if (e != hipSuccess && rc == DUO_OK) rc = hip_fail(e, "profile event");
+    total_ms[m.cls] += ms;
+    launches[m.cls] += 1;
+    h->event_pool.push_back(m.start);
+    h->event_pool.push_back(m.stop);
+  }
+  h->marks.clear();
+  return rc == DUO_OK ? ok() : rc;
+}
+
+int duo_synth_fill(void* d_out, int32_t dtype, uint64_t seed, uint32_t stream, uint64_t counter0, uint64_t n,
+                   void* hip_stream) {
+  int rc = check_ptr(d_out, "out");
+  if (rc) return rc;
+  if (dtype != DUO_DTYPE_F32 && dtype != DUO_DTYPE_BF16) return fail(DUO_E_INVALID, "unknown dtype");
+  if (seed >> 32) return fail(DUO_E_INVALID, "seed must fit in 32 bits");
+  hipError_t e = duo::launch_synth(d_out, dtype, seed, stream, counter0, n, as_stream(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "synth");
+  return ok();
+}
+
+}  // extern "C"

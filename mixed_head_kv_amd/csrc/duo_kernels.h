@@ -1,0 +1,59 @@
+// Launchers of the HIP kernels (internal to libduo_attn.so).  Each returns the
+// hipError_t of its launch; arguments are validated by the caller (duo_attn.cpp).
+#pragma once
+
+#include "duo_common.h"
+
+namespace duo {
+
+// Fused append/evict of T tokens at positions [t0, t0 + T) into every cache of the
+// layer: retrieval heads store every row, streaming heads keep sinks and the last
+// `recent` positions.  `which`: 1 = retrieval caches only, 2 = streaming only, 3 = both.
+hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, const void* v, int T,
+                         int64_t t0, int which, hipStream_t st);
+
+// Straightforward causal prefill attention on the vector ALUs (any dtype, D 64/128).
+// Keys before t0 come from the caches, keys from t0 on from the chunk inputs.
+hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q, const void* k,
+                               const void* v, void* out, int T, int64_t t0, hipStream_t st);
+
+// Retrieval-head prefill on bf16 MFMA (D = 128).  Reads keys [0, t0 + T) from the
+// retrieval cache, so the chunk must have been appended to the retrieval caches first.
+hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T,
+                               int64_t t0, hipStream_t st);
+
+// Streaming-head (sink + window) prefill on bf16 MFMA (D = 128); reads the streaming
+// caches as they stood before the chunk plus the chunk inputs.
+hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const void* q, const void* k,
+                                      const void* v, void* out, int T, int64_t t0, hipStream_t st);
+
+struct DecodePlan {
+  int64_t t;          // query position
+  int chunk_r;        // keys per split, retrieval heads
+  int nsplit_r;
+  int chunk_s;        // keys per split, streaming heads
+  int nsplit_s;
+  float* partials;    // [B * Hq * kMaxSplits * (D + 2)]
+  int* counters;      // [B * Hkv] arrival counters, zero between calls
+};
+
+// Split-K decode attention (all heads of the layer, one launch, merge by the last
+// arriving workgroup of each KV head).  VALU version, any dtype / format.
+hipError_t launch_decode_valu(const Geom& g, const LayerView& lv, const DecodePlan& p, const void* q,
+                              void* out, hipStream_t st);
+
+// Same on MFMA for bf16 and int4 caches with D = 128.
+hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePlan& p, const void* q,
+                              void* out, hipStream_t st);
+
+// Inspection: stored vectors of positions [pos0, pos0 + n) of one cache, as fp32
+// (dequantised for int4) or as raw int4 codes + (scale, zero).
+hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,
+                       int n, int which, float* out, hipStream_t st);
+hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,
+                            int n, int which, uint8_t* codes, uint16_t* meta, hipStream_t st);
+hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st);
+hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, uint64_t c0, uint64_t n,
+                        hipStream_t st);
+
+}  // namespace duo

@@ -1,0 +1,319 @@
+// KV-cache kernels: fused append/evict (with int4 quantisation), inspection reads,
+// counter clearing and the seeded synthetic fill.
+//
+// Append/evict follows the cache split of the hotpaper.ai page "DuoAttention:
+// Efficient Long-Context LLM Inference with Retrieval and Streaming Heads" (abstract
+// and technical-approach section): a retrieval head keeps every token, a streaming
+// head keeps a constant-length cache of the attention sinks and the recent tokens.
+#include "duo_kernels.h"
+
+namespace duo {
+namespace {
+
+// Source token (index into the chunk) that lands in destination row `row`, or -1.
+// Retrieval rows are absolute positions.  Streaming slot s < S holds sink position s;
+// a ring slot holds the unique position p >= S with p = S + (s - S) mod R that is
+// among the last R tokens of the sequence after the chunk.
+__device__ inline int source_token(bool streaming, int64_t row, int64_t t0, int T, int S, int R) {
+  if (!streaming) {
+    int64_t t = row - t0;
+    return (t >= 0 && t < T) ? static_cast<int>(t) : -1;
+  }
+  if (row >= S + R) return -1;
+  if (row < S) {
+    int64_t t = row - t0;
+    return (t >= 0 && t < T) ? static_cast<int>(t) : -1;
+  }
+  int64_t hi = t0 + T;
+  int64_t lo = t0;
+  if (lo < S) lo = S;
+  if (lo < hi - R) lo = hi - R;
+  if (lo >= hi) return -1;
+  int64_t want = row - S;                      // ring index of this slot
+  int64_t have = (lo - S) % R;                 // ring index of position lo
+  int64_t p = lo + ((want - have) % R + R) % R;
+  return p < hi ? static_cast<int>(p - t0) : -1;
+}
+
+// One thread per (8-row tile, dimension d).  K rows are copied element by element
+// (coalesced across d); the 8 V values of the tile are gathered and written as one
+// contiguous 8-element run of the d-major tile layout.
+template <typename T>
+__global__ void __launch_bounds__(256) k_append(Geom g, LayerView lv, const T* __restrict__ k,
+                                                const T* __restrict__ v, int T_, int64_t t0, int which,
+                                                int64_t ret_tile0, int ret_tiles, int str_tiles) {
+  const int D = g.D;
+  const int per_block = 256 / D;
+  const int d = threadIdx.x % D;
+  const int local = threadIdx.x / D;
+  const int nret = g.B * lv.n_ret;
+  const int y = blockIdx.y;
+  const bool streaming = y >= nret;
+  if (streaming && !(which & 2)) return;
+  if (!streaming && !(which & 1)) return;
+  const int cache = streaming ? y - nret : y;
+  const int b = streaming ? cache / lv.n_str : cache / lv.n_ret;
+  const int idx = streaming ? cache % lv.n_str : cache % lv.n_ret;
+  const int kvh = streaming ? lv.str_kv[idx] : lv.ret_kv[idx];
+  const CacheRegion& c = streaming ? lv.str : lv.ret;
+  const int tile = blockIdx.x * per_block + local;
+  if (tile >= (streaming ? str_tiles : ret_tiles)) return;
+  const int64_t row0 = (streaming ? int64_t(tile) : ret_tile0 + tile) * 8;
+  T* K = reinterpret_cast<T*>(c.k);
+  T* V = reinterpret_cast<T*>(c.v);
+  T vbuf[8];
+  int nvalid = 0;
+  for (int r = 0; r < 8; ++r) {
+    const int64_t row = row0 + r;
+    const int t = source_token(streaming, row, t0, T_, g.S, g.R);
+    if (t >= 0) {
+      const int64_t src = ((int64_t(b) * T_ + t) * g.Hkv + kvh) * D + d;
+      K[k_index(cache, c.rows, row, D, d)] = k[src];
+      vbuf[r] = v[src];
+      ++nvalid;
+    }
+  }
+  if (nvalid == 8) {
+    T* dst = V + v_index(cache, c.rows, row0, D, d);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) dst[r] = vbuf[r];
+  } else if (nvalid) {
+    for (int r = 0; r < 8; ++r) {
+      const int64_t row = row0 + r;
+      if (source_token(streaming, row, t0, T_, g.S, g.R) >= 0) V[v_index(cache, c.rows, row, D, d)] = vbuf[r];
+    }
+  }
+}
+
+__device__ inline float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// int4 group-128 quantisation of one vector held two values per lane (d = 2*lane,
+// 2*lane + 1).  Steps and rounding are those of the format: fp32 range, fp32 divide
+// by 15, fp16 round of scale and zero, fp32 (x - z) / s, round half to even, clamp.
+struct Q4 {
+  uint32_t q0, q1;
+  uint16_t s_bits, z_bits;
+};
+__device__ inline Q4 quantize_pair(float x0, float x1) {
+  const float mn = wave_min(fminf(x0, x1));
+  const float mx = wave_max(fmaxf(x0, x1));
+  const float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  const __half sh = __float2half_rn(s32);
+  const __half zh = __float2half_rn(mn);
+  const float s = __half2float(sh);
+  const float z = __half2float(zh);
+  Q4 r;
+  r.s_bits = __half_as_ushort(sh);
+  r.z_bits = __half_as_ushort(zh);
+  if (s == 0.0f) {
+    r.q0 = r.q1 = 0;
+  } else {
+    const float a = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x0, z), s)), 0.0f), 15.0f);
+    const float c = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x1, z), s)), 0.0f), 15.0f);
+    r.q0 = static_cast<uint32_t>(a);
+    r.q1 = static_cast<uint32_t>(c);
+  }
+  return r;
+}
+
+// One wavefront per (cache, 8-row tile); D = 128, bf16 input.
+__global__ void __launch_bounds__(256) k_append_int4(Geom g, LayerView lv, const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v, int T_, int64_t t0,
+                                                     int which, int64_t ret_tile0, int ret_tiles,
+                                                     int str_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nret = g.B * lv.n_ret;
+  const int y = blockIdx.y;
+  const bool streaming = y >= nret;
+  if (streaming && !(which & 2)) return;
+  if (!streaming && !(which & 1)) return;
+  if (tile >= (streaming ? str_tiles : ret_tiles)) return;
+  const int cache = streaming ? y - nret : y;
+  const int b = streaming ? cache / lv.n_str : cache / lv.n_ret;
+  const int idx = streaming ? cache % lv.n_str : cache % lv.n_ret;
+  const int kvh = streaming ? lv.str_kv[idx] : lv.ret_kv[idx];
+  const CacheRegion& c = streaming ? lv.str : lv.ret;
+  const int64_t row0 = (streaming ? int64_t(tile) : ret_tile0 + tile) * 8;
+  uint8_t* kc = reinterpret_cast<uint8_t*>(c.k);
+  uint32_t* vw = reinterpret_cast<uint32_t*>(c.v) + (cache * c.rows + row0) / 8 * 128;
+  uint32_t w0 = 0, w1 = 0, written = 0;
+  for (int r = 0; r < 8; ++r) {
+    const int64_t row = row0 + r;
+    const int t = source_token(streaming, row, t0, T_, g.S, g.R);
+    if (t < 0) continue;
+    const int64_t src = ((int64_t(b) * T_ + t) * g.Hkv + kvh) * 128 + 2 * lane;
+    const uint32_t kp = *reinterpret_cast<const uint32_t*>(k + src);
+    const uint32_t vp = *reinterpret_cast<const uint32_t*>(v + src);
+    const Q4 qk = quantize_pair(bf16_to_f32(kp & 0xffff), bf16_to_f32(kp >> 16));
+    const Q4 qv = quantize_pair(bf16_to_f32(vp & 0xffff), bf16_to_f32(vp >> 16));
+    kc[(cache * c.rows + row) * 64 + lane] = static_cast<uint8_t>(qk.q0 | (qk.q1 << 4));
+    if (lane == 0) {
+      uint16_t* km = c.k_meta + (cache * c.rows + row) * 2;
+      uint16_t* vm = c.v_meta + (cache * c.rows + row) * 2;
+      km[0] = qk.s_bits;
+      km[1] = qk.z_bits;
+      vm[0] = qv.s_bits;
+      vm[1] = qv.z_bits;
+    }
+    w0 |= qv.q0 << (4 * r);
+    w1 |= qv.q1 << (4 * r);
+    written |= 15u << (4 * r);
+  }
+  if (!written) return;
+  if (written != 0xffffffffu) {
+    w0 |= vw[2 * lane] & ~written;
+    w1 |= vw[2 * lane + 1] & ~written;
+  }
+  vw[2 * lane] = w0;
+  vw[2 * lane + 1] = w1;
+}
+
+template <int IO, int KVF>
+__global__ void k_read(Geom g, CacheRegion c, int64_t cache, int streaming, int64_t pos0, int n, int which,
+                       float* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(n) * g.D) return;
+  const int64_t p = pos0 + i / g.D;
+  const int d = static_cast<int>(i % g.D);
+  const int64_t row = streaming ? stream_slot(p, g.S, g.R) : p;
+  out[i] = which == 0 ? cache_k<IO, KVF>(c, cache, row, g.D, d) : cache_v<IO, KVF>(c, cache, row, g.D, d);
+}
+
+__global__ void k_read_int4(Geom g, CacheRegion c, int64_t cache, int streaming, int64_t pos0, int n, int which,
+                            uint8_t* __restrict__ codes, uint16_t* __restrict__ meta) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // one byte of codes
+  if (i >= int64_t(n) * 64) return;
+  const int64_t p = pos0 + i / 64;
+  const int kb = static_cast<int>(i % 64);
+  const int64_t row = streaming ? stream_slot(p, g.S, g.R) : p;
+  uint8_t byte;
+  if (which == 0) {
+    byte = reinterpret_cast<const uint8_t*>(c.k)[(cache * c.rows + row) * 64 + kb];
+  } else {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(c.v) + (cache * c.rows + (row & ~int64_t(7))) / 8 * 128;
+    const uint32_t lo = (w[2 * kb] >> (4 * (row & 7))) & 15u;
+    const uint32_t hi = (w[2 * kb + 1] >> (4 * (row & 7))) & 15u;
+    byte = static_cast<uint8_t>(lo | (hi << 4));
+  }
+  codes[i] = byte;
+  if (kb < 2) {
+    const uint16_t* m = (which == 0 ? c.k_meta : c.v_meta) + (cache * c.rows + row) * 2;
+    meta[(i / 64) * 2 + kb] = m[kb];
+  }
+}
+
+__global__ void k_zero_i32(int* p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// SplitMix64 finaliser (Steele, Lea and Flood, OOPSLA 2014).
+__device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+template <int IO>
+__global__ void k_synth(typename IoType<IO>::T* __restrict__ out, uint64_t key, uint64_t c0, uint64_t n) {
+  const float kScale = 0x1.bb67ae0000000p-16f;  // float32 nearest to sqrt(3) / 65536
+  for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x) {
+    const uint64_t w = mix64(key + (c0 + i + 1) * 0x9E3779B97F4A7C15ull);
+    const int s = static_cast<int>((w & 0xffff) + ((w >> 16) & 0xffff) + ((w >> 32) & 0xffff) + (w >> 48));
+    const float x = static_cast<float>(s - 131070) * kScale;
+    if constexpr (IO == DUO_DTYPE_F32) out[i] = x;
+    else out[i] = f32_to_bf16(x);
+  }
+}
+
+uint64_t host_mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, const void* v, int T, int64_t t0,
+                         int which, hipStream_t st) {
+  const int64_t first = t0 / 8, last = (t0 + T - 1) / 8;
+  const int ret_tiles = static_cast<int>(last - first + 1);
+  const int str_tiles = (g.S + g.R + 7) / 8;
+  const int ny = g.B * (lv.n_ret + lv.n_str);
+  if (ny == 0) return hipSuccess;
+  if (g.kvfmt == DUO_KV_INT4_G128) {
+    const int tiles = ret_tiles > str_tiles ? ret_tiles : str_tiles;
+    dim3 grid((tiles + 3) / 4, ny);
+    hipLaunchKernelGGL(k_append_int4, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), T, t0, which, first, ret_tiles, str_tiles);
+  } else {
+    const int per_block = 256 / g.D;
+    const int tiles = ret_tiles > str_tiles ? ret_tiles : str_tiles;
+    dim3 grid((tiles + per_block - 1) / per_block, ny);
+    if (g.io == DUO_DTYPE_F32)
+      hipLaunchKernelGGL(k_append<float>, grid, dim3(per_block * g.D), 0, st, g, lv, static_cast<const float*>(k),
+                         static_cast<const float*>(v), T, t0, which, first, ret_tiles, str_tiles);
+    else
+      hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(per_block * g.D), 0, st, g, lv,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), T, t0, which, first,
+                         ret_tiles, str_tiles);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0, int n,
+                       int which, float* out, hipStream_t st) {
+  const int64_t total = int64_t(n) * g.D;
+  dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  if (g.kvfmt == DUO_KV_INT4_G128)
+    hipLaunchKernelGGL((k_read<DUO_DTYPE_BF16, DUO_KV_INT4_G128>), grid, dim3(256), 0, st, g, c, cache,
+                       int(streaming), pos0, n, which, out);
+  else if (g.io == DUO_DTYPE_F32)
+    hipLaunchKernelGGL((k_read<DUO_DTYPE_F32, DUO_KV_SAME_AS_IO>), grid, dim3(256), 0, st, g, c, cache,
+                       int(streaming), pos0, n, which, out);
+  else
+    hipLaunchKernelGGL((k_read<DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO>), grid, dim3(256), 0, st, g, c, cache,
+                       int(streaming), pos0, n, which, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,
+                            int n, int which, uint8_t* codes, uint16_t* meta, hipStream_t st) {
+  const int64_t total = int64_t(n) * 64;
+  hipLaunchKernelGGL(k_read_int4, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, g, c, cache,
+                     int(streaming), pos0, n, which, codes, meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_i32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, uint64_t c0, uint64_t n,
+                        hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const uint64_t key = host_mix64((seed << 32) | stream);
+  uint64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (dtype == DUO_DTYPE_F32)
+    hipLaunchKernelGGL(k_synth<DUO_DTYPE_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<float*>(out), key, c0, n);
+  else
+    hipLaunchKernelGGL(k_synth<DUO_DTYPE_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<uint16_t*>(out), key, c0, n);
+  return hipGetLastError();
+}
+
+}  // namespace duo

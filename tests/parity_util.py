@@ -1,0 +1,119 @@
+"""Helpers shared by the GPU parity tests: run a workload through the HIP path (via the
+C-ABI binding) and through the oracle on the same seeded inputs, and compare."""
+
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+from mixed_head_kv_amd import inputs as I
+from oracle import attention as OA
+from oracle import int4 as OQ
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device_synth(w: I.Workload, layer: int, kind: str, pos0: int, T: int):
+    """Q/K/V rows [T, H, D] for positions [pos0, pos0+T) generated on the device by the
+    library's fill kernel (same definition as inputs.synth)."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    H = w.n_q_heads if kind == "q" else w.n_kv_heads
+    dt = torch.float32 if w.io_dtype == "f32" else torch.bfloat16
+    t = torch.empty((T, H, w.head_dim), dtype=dt, device="cuda")
+    B.duo_synth_fill(t, B.DUO_DTYPE_F32 if w.io_dtype == "f32" else B.DUO_DTYPE_BF16, w.seed,
+                     layer * 4 + I.KIND_STREAM[kind], pos0 * H * w.head_dim, T * H * w.head_dim)
+    return t
+
+
+def host_rows(w: I.Workload, layer: int, kind: str, pos0: int, T: int) -> np.ndarray:
+    H = w.n_q_heads if kind == "q" else w.n_kv_heads
+    return OA.upcast(I.synth(w.seed, layer, kind, pos0, T, H, w.head_dim, w.io_dtype), w.io_dtype)
+
+
+def host_history(w: I.Workload, layer: int, kind: str, L: int) -> np.ndarray:
+    """Full K or V history [L, Hkv, D] as the caches hold it: exact for bf16/f32, the
+    oracle codec's dequantised values for int4."""
+    raw = I.synth(w.seed, layer, kind, 0, L, w.n_kv_heads, w.head_dim, w.io_dtype)
+    if w.kv_format == "int4":
+        codes, s, z = OQ.quantize(raw)
+        return OQ.dequantize(codes, s, z).astype(np.float64)
+    return OA.upcast(raw, w.io_dtype)
+
+
+def q_rows(w: I.Workload, layer: int, rows) -> np.ndarray:
+    """Q [len(rows), Hq, D] at arbitrary absolute positions (stored dtype)."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    HD = w.n_q_heads * w.head_dim
+    counters = rows[:, None] * np.uint64(HD) + np.arange(HD, dtype=np.uint64)[None, :]
+    x = I.values_f32(w.seed, layer * 4 + I.KIND_STREAM["q"], counters)
+    x = I.f32_to_bf16_bits(x) if w.io_dtype == "bf16" else x
+    return x.reshape(len(rows), w.n_q_heads, w.head_dim)
+
+
+def to_f64(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_layer(w: I.Workload, chunks, decode_steps: int, layer: int = 0, kv=None, append_only_chunks=False):
+    """Prefill the chunks (or append them, for int4 / bulk fill) and run decode steps on
+    one layer.  Returns (kv, prefill outputs [sum(chunks), Hq, D] or None, decode outputs
+    [steps, Hq, D], total tokens)."""
+    import torch
+    from mixed_head_kv_amd.binding import DuoKV
+    if kv is None:
+        kv = DuoKV.for_workload(w)
+    total = sum(chunks) + decode_steps
+    Q = device_synth(w, layer, "q", 0, total)
+    K = device_synth(w, layer, "k", 0, total)
+    V = device_synth(w, layer, "v", 0, total)
+    pre = []
+    t = 0
+    for T in chunks:
+        if append_only_chunks:
+            kv.append(layer, K[t:t + T], V[t:t + T])
+        else:
+            pre.append(kv.prefill(layer, Q[t:t + T], K[t:t + T], V[t:t + T]))
+        t += T
+    dec = []
+    for _ in range(decode_steps):
+        dec.append(kv.decode(layer, Q[t], K[t], V[t]))
+        t += 1
+    torch.cuda.synchronize()
+    pre_out = torch.cat(pre, 0) if pre else None
+    dec_out = torch.stack(dec, 0) if dec else None
+    return kv, pre_out, dec_out, total
+
+
+def oracle_rows(w: I.Workload, layer: int, rows, total: int, heads=None) -> np.ndarray:
+    """Oracle outputs [len(rows), Hq, D] at absolute positions `rows`."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Kh = host_history(w, layer, "k", total)
+    Vh = host_history(w, layer, "v", total)
+    Qh = OA.upcast(q_rows(w, layer, rows), w.io_dtype)
+    return OA.layer_attention(Qh, rows, Kh, Vh, w.mask(layer), w.sink, w.recent, heads=heads)
+
+
+def compare(name: str, got: np.ndarray, ref: np.ndarray, tol: float):
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    say(f"  {name}: max-abs err {err:.3e} (tol {tol:g}) over {got.size} values")
+    assert err <= tol, f"{name}: max-abs error {err} > {tol}"
+    return err
+
+
+class Timer:
+    def __enter__(self):
+        self.t = time.perf_counter()
+        return self
+
+    def __exit__(self, *a):
+        self.dt = time.perf_counter() - self.t

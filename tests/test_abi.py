@@ -1,0 +1,155 @@
+"""The C-ABI library on the CPU: it loads, exports every function the public headers
+declare, and rejects bad arguments before touching the GPU (no compute calls here)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mixed_head_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libduo_attn.so not built (python -m mixed_head_kv_amd.build)")
+    return B.lib()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+\**(duo_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_headers_declare_the_boundary():
+    names = declared_functions()
+    for n in ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
+              "duo_kv_free", "duo_last_error", "duo_synth_fill"]:
+        assert n in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib_or_skip()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def _cfg(**kw):
+    base = dict(n_layers=2, batch=1, n_q_heads=8, n_kv_heads=4, head_dim=128, sink=4, recent=16,
+                max_context=1000, io_dtype=B.DUO_DTYPE_BF16, kv_format=B.DUO_KV_SAME_AS_IO,
+                retrieval_mask=np.array([[1, 0, 1, 0], [0, 0, 1, 1]]))
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def _bytes(cfg):
+    out = ctypes.c_uint64()
+    rc = B.lib().duo_kv_bytes(ctypes.byref(cfg), ctypes.byref(out))
+    return rc, out.value
+
+
+def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask):
+    al = lambda x, a: (x + a - 1) // a * a
+    cap, nslot = al(max_ctx, 64), al(S + R, 64)
+    vec = D // 2 if int4 else D * esize
+    off = 0
+    for l in range(n_layers):
+        nr = int(mask[l].sum())
+        ns = hkv - nr
+        for rows in (batch * nr * cap, batch * nr * cap, batch * ns * nslot, batch * ns * nslot):
+            off = al(off + rows * vec, 256)
+        if int4:
+            for rows in (batch * nr * cap, batch * nr * cap, batch * ns * nslot, batch * ns * nslot):
+                off = al(off + rows * 4, 256)
+    off = al(off + batch * hq * 1024 * (D + 2) * 4, 256)
+    off = al(off + batch * hkv * 4, 256)
+    return off
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(io_dtype=B.DUO_DTYPE_F32, head_dim=64, max_context=513),
+    dict(kv_format=B.DUO_KV_INT4_G128, max_context=3_300_000),
+    dict(batch=3, sink=0, recent=1),
+])
+def test_kv_bytes_matches_layout_arithmetic(kw):
+    _lib_or_skip()
+    cfg = _cfg(**kw)
+    rc, nbytes = _bytes(cfg)
+    assert rc == B.DUO_OK
+    mask = np.array([[1, 0, 1, 0], [0, 0, 1, 1]])
+    assert nbytes == expected_bytes(cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.sink,
+                                    cfg.recent, cfg.max_context, 4 if cfg.io_dtype == 0 else 2,
+                                    cfg.kv_format == 1, mask)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_layers=0), B.DUO_E_INVALID),
+    (dict(batch=0), B.DUO_E_INVALID),
+    (dict(n_q_heads=6), B.DUO_E_INVALID),
+    (dict(n_q_heads=4 * 17), B.DUO_E_UNSUPPORTED),
+    (dict(head_dim=96), B.DUO_E_UNSUPPORTED),
+    (dict(sink=-1), B.DUO_E_INVALID),
+    (dict(recent=0), B.DUO_E_INVALID),
+    (dict(max_context=0), B.DUO_E_INVALID),
+    (dict(io_dtype=7), B.DUO_E_INVALID),
+    (dict(kv_format=3), B.DUO_E_INVALID),
+    (dict(kv_format=B.DUO_KV_INT4_G128, io_dtype=B.DUO_DTYPE_F32), B.DUO_E_UNSUPPORTED),
+    (dict(kv_format=B.DUO_KV_INT4_G128, head_dim=64), B.DUO_E_UNSUPPORTED),
+    (dict(retrieval_mask=np.array([[2, 0, 0, 0], [0, 0, 0, 0]])), B.DUO_E_INVALID),
+    (dict(n_kv_heads=65, n_q_heads=65, retrieval_mask=np.zeros((2, 65))), B.DUO_E_INVALID),
+])
+def test_bad_configs_are_rejected(kw, code):
+    _lib_or_skip()
+    rc, _ = _bytes(_cfg(**kw))
+    assert rc == code
+    assert B.duo_last_error()
+    h = ctypes.c_void_p()
+    rc2 = B.lib().duo_kv_init(ctypes.byref(_cfg(**kw)), ctypes.c_void_p(256), 1 << 40, None, ctypes.byref(h))
+    assert rc2 == code and not h.value
+
+
+def test_init_rejects_small_or_misaligned_workspace():
+    L = _lib_or_skip()
+    cfg = _cfg()
+    _, need = _bytes(cfg)
+    h = ctypes.c_void_p()
+    assert L.duo_kv_init(ctypes.byref(cfg), ctypes.c_void_p(4096), need - 1, None, ctypes.byref(h)) == B.DUO_E_CAPACITY
+    assert L.duo_kv_init(ctypes.byref(cfg), ctypes.c_void_p(4096 + 16), need, None, ctypes.byref(h)) == B.DUO_E_INVALID
+    assert L.duo_kv_init(ctypes.byref(cfg), None, need, None, ctypes.byref(h)) == B.DUO_E_INVALID
+    assert L.duo_kv_init(ctypes.byref(cfg), ctypes.c_void_p(4096), need, None, None) == B.DUO_E_INVALID
+    assert not h.value
+
+
+def test_null_handle_calls_fail_cleanly():
+    L = _lib_or_skip()
+    p = ctypes.c_void_p(4096)
+    assert L.duo_prefill(None, 0, p, p, p, 4, p, None) == B.DUO_E_INVALID
+    assert L.duo_kv_append(None, 0, p, p, 4, None) == B.DUO_E_INVALID
+    assert L.duo_decode(None, 0, p, p, p, p, None) == B.DUO_E_INVALID
+    n = ctypes.c_int64()
+    assert L.duo_kv_length(None, 0, ctypes.byref(n)) == B.DUO_E_INVALID
+    assert L.duo_kv_read(None, 0, 0, 0, 0, 0, 1, p, None) == B.DUO_E_INVALID
+    L.duo_kv_free(None)
+    assert L.duo_synth_fill(None, 1, 1, 0, 0, 10, None) == B.DUO_E_INVALID
+    assert L.duo_synth_fill(ctypes.c_void_p(4098), 1, 1, 0, 0, 10, None) == B.DUO_E_INVALID
+    assert L.duo_synth_fill(p, 5, 1, 0, 0, 10, None) == B.DUO_E_INVALID
+    assert L.duo_synth_fill(p, 1, 1 << 40, 0, 0, 10, None) == B.DUO_E_INVALID
+
+
+def test_product_package_has_no_oracle_or_cpu_fallback():
+    """The HIP path never reaches the oracle: no module of the package names it."""
+    pkg = os.path.join(ROOT, "mixed_head_kv_amd")
+    for fn in glob.glob(os.path.join(pkg, "**", "*.*"), recursive=True):
+        if fn.endswith((".py", ".hip", ".cpp", ".h")):
+            text = open(fn).read()
+            assert "import oracle" not in text and "from oracle" not in text, fn

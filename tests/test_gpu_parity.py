@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on identical
+seeded inputs.  Tolerances: max-abs 2e-2 for bf16 I/O, 1e-5 for fp32 I/O; caches and
+int4 codes bit-exact."""
+
+import numpy as np
+import pytest
+
+from mixed_head_kv_amd import inputs as I
+from oracle import attention as OA
+from oracle import int4 as OQ
+
+from parity_util import TOL, compare, device_synth, host_history, oracle_rows, q_rows, run_layer, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, seed, hq, hkv, D, io, S, R, ctx, steps, nr, fmt="same", layers=1, fixed=None):
+    return I.Workload(name, seed, layers, hq, hkv, D, io, fmt, S, R, ctx, 0, steps, nr, fixed)
+
+
+SMALL = {
+    "mha_bf16": W("mha_bf16", 11, 8, 8, 128, "bf16", 8, 32, 557, 20, 3),
+    "gqa_bf16": W("gqa_bf16", 12, 16, 4, 128, "bf16", 4, 64, 1024, 12, 2),
+    "mha_f32_d128": W("mha_f32_d128", 13, 4, 4, 128, "f32", 2, 16, 300, 9, 2),
+    "gqa_bf16_d64": W("gqa_bf16_d64", 14, 8, 2, 64, "bf16", 0, 8, 200, 7, 1),
+    "mha_f32_d64_nosink": W("mha_f32_d64_nosink", 15, 2, 2, 64, "f32", 0, 1, 70, 5, 1),
+    "all_streaming_bf16": W("all_streaming_bf16", 16, 4, 2, 128, "bf16", 16, 48, 400, 6, 0),
+    "all_retrieval_bf16": W("all_retrieval_bf16", 17, 4, 2, 128, "bf16", 16, 48, 400, 6, 2),
+}
+CHUNKS = {
+    "mha_bf16": [100, 156, 1, 300],
+    "gqa_bf16": [257, 255, 512],
+    "mha_f32_d128": [64, 1, 235],
+    "gqa_bf16_d64": [3, 197],
+    "mha_f32_d64_nosink": [70],
+    "all_streaming_bf16": [40, 360],
+    "all_retrieval_bf16": [400],
+}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_synth_matches_host_generator(torch_cuda, dtype):
+    w = W("synth", 99, 4, 2, 64, dtype, 1, 1, 10, 0, 1)
+    say(f"synth {dtype}")
+    got = device_synth(w, 3, "k", 5, 77).cpu()
+    ref = I.synth(99, 3, "k", 5, 77, 2, 64, dtype)
+    if dtype == "bf16":
+        got = got.view(torch_cuda.int16).numpy().view(np.uint16)
+    else:
+        got = got.numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa_bf16", "mha_f32_d128", "gqa_bf16_d64"])
+def test_append_then_read_is_bit_exact(torch_cuda, name):
+    w = SMALL[name]
+    chunks = CHUNKS[name]
+    say(f"append/read {name} chunks={chunks}")
+    kv, _, _, total = run_layer(w, chunks, 0, append_only_chunks=True)
+    mask = w.mask(0)
+    for which, kind in ((0, "k"), (1, "v")):
+        hist = host_history(w, 0, kind, total)
+        for g in range(w.n_kv_heads):
+            if mask[g]:
+                got = to_f64(kv.read(0, g, which, 0, total))
+                assert np.array_equal(got, hist[:, g]), (kind, g)
+            else:
+                last = total - 1
+                held = [p for p in range(total) if p < w.sink or last - p < w.recent]
+                for p in held:
+                    got = to_f64(kv.read(0, g, which, p, 1))
+                    assert np.array_equal(got[0], hist[p, g]), (kind, g, p)
+
+
+def test_int4_append_codes_and_dequant_are_bit_exact(torch_cuda):
+    w = W("int4", 21, 8, 4, 128, "bf16", 4, 32, 0, 0, 2, fmt="int4")
+    chunks = [3, 50, 8, 1, 100, 9]
+    total = sum(chunks)
+    w = w.scaled(context=total)
+    say(f"int4 append chunks={chunks}")
+    kv, _, _, _ = run_layer(w, chunks, 0, append_only_chunks=True)
+    mask = w.mask(0)
+    for which, kind in ((0, "k"), (1, "v")):
+        raw = I.synth(w.seed, 0, kind, 0, total, w.n_kv_heads, 128, "bf16")
+        codes, s, z = OQ.quantize(raw)
+        deq = OQ.dequantize(codes, s, z)
+        for g in range(w.n_kv_heads):
+            pos = list(range(total)) if mask[g] else [p for p in range(total) if p < w.sink or total - 1 - p < w.recent]
+            for a in ([pos] if mask[g] else [[p] for p in pos]):
+                c_dev, m_dev = kv.read_int4(0, g, which, a[0], len(a))
+                c_dev = c_dev.cpu().numpy()
+                m_dev = m_dev.cpu().numpy().view(np.uint16)
+                assert np.array_equal(c_dev, codes[a, g]), (kind, g, a[0])
+                assert np.array_equal(m_dev[:, 0], s[a, g].view(np.uint16)), (kind, g, "scale")
+                assert np.array_equal(m_dev[:, 1], z[a, g].view(np.uint16)), (kind, g, "zero")
+                x = kv.read(0, g, which, a[0], len(a)).cpu().numpy()
+                assert np.array_equal(x.view(np.uint32), deq[a, g].view(np.uint32)), (kind, g, "dequant")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prefill_and_decode_match_oracle(torch_cuda, name):
+    w = SMALL[name]
+    chunks = CHUNKS[name]
+    say(f"prefill+decode {name} chunks={chunks} steps={w.decode_steps}")
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    L = sum(chunks)
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare(f"{name} prefill", to_f64(pre), ref[:L], TOL[w.io_dtype])
+    compare(f"{name} decode", to_f64(dec), ref[L:], TOL[w.io_dtype])
+    assert kv.length(0) == total
+
+
+def test_int4_decode_matches_oracle(torch_cuda):
+    w = W("int4_gqa", 22, 8, 4, 128, "bf16", 4, 32, 700, 10, 2, fmt="int4")
+    say("int4 decode")
+    kv, _, dec, total = run_layer(w, [300, 400], w.decode_steps, append_only_chunks=True)
+    ref = oracle_rows(w, 0, np.arange(700, total), total)
+    compare("int4 decode", to_f64(dec), ref, TOL["bf16"])
+
+
+def test_decode_without_new_kv_uses_appended_token(torch_cuda):
+    import torch
+    w = SMALL["gqa_bf16"]
+    say("decode with NULL k/v")
+    kv, _, _, total = run_layer(w, [200], 0)
+    q = device_synth(w, 0, "q", 0, 203)
+    k = device_synth(w, 0, "k", 0, 203)
+    v = device_synth(w, 0, "v", 0, 203)
+    kv.append(0, k[200:203], v[200:203])
+    out = kv.decode(0, q[202])
+    torch.cuda.synchronize()
+    ref = oracle_rows(w, 0, [202], 203)
+    compare("null-kv decode", to_f64(out)[None], ref, TOL["bf16"])
+
+
+def test_tiny_workload_exact_config(torch_cuda):
+    """4 heads (0 and 2 retrieval), head_dim 64, fp32, 512-token causal prefill, 16 decode steps."""
+    w = I.WORKLOADS["tiny_mha_f32_512"]
+    say("tiny_mha_f32_512")
+    kv, pre, dec, total = run_layer(w, [512], 16)
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare("tiny prefill", to_f64(pre), ref[:512], TOL["f32"])
+    compare("tiny decode", to_f64(dec), ref[512:], TOL["f32"])
+
+
+def test_outputs_are_bitwise_repeatable(torch_cuda):
+    w = SMALL["gqa_bf16"]
+    say("repeatability")
+    _, p1, d1, _ = run_layer(w, CHUNKS["gqa_bf16"], 5)
+    _, p2, d2, _ = run_layer(w, CHUNKS["gqa_bf16"], 5)
+    assert torch_cuda.equal(p1, p2) and torch_cuda.equal(d1, d2)
+
+
+def test_failed_calls_leave_state_unchanged(torch_cuda):
+    from mixed_head_kv_amd import binding as B
+    w = SMALL["mha_bf16"].scaled(context=64, decode_steps=0)
+    say("error paths")
+    kv = B.DuoKV.for_workload(w)
+    k = device_synth(w, 0, "k", 0, 65)
+    v = device_synth(w, 0, "v", 0, 65)
+    q = device_synth(w, 0, "q", 0, 65)
+    kv.prefill(0, q[:60], k[:60], v[:60])
+    with pytest.raises(B.DuoError) as e:
+        kv.prefill(0, q[:5], k[:5], v[:5])
+    assert e.value.code == B.DUO_E_CAPACITY and kv.length(0) == 60
+    with pytest.raises(B.DuoError) as e:
+        B.duo_decode(kv.h, 0, q[0], k[0], None, q[1])
+    assert e.value.code == B.DUO_E_STATE and kv.length(0) == 60
+    with pytest.raises(B.DuoError) as e:
+        B.duo_prefill(kv.h, 1, q, k, v, 4, q)
+    assert e.value.code == B.DUO_E_INVALID
+    with pytest.raises(B.DuoError) as e:
+        kv.read(0, int(np.nonzero(~w.mask(0))[0][0]), 0, 20, 1)  # evicted from a streaming cache
+    assert e.value.code == B.DUO_E_INVALID
+    kv.prefill(0, q[60:64], k[60:64], v[60:64])
+    assert kv.length(0) == 64
+
+
+def test_llama2_7b_mha_32k_layer(torch_cuda):
+    """32 heads (8 retrieval), head_dim 128, bf16, 8 prefill chunks of 4096 and 128 decode
+    steps.  Every decode output is checked; prefill rows are sampled: the first 64 and last
+    64 rows of every chunk, +-R rows around every chunk boundary, 128 seeded rows per chunk."""
+    w = I.WORKLOADS["llama2_7b_mha_32k"]
+    say("llama2_7b_mha_32k")
+    chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    rng = np.random.default_rng(0)
+    rows = set()
+    for c in range(len(chunks)):
+        a = c * w.prefill_chunk
+        b = a + w.prefill_chunk
+        rows |= set(range(a, a + 64)) | set(range(b - 64, b))
+        rows |= set(range(max(0, a - w.recent - 2), min(w.context, a + w.recent + 2)))
+        rows |= set(rng.integers(a, b, 128).tolist())
+    rows = np.array(sorted(rows))
+    ref_dec = oracle_rows(w, 0, np.arange(w.context, total), total)
+    compare("32k decode", to_f64(dec), ref_dec, TOL["bf16"])
+    ref_pre = oracle_rows(w, 0, rows, total)
+    compare("32k prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
