@@ -8,12 +8,10 @@
 // every key j <= i; a streaming head's query sees the sinks j < S and the recent
 // window i - j < R.  Softmax runs in the base-2 domain (scores pre-multiplied by
 // scale * log2 e) with an online running max and sum.
-#include "duo_kernels.h"
+#include "decode_common.h"
 
 namespace duo {
 namespace {
-
-constexpr float kNegInf = -__builtin_huge_valf();
 
 // One thread per query row (64 rows per workgroup), online softmax over the row's
 // visible keys.  Keys before t0 come from the caches as they stood before the chunk;
@@ -81,89 +79,6 @@ __global__ void __launch_bounds__(64) k_prefill_valu(Geom g, LayerView lv, const
   const int64_t orow = ((int64_t(b) * T + t) * g.Hq + h) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) io_store<IO>(out, orow + d, o[d] * inv);
-}
-
-// ---- split-K decode -----------------------------------------------------------------
-
-struct DecodeItem {
-  int b, kvh, split, nsplit;
-  bool retrieval;
-  int64_t cache, key0, key1;  // cache rows [key0, key1) of this split
-};
-
-// Workgroups are laid out retrieval splits first, then streaming splits, per sequence.
-__device__ inline DecodeItem decode_item(const Geom& g, const LayerView& lv, const DecodePlan& p, int item) {
-  DecodeItem it;
-  const int per_b = lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s;
-  it.b = item / per_b;
-  int r = item % per_b;
-  int64_t nkeys;
-  int chunk, idx;
-  if (r < lv.n_ret * p.nsplit_r) {
-    it.retrieval = true;
-    idx = r / p.nsplit_r;
-    it.split = r % p.nsplit_r;
-    it.nsplit = p.nsplit_r;
-    chunk = p.chunk_r;
-    nkeys = p.t + 1;
-    it.kvh = lv.ret_kv[idx];
-    it.cache = int64_t(it.b) * lv.n_ret + idx;
-  } else {
-    r -= lv.n_ret * p.nsplit_r;
-    it.retrieval = false;
-    idx = r / p.nsplit_s;
-    it.split = r % p.nsplit_s;
-    it.nsplit = p.nsplit_s;
-    chunk = p.chunk_s;
-    nkeys = p.t + 1 < g.S + g.R ? p.t + 1 : g.S + g.R;  // valid slots are [0, nkeys)
-    it.kvh = lv.str_kv[idx];
-    it.cache = int64_t(it.b) * lv.n_str + idx;
-  }
-  it.key0 = int64_t(it.split) * chunk;
-  it.key1 = it.key0 + chunk < nkeys ? it.key0 + chunk : nkeys;
-  return it;
-}
-
-__device__ inline float* partial_ptr(const Geom& g, const DecodePlan& p, int b, int h, int split) {
-  return p.partials + ((int64_t(b) * g.Hq + h) * kMaxSplits + split) * (g.D + 2);
-}
-
-// Merge of the split partials of one KV head's G query heads: (m_s, l_s, o_s) in the
-// base-2 domain; o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <int IO>
-__device__ void merge_splits(const Geom& g, const DecodePlan& p, int b, int kvh, int nsplit, void* out) {
-  const int pairs = g.G * g.D;
-  for (int e = threadIdx.x; e < pairs; e += blockDim.x) {
-    const int i = e / g.D, d = e % g.D;
-    const int h = kvh * g.G + i;
-    float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, partial_ptr(g, p, b, h, s)[0]);
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = partial_ptr(g, p, b, h, s);
-      const float w = exp2f(ps[0] - M);
-      L = fmaf(w, ps[1], L);
-      acc = fmaf(w, ps[2 + d], acc);
-    }
-    io_store<IO>(out, (int64_t(b) * g.Hq + h) * g.D + d, acc / L);
-  }
-}
-
-// Returns true in every thread of the workgroup that arrived last for (b, kvh); the
-// partials of all splits are then visible to it.  Resets the counter for the next call.
-__device__ inline bool last_arrival(int* counter, int nsplit) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(counter, 1);
-    s_last = prev == nsplit - 1;
-    if (s_last) atomicExch(counter, 0);
-  }
-  __syncthreads();
-  const bool last = s_last;
-  if (last) __threadfence();
-  return last;
 }
 
 // One workgroup (256 threads) per (sequence, KV head, split).  Scores of 256 keys at a
@@ -259,10 +174,10 @@ __global__ void __launch_bounds__(256) k_decode_valu(Geom g, LayerView lv, Decod
     if (e < G * D) {
       const int i = e / D, d = e % D;
       float* ps = partial_ptr(g, p, it.b, it.kvh * G + i, it.split);
-      ps[2 + d] = acc[a];
+      store_coherent(ps + 2 + d, acc[a]);
       if (d == 0) {
-        ps[0] = m_run[i];
-        ps[1] = l_run[i];
+        store_coherent(ps, m_run[i]);
+        store_coherent(ps + 1, l_run[i]);
       }
     }
   }

@@ -1,0 +1,269 @@
+// Split-K flash decoding on bf16 MFMA for gfx950 (head_dim 128).
+//
+// One decoding step of one layer: every retrieval KV head attends over its full cache
+// (t + 1 rows) and every streaming KV head over its sink + recent slots, one launch for
+// both kinds (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference
+// with Retrieval and Streaming Heads", abstract: full KV cache for retrieval heads, a
+// constant-length cache for streaming heads, decoding speed-up).  Each workgroup takes
+// one key range of one KV head for all G query heads of that KV head (GQA shares every
+// K/V byte read), keeps an online softmax in the base-2 domain, and writes an fp32
+// partial (m, l, o); the last workgroup of each KV head merges the partials.
+//
+// Per wavefront, 32 keys at a time, with v_mfma_f32_16x16x32_bf16:
+//   S^T[16 keys x 16 queries] = K[16 keys x 128] * Q^T   (two tiles, 4 k-steps each)
+//   O^T[16 d x 16 queries]  += V^T[16 d x 32 keys] * P^T  (8 d-blocks)
+// Query columns beyond G are zero and ignored.  Tile rows are loaded in the key order
+// that makes each lane's 8 scores the 8 consecutive keys that lane then needs as the
+// B operand of P*V, so probabilities never leave registers; V is read from the cache's
+// d-major 8-key tiles, which already are the A-operand order of V^T.
+#include "decode_common.h"
+
+namespace duo {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+struct Tile {
+  u32x4 k0[4], k1[4];  // K rows for the two 16-key MFMA tiles, 4 k-steps each
+  u32x4 v[8];          // V^T operand for the 8 d-blocks
+};
+
+// Loads the 32-key tile starting at cache row `base`.  Lane l (row r = l % 16, group
+// g = l / 16) reads key base + 8*(r/4) + (r%4) (tile 0) and that + 4 (tile 1), dims
+// 32g .. 32g+31, and the V^T rows d = 16j + r of the 8-key block base + 8g.  The K
+// row `new_row` (the token being appended in this step, or -1) is read from k_new
+// instead of the cache; its V element is patched in by patch_v at the point of use,
+// so nothing here waits on the loads it issues.
+__device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                 int64_t cache_row0, int64_t base, int r, int grp, int64_t new_row,
+                                 const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
+  const int64_t key0 = base + 8 * (r >> 2) + (r & 3);
+  const uint16_t* k0p = key0 == new_row ? k_new : K + (cache_row0 + key0) * 128;
+  const uint16_t* k1p = key0 + 4 == new_row ? k_new : K + (cache_row0 + key0 + 4) * 128;
+  const u32x4* k0 = reinterpret_cast<const u32x4*>(k0p + 32 * grp);
+  const u32x4* k1 = reinterpret_cast<const u32x4*>(k1p + 32 * grp);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    t.k0[s] = __builtin_nontemporal_load(k0 + s);
+    t.k1[s] = __builtin_nontemporal_load(k1 + s);
+  }
+  const int64_t b8 = base + 8 * grp;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(V + (cache_row0 + b8) * 128) + r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t.v[j] = __builtin_nontemporal_load(vb + 16 * j);
+}
+
+// Replace the V element of row `new_row` (inside this lane's 8-key block) by v_new.
+__device__ inline void patch_v(Tile& t, int64_t base, int r, int grp, int64_t new_row,
+                               const uint16_t* __restrict__ v_new) {
+  const int64_t e = new_row - (base + 8 * grp);
+  if (e < 0 || e >= 8) return;
+  const int w = static_cast<int>(e >> 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t x = v_new[16 * j + r];
+    const uint32_t word = t.v[j][w];
+    t.v[j][w] = (e & 1) ? ((word & 0xffffu) | (x << 16)) : ((word & 0xffff0000u) | x);
+  }
+}
+
+// Merge of the split partials of one KV head (run by the last workgroup to finish):
+// every (m_s, l_s) is loaded at once into LDS, the weights 2^(m_s - M) are formed per
+// query, then each thread sums its output elements over the splits with independent
+// loads in flight.  `scratch` holds G * nsplit * 2 floats.
+__device__ void merge_splits_wide(const Geom& g, const DecodePlan& p, int b, int kvh, int nsplit, float* scratch,
+                                  uint16_t* __restrict__ out) {
+  const int G = g.G;
+  float* w = scratch;                 // [G][nsplit] weights, first m then 2^(m - M)
+  float* lsum = scratch + G * nsplit; // [G][nsplit] l
+  for (int e = threadIdx.x; e < G * nsplit; e += 256) {
+    const int i = e / nsplit, s = e % nsplit;
+    const float* pp = partial_ptr(g, p, b, kvh * G + i, s);
+    w[e] = load_coherent(pp);
+    lsum[e] = load_coherent(pp + 1);
+  }
+  __syncthreads();
+  __shared__ float s_M[DUO_MAX_GROUP], s_L[DUO_MAX_GROUP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = wave; i < G; i += 4) {
+    float M = kNegInf;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, w[i * nsplit + s]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.0f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float x = exp2f(w[i * nsplit + s] - M);
+      w[i * nsplit + s] = x;
+      L = fmaf(x, lsum[i * nsplit + s], L);
+    }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (lane == 0) s_L[i] = L;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * 128; e += 256) {
+    const int i = e >> 7, d = e & 127;
+    const float* base = partial_ptr(g, p, b, kvh * G + i, 0) + 2 + d;
+    const int64_t stride = 130;
+    float acc = 0.0f;
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = load_coherent(base + (s + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(w[i * nsplit + s + u], x[u], acc);
+    }
+    for (; s < nsplit; ++s) acc = fmaf(w[i * nsplit + s], load_coherent(base + s * stride), acc);
+    out[(int64_t(b) * g.Hq + kvh * G + i) * 128 + d] = f32_to_bf16(acc / s_L[i]);
+  }
+}
+
+__global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, DecodePlan p,
+                                                       const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_o[4][16][129];  // also the merge scratch (G * nsplit * 2 floats)
+
+  const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int G = g.G;
+  const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(c.k);
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(c.v);
+  const int64_t row0 = it.cache * c.rows;
+  // fused append of this step's token: retrieval row t or streaming slot new_slot
+  const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
+  const uint16_t* k_new = p.k_new ? p.k_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
+  const uint16_t* v_new = p.v_new ? p.v_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
+  if (new_row >= it.key0 && new_row < it.key1 && threadIdx.x < 128) {
+    // no workgroup reads this row from the cache in this launch: the one that covers it
+    // takes it from the inputs, so the cache write can go out at once
+    uint16_t* Kw = reinterpret_cast<uint16_t*>(c.k);
+    uint16_t* Vw = reinterpret_cast<uint16_t*>(c.v);
+    const int d = threadIdx.x;
+    Kw[(row0 + new_row) * 128 + d] = k_new[d];
+    Vw[v_index(it.cache, c.rows, new_row, 128, d)] = v_new[d];
+  }
+
+  // Q^T operand: column r = query head kvh*G + r (zero beyond G), dims 32g + 8s .. +7.
+  u32x4 qop[4];
+  {
+    const bool real = r < G;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t(it.b) * g.Hq + it.kvh * G + (real ? r : 0)) * 128 +
+                                                     32 * grp);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = real ? qp[s] : u32x4{0, 0, 0, 0};
+  }
+
+  float m = kNegInf, l = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const float sl2 = g.scale_log2;
+  int64_t base = it.key0 + 32 * wave;
+  Tile cur, nxt;
+  if (base < it.key1) load_tile(cur, K, V, row0, base, r, grp, new_row, k_new, v_new);
+  for (; base < it.key1; base += 128) {
+    const int64_t next = base + 128;
+    if (next < it.key1) load_tile(nxt, K, V, row0, next, r, grp, new_row, k_new, v_new);
+    if (new_row >= base && new_row < base + 32) patch_v(cur, base, r, grp, new_row, v_new);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      s0 = mfma16(cur.k0[s], qop[s], s0);
+      s1 = mfma16(cur.k1[s], qop[s], s1);
+    }
+    // lane holds scores of keys base + 8*grp + 0..7 for query r
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    const int64_t kfirst = base + 8 * grp;
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sc[i] = kfirst + i < it.key1 ? sc[i] * sl2 : kNegInf;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sc[i] = exp2f(sc[i] - mn);
+      ps += sc[i];
+    }
+    l = l * alpha + ps;
+    const u32x4 pb = {pack_bf16(sc[0], sc[1]), pack_bf16(sc[2], sc[3]), pack_bf16(sc[4], sc[5]),
+                      pack_bf16(sc[6], sc[7])};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j] * alpha);
+    cur = nxt;
+  }
+
+  // Combine the four wavefronts: lane sums over its group, then across waves in LDS.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (grp == 0) {
+    s_m[wave][r] = m;
+    s_l[wave][r] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][r][16 * j + 4 * grp + i] = o[j][i];
+  __syncthreads();
+
+  const int pairs = G * 128;
+  for (int e = threadIdx.x; e < pairs; e += 256) {
+    const int qi = e >> 7, d = e & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][qi]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
+      L = fmaf(wt, s_l[w][qi], L);
+      acc = fmaf(wt, s_o[w][qi][d], acc);
+    }
+    const int h = it.kvh * G + qi;
+    if (it.nsplit == 1) {
+      out[(int64_t(it.b) * g.Hq + h) * 128 + d] = f32_to_bf16(acc / L);
+    } else {
+      float* pp = partial_ptr(g, p, it.b, h, it.split);
+      store_coherent(pp + 2 + d, acc);
+      if (d == 0) {
+        store_coherent(pp, M);
+        store_coherent(pp + 1, L);
+      }
+    }
+  }
+  if (it.nsplit > 1 && last_arrival(p.counters + it.b * g.Hkv + it.kvh, it.nsplit))
+    merge_splits_wide(g, p, it.b, it.kvh, it.nsplit, &s_o[0][0][0], out);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePlan& p, const void* q, void* out,
+                              hipStream_t st) {
+  const int items = g.B * (lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s);
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+                     static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace duo

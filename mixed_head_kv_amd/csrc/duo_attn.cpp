@@ -205,28 +205,28 @@ int check_ptr(const void* p, const char* name) {
   return DUO_OK;
 }
 
-duo::DecodePlan make_plan(const duo_handle* h, int64_t t) {
+duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   duo::DecodePlan p;
   p.t = t;
   p.partials = h->partials;
   p.counters = h->counters;
+  p.k_new = nullptr;
+  p.v_new = nullptr;
+  p.new_slot = duo::stream_slot(t, h->cfg.sink, h->cfg.recent);
   const int64_t nkeys = t + 1;
-  const int B = h->cfg.batch;
-  const LayerView& lv = h->views[0];
-  (void)lv;
-  // Retrieval: enough splits for ~4 workgroups per CU over all retrieval heads, at
-  // least 256 keys per split, a multiple of 64, and never above kMaxSplits.
-  int64_t heads = 0;
-  for (const LayerLayout& y : h->layout.layers) heads = y.n_ret > heads ? y.n_ret : heads;
-  heads *= B;
-  int64_t chunk = 256;
+  const int64_t heads = int64_t(h->cfg.batch) * h->views[layer].n_ret;
+  // Retrieval heads: about one workgroup per CU over all of them, at least 512 keys
+  // per split (a multiple of 64), within the partial buffer and the merge's LDS.
+  int64_t chunk = 512;
   if (heads > 0) {
-    const int64_t target_wg = int64_t(h->num_cu) * 4;
-    const int64_t per_head = (target_wg + heads - 1) / heads;
+    const int64_t per_head = (h->num_cu + heads - 1) / heads;
     const int64_t want = (nkeys + per_head - 1) / per_head;
     if (want > chunk) chunk = want;
   }
-  const int64_t min_chunk = (nkeys + duo::kMaxSplits - 1) / duo::kMaxSplits;
+  int64_t max_splits = duo::kMaxSplits;
+  const int64_t merge_cap = duo::kMergeScratchFloats / (2 * h->geom.G);
+  if (h->use_mfma && merge_cap < max_splits) max_splits = merge_cap;
+  const int64_t min_chunk = (nkeys + max_splits - 1) / max_splits;
   if (chunk < min_chunk) chunk = min_chunk;
   if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
   chunk = int64_t(align_up(uint64_t(chunk), 64));
@@ -319,8 +319,16 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) h->num_cu = n;
   }
   if (const char* e = std::getenv("DUO_DECODE_CHUNK")) h->chunk_override = std::atoi(e);
-  h->use_mfma = false;
-  hipError_t e = duo::launch_zero_i32(h->counters, int64_t(cfg->batch) * cfg->n_kv_heads, as_stream(hip_stream));
+  // bf16 with head_dim 128 runs on the MFMA kernels; DUO_FORCE_VALU=1 keeps the
+  // vector-ALU kernels (used to compare the two paths).
+  const char* force_valu = std::getenv("DUO_FORCE_VALU");
+  h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 &&
+                cfg->kv_format == DUO_KV_SAME_AS_IO && !(force_valu && force_valu[0] == '1');
+  // Clear every cache and the counters.  The MFMA kernels read whole 32/64-row tiles
+  // and weight rows past the valid length by exactly zero, which needs those rows
+  // finite; cleared memory guarantees it.
+  hipError_t e = duo::launch_zero_bytes(h->ws, L.partials, as_stream(hip_stream));
+  if (e == hipSuccess) e = duo::launch_zero_i32(h->counters, int64_t(cfg->batch) * cfg->n_kv_heads, as_stream(hip_stream));
   if (e != hipSuccess) {
     delete h;
     return hip_fail(e, "clearing counters");
@@ -358,16 +366,42 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
   const int64_t t0 = h->len[layer];
   hipStream_t st = as_stream(hip_stream);
   hipError_t e;
-  {
-    KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
-    e = duo::launch_prefill_valu(h->geom, lv, q, k, v, out, n_tokens, t0, st);
+  if (h->use_mfma) {
+    // retrieval caches take the chunk first (the retrieval kernel reads keys from the
+    // cache); the streaming kernel reads the streaming caches as they stood before the
+    // chunk, which are updated last.
+    {
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 1, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append (retrieval)");
+    {
+      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+      e = duo::launch_prefill_mfma(h->geom, lv, q, out, n_tokens, t0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention (retrieval)");
+    {
+      KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
+      e = duo::launch_prefill_stream_mfma(h->geom, lv, q, k, v, out, n_tokens, t0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
+    {
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 2, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append (streaming)");
+  } else {
+    {
+      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+      e = duo::launch_prefill_valu(h->geom, lv, q, k, v, out, n_tokens, t0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention");
+    {
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 3, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append");
   }
-  if (e != hipSuccess) return hip_fail(e, "prefill attention");
-  {
-    KernelMark m(h, DUO_KERNEL_APPEND, st);
-    e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 3, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "prefill append");
   h->len[layer] = t0 + n_tokens;
   return ok();
 }
@@ -403,15 +437,20 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   hipStream_t st = as_stream(hip_stream);
   const int64_t t = append ? len : len - 1;
   hipError_t e;
-  if (append) {
+  duo::DecodePlan p = make_plan(h, layer, t);
+  if (append && h->use_mfma) {
+    // the MFMA decode appends the token itself (the workgroup covering its row)
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
+  } else if (append) {
     KernelMark m(h, DUO_KERNEL_APPEND, st);
     e = duo::launch_append(h->geom, lv, k_new, v_new, 1, t, 3, st);
     if (e != hipSuccess) return hip_fail(e, "decode append");
   }
-  const duo::DecodePlan p = make_plan(h, t);
   {
     KernelMark m(h, DUO_KERNEL_DECODE, st);
-    e = duo::launch_decode_valu(h->geom, lv, p, q, out, st);
+    e = h->use_mfma ? duo::launch_decode_mfma(h->geom, lv, p, q, out, st)
+                    : duo::launch_decode_valu(h->geom, lv, p, q, out, st);
   }
   if (e != hipSuccess) return hip_fail(e, "decode attention");
   if (append) h->len[layer] = len + 1;

@@ -25,6 +25,7 @@
 namespace duo {
 
 constexpr int kMaxSplits = 1024;    // split-K partials per query head (decode)
+constexpr int kMergeScratchFloats = 4 * 16 * 129;  // LDS the MFMA decode merge may use
 constexpr int kRowAlign = 64;       // cache rows are allocated in multiples of this
 constexpr int kKindRetrieval = 1;
 constexpr int kKindStreaming = 0;

@@ -35,6 +35,12 @@ struct DecodePlan {
   int nsplit_s;
   float* partials;    // [B * Hq * kMaxSplits * (D + 2)]
   int* counters;      // [B * Hkv] arrival counters, zero between calls
+  // Fused append (MFMA decode): K/V of the token at position t ([B, Hkv, D]), or null
+  // when the token is already in the caches.  It lands in retrieval row t and in
+  // streaming slot `new_slot`.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_slot;
 };
 
 // Split-K decode attention (all heads of the layer, one launch, merge by the last
@@ -53,6 +59,8 @@ hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool 
 hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,
                             int n, int which, uint8_t* codes, uint16_t* meta, hipStream_t st);
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st);
+// Clears n_bytes (a multiple of 16, 16-byte aligned) with a fill kernel.
+hipError_t launch_zero_bytes(void* p, uint64_t n_bytes, hipStream_t st);
 hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, uint64_t c0, uint64_t n,
                         hipStream_t st);
 

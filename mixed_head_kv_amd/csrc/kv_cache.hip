@@ -217,6 +217,11 @@ __global__ void k_zero_i32(int* p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
+__global__ void k_zero_16b(uint4* p, uint64_t n) {
+  for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
 // SplitMix64 finaliser (Steele, Lea and Flood, OOPSLA 2014).
 __device__ inline uint64_t mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -298,6 +303,15 @@ hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, 
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_zero_i32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void* p, uint64_t n_bytes, hipStream_t st) {
+  const uint64_t n = n_bytes / 16;
+  if (n == 0) return hipSuccess;
+  uint64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_zero_16b, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n);
   return hipGetLastError();
 }
 

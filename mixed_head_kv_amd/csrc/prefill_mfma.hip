@@ -1,0 +1,397 @@
+// Flash-style pre-filling on bf16 MFMA for gfx950 (head_dim 128), one kernel with two
+// key sources:
+//   retrieval heads: causal attention of the chunk's queries over every key [0, i],
+//     read from the retrieval cache (the chunk is appended to it first);
+//   streaming heads: the Lambda-shaped mask of sinks [0, S) plus the recent window
+//     (i - R, i], visiting only the key tiles that hold sinks or window keys; keys
+//     before the chunk come from the constant-length cache as it stood before the
+//     chunk, keys of the chunk from its K/V inputs.
+// Source: hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with
+// Retrieval and Streaming Heads", abstract (full attention for retrieval heads, recent
+// tokens and sinks for streaming heads, lower pre-filling latency) and its technical-
+// approach section; cn.bg3.co article, 研究背景 section (pre-filling cost of full
+// attention grows quadratically with the context).
+//
+// Workgroup: 4 wavefronts x 32 queries of one query head.  Keys move through LDS in
+// 64-key tiles, double-buffered (K rows with their 16-byte chunks XOR-swizzled by the
+// row index so the permuted row reads hit distinct banks; V in d-major 8-key blocks).  Per
+// 32-key half tile each wavefront runs, with v_mfma_f32_32x32x16_bf16,
+//   S^T[32 keys x 32 queries] = K * Q^T    (8 k-steps over head_dim)
+//   O^T[32 d x 32 queries]   += V^T * P^T  (4 d-blocks x 2 k-steps)
+// Rows of the K operand are read in the permuted key order that leaves each lane
+// holding, per k-step of P*V, the probabilities of 8 consecutive keys: exactly the
+// B operand, so P stays in registers.  Every lane owns one query, so the online
+// softmax rescale is lane-uniform; the row max needs one cross-half exchange.
+#include "decode_common.h"
+
+namespace duo {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileKeys = 64;
+constexpr int kKBytes = kTileKeys * 256;           // K rows, 16-byte chunks XOR-swizzled by row
+constexpr int kVBytes = kTileKeys * 128 * 2;       // 16384
+constexpr int kQRows = 128;                        // queries per workgroup
+
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+struct PrefillArgs {
+  Geom g;
+  LayerView lv;
+  const uint16_t* q;    // [B, T, Hq, 128]
+  const uint16_t* k;    // chunk inputs [B, T, Hkv, 128] (streaming heads)
+  const uint16_t* v;
+  uint16_t* out;        // [B, T, Hq, 128]
+  int T;
+  int64_t t0;
+  int streaming;        // 0: retrieval heads, 1: streaming heads
+  int n_heads;          // query heads of this kind per sequence
+  int n_qblocks;
+};
+
+// Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
+// this kind, in KV-head-major order.
+__device__ inline int kind_head(const PrefillArgs& a, int idx, int* kvh) {
+  const int G = a.g.G;
+  const int kv = a.streaming ? a.lv.str_kv[idx / G] : a.lv.ret_kv[idx / G];
+  *kvh = kv;
+  return kv * G + idx % G;
+}
+
+// One 64-key tile moves HBM -> registers -> LDS in two phases so the next tile's loads
+// are in flight while the current tile is computed.  Each thread carries four 16-byte
+// K chunks and four 16-byte V units.  Modes (uniform per tile):
+//   kCopy   : 64 contiguous cache rows (retrieval rows, or streaming sink slots that
+//             equal their positions): K rows and d-major V blocks copied as they are;
+//   kInput  : 64 positions inside the chunk: K rows from the input; V rows of key pairs
+//             (2k, 2k+1) x 8 dims, transposed into the d-major blocks on the LDS store;
+//   kGather : anything else (window keys that straddle the chunk start, or sinks mixed
+//             with ring slots): every key looked up in the chunk or its cache slot.
+enum { kCopy = 0, kInput = 1, kGather = 2 };
+
+struct Stage {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+__device__ inline int64_t slot_of(int64_t pos, int S, int R) {
+  return pos < S ? pos : S + static_cast<int>(pos - S) % R;
+}
+
+template <bool STREAMING>
+__device__ inline void stage_load(const PrefillArgs& a, int b, int kvh, int64_t cache, int64_t kb, int mode,
+                                  Stage& st) {
+  const int tid = threadIdx.x;
+  const Geom& g = a.g;
+  const CacheRegion& c = STREAMING ? a.lv.str : a.lv.ret;
+  if (mode == kCopy) {
+    const char* K = c.k + ((cache * c.rows + kb) * 128) * 2;
+    const char* V = c.v + ((cache * c.rows + kb) * 128) * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ch = tid + 256 * u;  // 16-byte chunk of the 16 KB tile
+      st.k[u] = *reinterpret_cast<const u32x4*>(K + ch * 16);
+      st.v[u] = *reinterpret_cast<const u32x4*>(V + ch * 16);
+    }
+    return;
+  }
+  if constexpr (STREAMING) {
+    const int64_t in_row = (int64_t(b) * a.T) * g.Hkv + kvh;  // + t * Hkv gives the input row of chunk token t
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ch = tid + 256 * u;
+      const int row = ch >> 4, col = ch & 15;
+      const int64_t pos = kb + row;
+      const uint16_t* src = nullptr;
+      if (pos >= a.t0) {
+        const int64_t t = pos - a.t0;
+        if (t < a.T) src = a.k + (in_row + t * g.Hkv) * 128;
+      } else {
+        src = reinterpret_cast<const uint16_t*>(c.k) + (cache * c.rows + slot_of(pos, g.S, g.R)) * 128;
+      }
+      st.k[u] = src ? *reinterpret_cast<const u32x4*>(src + col * 8) : u32x4{0, 0, 0, 0};
+    }
+    // V: task = (key pair kp in 0..31, 8-dim chunk dc in 0..15); two tasks per thread,
+    // each two 16-byte rows (keys 2kp and 2kp + 1, dims 8dc .. 8dc+7).
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int task = tid + 256 * u;
+      const int kp = task >> 4, dc = task & 15;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t pos = kb + 2 * kp + e;
+        u32x4 val = {0, 0, 0, 0};
+        if (pos >= a.t0) {
+          const int64_t t = pos - a.t0;
+          if (t < a.T) val = *reinterpret_cast<const u32x4*>(a.v + (in_row + t * g.Hkv) * 128 + 8 * dc);
+        } else if (mode == kGather) {
+          const uint16_t* V = reinterpret_cast<const uint16_t*>(c.v);
+          const int64_t slot = slot_of(pos, g.S, g.R);
+          uint16_t x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = V[v_index(cache, c.rows, slot, 128, 8 * dc + i)];
+          val = u32x4{uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16),
+                      uint32_t(x[4]) | (uint32_t(x[5]) << 16), uint32_t(x[6]) | (uint32_t(x[7]) << 16)};
+        }
+        st.v[2 * u + e] = val;
+      }
+    }
+  }
+}
+
+template <bool STREAMING>
+__device__ inline void stage_store(int mode, const Stage& st, char* ldsK, char* ldsV) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ch = tid + 256 * u;
+    const int row = ch >> 4;
+    *reinterpret_cast<u32x4*>(ldsK + row * 256 + (((ch & 15) ^ (row & 15)) * 16)) = st.k[u];
+  }
+  if (!STREAMING || mode == kCopy) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(ldsV + (tid + 256 * u) * 16) = st.v[u];
+    return;
+  }
+  // transpose key pairs into d-major 8-key blocks: dword (d, keys 2kp, 2kp+1)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int task = tid + 256 * u;
+    const int kp = task >> 4, dc = task & 15;
+    const u32x4 lo = st.v[2 * u], hi = st.v[2 * u + 1];
+    char* dst = ldsV + ((2 * kp) >> 3) * 2048 + (8 * dc) * 16 + ((2 * kp) & 7) * 2;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // dims 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
+      const uint32_t even = __builtin_amdgcn_perm(hi[w], lo[w], 0x05040100u);
+      const uint32_t odd = __builtin_amdgcn_perm(hi[w], lo[w], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(dst + (2 * w) * 16) = even;
+      *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * 16) = odd;
+    }
+  }
+}
+
+template <bool STREAMING>
+__global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // two tile buffers
+
+  const Geom& g = a.g;
+  // Longest query blocks first; heads of one block adjacent.
+  const int per_b = a.n_heads * a.n_qblocks;
+  const int b = blockIdx.x / per_b;
+  const int rem = blockIdx.x % per_b;
+  const int qb = a.n_qblocks - 1 - rem / a.n_heads;
+  int kvh;
+  const int h = kind_head(a, rem % a.n_heads, &kvh);
+  const int64_t cache = int64_t(b) * (STREAMING ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int q_first = qb * kQRows;                        // chunk-relative
+  const int q_last = min(q_first + kQRows, a.T) - 1;
+  const int my_q = q_first + 32 * wave + col;             // this lane's query
+  const bool q_valid = my_q < a.T;
+  const int64_t i_pos = a.t0 + (q_valid ? my_q : q_last); // absolute position
+  const int64_t wave_q_hi = a.t0 + min(q_first + 32 * wave + 31, q_last);
+  const int64_t wave_q_lo = a.t0 + q_first + 32 * wave;
+
+  // Q^T operand: lane (col, half) holds dims 64*half + 8s .. +7 of its query, s = 0..7.
+  u32x4 qop[8];
+  {
+    const int qrow = q_valid ? my_q : q_last;
+    const u32x4* qp =
+        reinterpret_cast<const u32x4*>(a.q + ((int64_t(b) * a.T + qrow) * g.Hq + h) * 128 + 64 * half);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qop[s] = qp[s];
+  }
+
+  float m = kNegInf, l = 0.0f;
+  f32x16 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
+
+  // Key tiles to visit.  Retrieval: [0, t0 + q_last].  Streaming: the sink tiles
+  // covering [0, S) and the window tiles covering [max(S, lo - R + 1), hi].
+  const int64_t hi = a.t0 + q_last;
+  int64_t n0, n1 = 0, s1_start = 0;
+  if (!STREAMING) {
+    n0 = (hi + 1 + kTileKeys - 1) / kTileKeys;
+  } else {
+    const int64_t seg0_end = g.S < hi + 1 ? g.S : hi + 1;
+    n0 = (seg0_end + kTileKeys - 1) / kTileKeys;
+    int64_t wlo = a.t0 + q_first - g.R + 1;
+    if (wlo < g.S) wlo = g.S;
+    if (wlo <= hi) {
+      s1_start = wlo / kTileKeys;
+      n1 = hi / kTileKeys - s1_start + 1;
+      if (s1_start < n0) {
+        n1 -= n0 - s1_start;
+        s1_start = n0;
+      }
+      if (n1 < 0) n1 = 0;
+    }
+  }
+  const int64_t ntiles = n0 + n1;
+  auto tile_start = [&](int64_t ti) -> int64_t { return (ti < n0 ? ti : s1_start + (ti - n0)) * kTileKeys; };
+  auto tile_mode = [&](int64_t kb) -> int {
+    if (!STREAMING) return kCopy;
+    const int64_t lim = g.S < a.t0 ? g.S : a.t0;  // positions below this sit in their own sink slot
+    if (kb + kTileKeys <= lim) return kCopy;
+    if (kb >= a.t0 && kb + kTileKeys <= a.t0 + a.T) return kInput;
+    return kGather;
+  };
+  const float sl2 = g.scale_log2;
+
+  Stage stage;
+  if (ntiles > 0) {
+    const int64_t kb = tile_start(0);
+    const int mode = tile_mode(kb);
+    stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
+    stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
+  }
+  __syncthreads();
+
+  for (int64_t ti = 0; ti < ntiles; ++ti) {
+    char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
+    char* ldsV = ldsK + kKBytes;
+    const int64_t kb = tile_start(ti);
+    const bool more = ti + 1 < ntiles;
+    int next_mode = kCopy;
+    if (more) {
+      const int64_t nkb = tile_start(ti + 1);
+      next_mode = tile_mode(nkb);
+      stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);  // in flight during the compute
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int64_t base = kb + 32 * sub;
+      if (base > wave_q_hi) continue;  // every key of this half tile is after the wave's queries
+      // S^T: row rho of the K operand is key base + pi(rho), pi(8j + 4h + i) = 16(j>>1) + 8h + 4(j&1) + i
+      const int rho = col;
+      const int pk = 16 * (rho >> 4) + 8 * ((rho >> 2) & 1) + 4 * ((rho >> 3) & 1) + (rho & 3);
+      const int krow_i = 32 * sub + pk;
+      const char* krow = ldsK + krow_i * 256;
+      f32x16 s = {};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
+        s = mfma32(kop, qop[st], s);
+      }
+      // lane's 16 scores: register 4j + i is key base + 16(j>>1) + 8*half + 4(j&1) + i
+      const bool need_mask = STREAMING || base + 31 > wave_q_lo;
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = base + 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
+          float v = s[4 * j + i] * sl2;
+          if (need_mask) {
+            bool vis = key <= i_pos;
+            if (STREAMING) vis = vis && (key < g.S || i_pos - key < g.R);
+            v = vis ? v : kNegInf;
+          }
+          s[4 * j + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float mref = mn == kNegInf ? 0.0f : mn;
+      const float alpha = exp2f(m - mref);
+      m = mn;
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = exp2f(s[e] - mref);
+        ps += s[e];
+      }
+      l = l * alpha + ps;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] *= alpha;
+      // P^T operand for k-step u: keys base + 16u + 8*half + 0..7 = registers 8u .. 8u+7
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb = {pack_bf16(s[8 * u + 0], s[8 * u + 1]), pack_bf16(s[8 * u + 2], s[8 * u + 3]),
+                          pack_bf16(s[8 * u + 4], s[8 * u + 5]), pack_bf16(s[8 * u + 6], s[8 * u + 7])};
+        // V^T rows d = 32 jd + col, keys 32 sub + 16u + 8 half .. +7: one 16-byte block row
+        const char* vblk = ldsV + ((32 * sub + 16 * u + 8 * half) >> 3) * 2048 + col * 16;
+#pragma unroll
+        for (int jd = 0; jd < 4; ++jd) {
+          const u32x4 vop = *reinterpret_cast<const u32x4*>(vblk + jd * 32 * 16);
+          o[jd] = mfma32(vop, pb, o[jd]);
+        }
+      }
+    }
+    if (more) {
+      char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
+      stage_store<STREAMING>(next_mode, stage, nK, nK + kKBytes);
+    }
+    __syncthreads();
+  }
+
+  // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
+  l += __shfl_xor(l, 32);
+  if (q_valid) {
+    const float inv = 1.0f / l;
+    uint16_t* orow = a.out + ((int64_t(b) * a.T + my_q) * g.Hq + h) * 128;
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * jd + 8 * j + 4 * half;
+        const uint32_t w0 = pack_bf16(o[jd][4 * j + 0] * inv, o[jd][4 * j + 1] * inv);
+        const uint32_t w1 = pack_bf16(o[jd][4 * j + 2] * inv, o[jd][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
+      }
+  }
+}
+
+}  // namespace
+
+static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
+                                      void* out, int T, int64_t t0, int streaming, hipStream_t st) {
+  PrefillArgs a;
+  a.g = g;
+  a.lv = lv;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.T = T;
+  a.t0 = t0;
+  a.streaming = streaming;
+  a.n_heads = (streaming ? lv.n_str : lv.n_ret) * g.G;
+  a.n_qblocks = (T + kQRows - 1) / kQRows;
+  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks;
+  if (blocks == 0) return hipSuccess;
+  const unsigned lds = 2 * (kKBytes + kVBytes);
+  if (streaming)
+    hipLaunchKernelGGL(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T, int64_t t0,
+                               hipStream_t st) {
+  return launch_prefill_kind(g, lv, q, nullptr, nullptr, out, T, t0, 0, st);
+}
+
+hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
+                                      void* out, int T, int64_t t0, hipStream_t st) {
+  return launch_prefill_kind(g, lv, q, k, v, out, T, t0, 1, st);
+}
+
+}  // namespace duo

@@ -118,6 +118,25 @@ def test_prefill_and_decode_match_oracle(torch_cuda, name):
     assert kv.length(0) == total
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16"])
+def test_poisoned_workspace_is_cleared_by_init(torch_cuda, name):
+    """Whole tiles are read past the valid length and weighted by zero; init must clear
+    the workspace so stale NaN bit patterns can never reach the math."""
+    from mixed_head_kv_amd import binding as B
+    w = SMALL[name]
+    chunks = CHUNKS[name]
+    say(f"poisoned workspace {name}")
+    kv = B.DuoKV.for_workload(w)
+    B.duo_kv_free(kv.h)
+    kv.workspace.fill_(255)
+    kv.h = B.duo_kv_init(kv.cfg, kv.workspace)
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps, kv=kv)
+    L = sum(chunks)
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare(f"{name} prefill (poisoned)", to_f64(pre), ref[:L], TOL[w.io_dtype])
+    compare(f"{name} decode (poisoned)", to_f64(dec), ref[L:], TOL[w.io_dtype])
+
+
 def test_int4_decode_matches_oracle(torch_cuda):
     w = W("int4_gqa", 22, 8, 4, 128, "bf16", 4, 32, 700, 10, 2, fmt="int4")
     say("int4 decode")
