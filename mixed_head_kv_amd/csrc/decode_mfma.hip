@@ -31,8 +31,12 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 struct Tile {
@@ -185,31 +189,37 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, De
       s0 = mfma16(cur.k0[s], qop[s], s0);
       s1 = mfma16(cur.k1[s], qop[s], s1);
     }
-    // lane holds scores of keys base + 8*grp + 0..7 for query r
+    // lane holds scores of keys base + 8*grp + 0..7 for query r; keys past the range
+    // become -inf, the max is kept on raw scores and the scale folded into the FMA
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     const int64_t kfirst = base + 8 * grp;
-    float mx = kNegInf;
+    if (base + 32 > it.key1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sc[i] = kfirst + i < it.key1 ? sc[i] * sl2 : kNegInf;
-      mx = fmaxf(mx, sc[i]);
+      for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
     }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+    const float mref = mn == kNegInf ? 0.0f : mn;
+    if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] *= alpha;
+    }
     m = mn;
-    float ps = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sc[i] = exp2f(sc[i] - mn);
-      ps += sc[i];
+      sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
+      l += sc[i];
     }
-    l = l * alpha + ps;
     const u32x4 pb = {pack_bf16(sc[0], sc[1]), pack_bf16(sc[2], sc[3]), pack_bf16(sc[4], sc[5]),
                       pack_bf16(sc[6], sc[7])};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j] * alpha);
+    for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j]);
     cur = nxt;
   }
 
@@ -255,14 +265,220 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, De
     merge_splits_wide(g, p, it.b, it.kvh, it.nsplit, &s_o[0][0][0], out);
 }
 
+// ---- int4 caches ------------------------------------------------------------------
+//
+// Codes enter the bf16 MFMA as the exact values 128 + c (bf16 bits 0x4300 | c), built
+// with one byte permute per pair of codes, and the per-vector scale s and zero z are
+// applied algebraically (hotpaper.ai page, abstract and main results: the method runs
+// with a 4-bit KV cache; the format is one group per 128-value vector with fp16 s, z):
+//   score_j = s_j * (sum_d q_d (128 + c_jd) - 128 * sum_d q_d) + z_j * sum_d q_d
+//   o_d     = sum_j p'_j (128 + c_jd) - 128 * sum_j p'_j + sum_j p_j z_j,  p'_j = bf16(p_j s_j)
+// which equals attention over the dequantised values s*c + z up to rounding.
+
+// Eight 4-bit codes (byte b: codes 2b low, 2b+1 high) -> eight bf16 values 128 + c in
+// the element order (0, 2, 4, 6, 1, 3, 5, 7).
+__device__ inline u32x4 codes_to_bf16(uint32_t x) {
+  const uint32_t lo = x & 0x0F0F0F0Fu;
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+  const uint32_t k43 = 0x43434343u;
+  return u32x4{__builtin_amdgcn_perm(k43, lo, 0x04010400u), __builtin_amdgcn_perm(k43, lo, 0x04030402u),
+               __builtin_amdgcn_perm(k43, hi, 0x04010400u), __builtin_amdgcn_perm(k43, hi, 0x04030402u)};
+}
+
+// Reorder 8 bf16 (one u32x4, element order 0..7) to (0, 2, 4, 6, 1, 3, 5, 7).
+__device__ inline u32x4 even_odd_bf16(u32x4 v) {
+  return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+               __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+}
+
+__device__ inline float half_lo(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xffff))); }
+__device__ inline float half_hi(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16))); }
+
+struct Tile4 {
+  uint32_t k0[4], k1[4];  // 32 codes (16 bytes) of the two K rows, one word per k-step
+  uint32_t v[8];          // 8 codes (keys of the lane's block) for dims 16j + r
+  u32x4 km0, km1;         // K (scale, zero) of keys base + 8g + 0..7 (4 per u32x4)
+  u32x4 vm0, vm1;         // V (scale, zero) of the same keys
+};
+
+__device__ inline void load_tile4(Tile4& t, const CacheRegion& c, int64_t cache, int64_t base, int r, int grp) {
+  const int64_t row0 = cache * c.rows;
+  const int64_t key0 = base + 8 * (r >> 2) + (r & 3);
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(c.k);
+  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (row0 + key0) * 64 + 16 * grp));
+  const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (row0 + key0 + 4) * 64 + 16 * grp));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    t.k0[s] = a[s];
+    t.k1[s] = b[s];
+  }
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(c.v) + (row0 + base + 8 * grp) / 8 * 128 + r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t.v[j] = __builtin_nontemporal_load(vw + 16 * j);
+  const u32x4* km = reinterpret_cast<const u32x4*>(c.k_meta + (row0 + base + 8 * grp) * 2);
+  const u32x4* vm = reinterpret_cast<const u32x4*>(c.v_meta + (row0 + base + 8 * grp) * 2);
+  t.km0 = __builtin_nontemporal_load(km);
+  t.km1 = __builtin_nontemporal_load(km + 1);
+  t.vm0 = __builtin_nontemporal_load(vm);
+  t.vm1 = __builtin_nontemporal_load(vm + 1);
+}
+
+__global__ void __launch_bounds__(256, 2) k_decode_mfma_int4(Geom g, LayerView lv, DecodePlan p,
+                                                            const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_o[4][16][129];  // also the merge scratch (G * nsplit * 2 floats)
+
+  const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int G = g.G;
+  const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
+
+  // Q^T operand in the codes' element order; Qsum = sum of the query's 128 values.
+  u32x4 qop[4];
+  float qsum;
+  {
+    const bool real = r < G;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t(it.b) * g.Hq + it.kvh * G + (real ? r : 0)) * 128 +
+                                                     32 * grp);
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 v = real ? qp[s] : u32x4{0, 0, 0, 0};
+      qop[s] = even_odd_bf16(v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part += bf16_to_f32(v[e] & 0xffff) + bf16_to_f32(v[e] >> 16);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    qsum = part;
+  }
+  const float q128 = 128.0f * qsum;
+
+  float m = kNegInf, l = 0.0f, asum = 0.0f, zsum = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = g.scale_log2;
+  int64_t base = it.key0 + 32 * wave;
+  Tile4 cur, nxt;
+  if (base < it.key1) load_tile4(cur, c, it.cache, base, r, grp);
+  for (; base < it.key1; base += 128) {
+    const int64_t next = base + 128;
+    if (next < it.key1) load_tile4(nxt, c, it.cache, next, r, grp);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      s0 = mfma16(codes_to_bf16(cur.k0[s]), qop[s], s0);
+      s1 = mfma16(codes_to_bf16(cur.k1[s]), qop[s], s1);
+    }
+    // keys base + 8*grp + i: (scale, zero) pairs in km0 (i < 4) and km1 (i >= 4)
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t mk = i < 4 ? cur.km0[i] : cur.km1[i - 4];
+      sc[i] = fmaf(half_lo(mk), sc[i] - q128, half_hi(mk) * qsum);
+    }
+    const int64_t kfirst = base + 8 * grp;
+    if (base + 32 > it.key1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const float mn = fmaxf(m, mx);
+    const float mref = mn == kNegInf ? 0.0f : mn;
+    if (__ballot(mn > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      l *= alpha;
+      asum *= alpha;
+      zsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] *= alpha;
+    }
+    m = mn;
+    float pw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pi = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
+      const uint32_t mv = i < 4 ? cur.vm0[i] : cur.vm1[i - 4];
+      l += pi;
+      zsum = fmaf(pi, half_hi(mv), zsum);
+      pw[i] = pi * half_lo(mv);
+    }
+    // P'^T operand in the V codes' key order (0, 2, 4, 6, 1, 3, 5, 7); asum adds the
+    // bf16-rounded weights exactly as the MFMA sees them
+    const u32x4 pb = {pack_bf16(pw[0], pw[2]), pack_bf16(pw[4], pw[6]), pack_bf16(pw[1], pw[3]),
+                      pack_bf16(pw[5], pw[7])};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asum += bf16_to_f32(pb[e] & 0xffff) + bf16_to_f32(pb[e] >> 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = mfma16(codes_to_bf16(cur.v[j]), pb, o[j]);
+    cur = nxt;
+  }
+
+  // Per-query corrections are summed over the lane's group, then applied to its O.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  asum += __shfl_xor(asum, 16);
+  asum += __shfl_xor(asum, 32);
+  zsum += __shfl_xor(zsum, 16);
+  zsum += __shfl_xor(zsum, 32);
+  const float corr = zsum - 128.0f * asum;
+  if (grp == 0) {
+    s_m[wave][r] = m;
+    s_l[wave][r] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][r][16 * j + 4 * grp + i] = o[j][i] + corr;
+  __syncthreads();
+
+  const int pairs = G * 128;
+  for (int e = threadIdx.x; e < pairs; e += 256) {
+    const int qi = e >> 7, d = e & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][qi]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
+      L = fmaf(wt, s_l[w][qi], L);
+      acc = fmaf(wt, s_o[w][qi][d], acc);
+    }
+    const int h = it.kvh * G + qi;
+    if (it.nsplit == 1) {
+      out[(int64_t(it.b) * g.Hq + h) * 128 + d] = f32_to_bf16(acc / L);
+    } else {
+      float* pp = partial_ptr(g, p, it.b, h, it.split);
+      store_coherent(pp + 2 + d, acc);
+      if (d == 0) {
+        store_coherent(pp, M);
+        store_coherent(pp + 1, L);
+      }
+    }
+  }
+  if (it.nsplit > 1 && last_arrival(p.counters + it.b * g.Hkv + it.kvh, it.nsplit))
+    merge_splits_wide(g, p, it.b, it.kvh, it.nsplit, &s_o[0][0][0], out);
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePlan& p, const void* q, void* out,
                               hipStream_t st) {
   const int items = g.B * (lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s);
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
-                     static_cast<uint16_t*>(out));
+  if (g.kvfmt == DUO_KV_INT4_G128)
+    hipLaunchKernelGGL(k_decode_mfma_int4, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+                       static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+                       static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ struct Layout {
   int64_t cap = 0;   // retrieval rows per cache
   int64_t nslot = 0; // streaming slots per cache
   std::vector<LayerLayout> layers;
-  uint64_t partials = 0, counters = 0, total = 0;
+  uint64_t partials = 0, counters = 0, prefill_counters = 0, total = 0;
 };
 
 int validate_config(const duo_config* c) {
@@ -126,6 +126,8 @@ bool make_layout(const duo_config* c, Layout* L) {
   off = align_up(off + B * c->n_q_heads * uint64_t(duo::kMaxSplits) * (D + 2) * 4, kAlign);
   L->counters = off;
   off = align_up(off + B * c->n_kv_heads * 4, kAlign);
+  L->prefill_counters = off;
+  off = align_up(off + uint64_t(duo::kPrefillCounters) * 4, kAlign);
   L->total = off;
   return true;
 }
@@ -142,10 +144,13 @@ struct duo_handle {
   std::vector<LayerView> views;
   std::vector<int64_t> len;
   float* partials = nullptr;
+  int64_t partial_floats = 0;
   int* counters = nullptr;
+  int* prefill_counters = nullptr;
   int num_cu = 256;
   int chunk_override = 0;
-  bool use_mfma = false;
+  bool use_mfma = false;         // bf16 caches: MFMA prefill + decode (append fused into decode)
+  bool use_mfma_decode = false;  // MFMA decode (bf16 or int4 caches)
   // kernel timing (duo_profile.h)
   bool profiling = false;
   struct Mark { int cls; hipEvent_t start, stop; };
@@ -225,7 +230,7 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   }
   int64_t max_splits = duo::kMaxSplits;
   const int64_t merge_cap = duo::kMergeScratchFloats / (2 * h->geom.G);
-  if (h->use_mfma && merge_cap < max_splits) max_splits = merge_cap;
+  if (h->use_mfma_decode && merge_cap < max_splits) max_splits = merge_cap;
   const int64_t min_chunk = (nkeys + max_splits - 1) / max_splits;
   if (chunk < min_chunk) chunk = min_chunk;
   if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
@@ -313,6 +318,8 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   h->len.assign(cfg->n_layers, 0);
   h->partials = reinterpret_cast<float*>(h->ws + L.partials);
   h->counters = reinterpret_cast<int*>(h->ws + L.counters);
+  h->prefill_counters = reinterpret_cast<int*>(h->ws + L.prefill_counters);
+  h->partial_floats = int64_t(cfg->batch) * cfg->n_q_heads * duo::kMaxSplits * (cfg->head_dim + 2);
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int n = 0;
@@ -322,13 +329,15 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   // bf16 with head_dim 128 runs on the MFMA kernels; DUO_FORCE_VALU=1 keeps the
   // vector-ALU kernels (used to compare the two paths).
   const char* force_valu = std::getenv("DUO_FORCE_VALU");
-  h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 &&
-                cfg->kv_format == DUO_KV_SAME_AS_IO && !(force_valu && force_valu[0] == '1');
+  const bool valu = force_valu && force_valu[0] == '1';
+  h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && cfg->kv_format == DUO_KV_SAME_AS_IO && !valu;
+  h->use_mfma_decode = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && !valu;
   // Clear every cache and the counters.  The MFMA kernels read whole 32/64-row tiles
   // and weight rows past the valid length by exactly zero, which needs those rows
   // finite; cleared memory guarantees it.
   hipError_t e = duo::launch_zero_bytes(h->ws, L.partials, as_stream(hip_stream));
-  if (e == hipSuccess) e = duo::launch_zero_i32(h->counters, int64_t(cfg->batch) * cfg->n_kv_heads, as_stream(hip_stream));
+  if (e == hipSuccess)
+    e = duo::launch_zero_bytes(h->ws + L.counters, L.total - L.counters, as_stream(hip_stream));
   if (e != hipSuccess) {
     delete h;
     return hip_fail(e, "clearing counters");
@@ -377,7 +386,8 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
     if (e != hipSuccess) return hip_fail(e, "prefill append (retrieval)");
     {
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
-      e = duo::launch_prefill_mfma(h->geom, lv, q, out, n_tokens, t0, st);
+      e = duo::launch_prefill_mfma(h->geom, lv, q, out, n_tokens, t0, h->partials, h->partial_floats,
+                                   h->prefill_counters, h->num_cu, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill attention (retrieval)");
     {
@@ -449,8 +459,8 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   }
   {
     KernelMark m(h, DUO_KERNEL_DECODE, st);
-    e = h->use_mfma ? duo::launch_decode_mfma(h->geom, lv, p, q, out, st)
-                    : duo::launch_decode_valu(h->geom, lv, p, q, out, st);
+    e = h->use_mfma_decode ? duo::launch_decode_mfma(h->geom, lv, p, q, out, st)
+                           : duo::launch_decode_valu(h->geom, lv, p, q, out, st);
   }
   if (e != hipSuccess) return hip_fail(e, "decode attention");
   if (append) h->len[layer] = len + 1;

@@ -24,7 +24,8 @@
 
 namespace duo {
 
-constexpr int kMaxSplits = 1024;    // split-K partials per query head (decode)
+constexpr int kMaxSplits = 2048;    // split-K partial slots per query head (decode; prefill reuses the buffer)
+constexpr int kPrefillCounters = 1 << 16;  // arrival counters for split prefill query blocks
 constexpr int kMergeScratchFloats = 4 * 16 * 129;  // LDS the MFMA decode merge may use
 constexpr int kRowAlign = 64;       // cache rows are allocated in multiples of this
 constexpr int kKindRetrieval = 1;

@@ -19,8 +19,12 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
 
 // Retrieval-head prefill on bf16 MFMA (D = 128).  Reads keys [0, t0 + T) from the
 // retrieval cache, so the chunk must have been appended to the retrieval caches first.
+// When the grid is small (under two workgroups per CU) each query block's key range is
+// split over two workgroups that merge through `scratch` (fp32 partials, coherent)
+// and `counters` (kPrefillCounters ints, zero between calls).
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T,
-                               int64_t t0, hipStream_t st);
+                               int64_t t0, float* scratch, int64_t scratch_floats, int* counters, int num_cu,
+                               hipStream_t st);
 
 // Streaming-head (sink + window) prefill on bf16 MFMA (D = 128); reads the streaming
 // caches as they stood before the chunk plus the chunk inputs.

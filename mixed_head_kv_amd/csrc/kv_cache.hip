@@ -85,6 +85,95 @@ __global__ void __launch_bounds__(256) k_append(Geom g, LayerView lv, const T* _
   }
 }
 
+// Source token of destination row `row` for a bf16 append, with the ring position
+// precomputed on the host: ring_lo = max(t0, S, t0 + T - R) is the first chunk
+// position that survives in the ring, ring_have = (ring_lo - S) mod R its ring index.
+__device__ inline int source_token_fast(bool streaming, int64_t row, int64_t t0, int T, int S, int R,
+                                        int64_t ring_lo, int ring_have) {
+  if (!streaming || row < S) {
+    if (streaming && row >= S + R) return -1;
+    const int64_t t = row - t0;
+    return (t >= 0 && t < T) ? static_cast<int>(t) : -1;
+  }
+  if (row >= S + R || ring_lo >= t0 + T) return -1;
+  int d = static_cast<int>(row - S) - ring_have;
+  if (d < 0) d += R;
+  const int64_t p = ring_lo + d;
+  return p < t0 + T ? static_cast<int>(p - t0) : -1;
+}
+
+// bf16 append, one thread per (8-row tile, 8-dim chunk): eight 16-byte K row pieces are
+// copied as they are, and the 8x8 block of V is transposed in registers (byte
+// permutes) into eight 16-byte runs of the d-major tile layout.  Tiles with rows that
+// receive no token (range edges, evicted ring slots) write row by row.
+__global__ void __launch_bounds__(256) k_append_bf16(Geom g, LayerView lv, const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v, int T_, int64_t t0, int which,
+                                                     int64_t ret_tile0, int ret_tiles, int str_tiles,
+                                                     int64_t ring_lo, int ring_have) {
+  const int D = g.D;
+  const int nchunk = D / 8;
+  const int nret = g.B * lv.n_ret;
+  const int y = blockIdx.y;
+  const bool streaming = y >= nret;
+  if (streaming && !(which & 2)) return;
+  if (!streaming && !(which & 1)) return;
+  const int task = blockIdx.x * 256 + threadIdx.x;
+  const int tile = task / nchunk, ch = task % nchunk;
+  if (tile >= (streaming ? str_tiles : ret_tiles)) return;
+  const int cache = streaming ? y - nret : y;
+  const int b = streaming ? cache / lv.n_str : cache / lv.n_ret;
+  const int idx = streaming ? cache % lv.n_str : cache % lv.n_ret;
+  const int kvh = streaming ? lv.str_kv[idx] : lv.ret_kv[idx];
+  const CacheRegion& c = streaming ? lv.str : lv.ret;
+  const int64_t row0 = (streaming ? int64_t(tile) : ret_tile0 + tile) * 8;
+  uint16_t* K = reinterpret_cast<uint16_t*>(c.k);
+  uint16_t* V = reinterpret_cast<uint16_t*>(c.v);
+  int src[8];
+  int nvalid = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    src[r] = source_token_fast(streaming, row0 + r, t0, T_, g.S, g.R, ring_lo, ring_have);
+    nvalid += src[r] >= 0;
+  }
+  if (nvalid == 0) return;
+  const int64_t in0 = (int64_t(b) * T_) * g.Hkv + kvh;  // input row of token t: in0 + t * Hkv
+  uint4 vr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (src[r] < 0) {
+      vr[r] = make_uint4(0, 0, 0, 0);
+      continue;
+    }
+    const int64_t off = (in0 + int64_t(src[r]) * g.Hkv) * D + 8 * ch;
+    *reinterpret_cast<uint4*>(K + (int64_t(cache) * c.rows + row0 + r) * D + 8 * ch) =
+        *reinterpret_cast<const uint4*>(k + off);
+    vr[r] = *reinterpret_cast<const uint4*>(v + off);
+  }
+  // V tile: element (row r, dim 8ch + e) goes to tile[8ch + e][r]
+  uint16_t* vt = V + (int64_t(cache) * c.rows + row0) * D + 8 * ch * 8;
+  if (nvalid == 8) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(vr);  // w[4r + e/2] holds dims e, e+1 of row r
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      uint4 out;
+      out.x = __builtin_amdgcn_perm(w[4 * 1 + e / 2], w[4 * 0 + e / 2], sel);
+      out.y = __builtin_amdgcn_perm(w[4 * 3 + e / 2], w[4 * 2 + e / 2], sel);
+      out.z = __builtin_amdgcn_perm(w[4 * 5 + e / 2], w[4 * 4 + e / 2], sel);
+      out.w = __builtin_amdgcn_perm(w[4 * 7 + e / 2], w[4 * 6 + e / 2], sel);
+      *reinterpret_cast<uint4*>(vt + e * 8) = out;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (src[r] < 0) continue;
+      const uint16_t* x = reinterpret_cast<const uint16_t*>(&vr[r]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[e * 8 + r] = x[e];
+    }
+  }
+}
+
 __device__ inline float wave_min(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
@@ -262,8 +351,18 @@ hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, cons
     hipLaunchKernelGGL(k_append_int4, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), T, t0, which, first, ret_tiles, str_tiles);
   } else {
-    const int per_block = 256 / g.D;
     const int tiles = ret_tiles > str_tiles ? ret_tiles : str_tiles;
+    if (g.io == DUO_DTYPE_BF16) {
+      int64_t ring_lo = t0 > g.S ? t0 : g.S;
+      if (ring_lo < t0 + T - g.R) ring_lo = t0 + T - g.R;
+      const int ring_have = ring_lo >= g.S ? static_cast<int>((ring_lo - g.S) % g.R) : 0;
+      const int64_t tasks = int64_t(tiles) * (g.D / 8);
+      dim3 grid(static_cast<unsigned>((tasks + 255) / 256), ny);
+      hipLaunchKernelGGL(k_append_bf16, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), T, t0, which, first, ret_tiles, str_tiles, ring_lo, ring_have);
+      return hipGetLastError();
+    }
+    const int per_block = 256 / g.D;
     dim3 grid((tiles + per_block - 1) / per_block, ny);
     if (g.io == DUO_DTYPE_F32)
       hipLaunchKernelGGL(k_append<float>, grid, dim3(per_block * g.D), 0, st, g, lv, static_cast<const float*>(k),

@@ -22,6 +22,8 @@
 // holding, per k-step of P*V, the probabilities of 8 consecutive keys: exactly the
 // B operand, so P stays in registers.  Every lane owns one query, so the online
 // softmax rescale is lane-uniform; the row max needs one cross-half exchange.
+#include <cstdlib>
+
 #include "decode_common.h"
 
 namespace duo {
@@ -41,8 +43,12 @@ __device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 struct PrefillArgs {
@@ -57,7 +63,13 @@ struct PrefillArgs {
   int streaming;        // 0: retrieval heads, 1: streaming heads
   int n_heads;          // query heads of this kind per sequence
   int n_qblocks;
+  int nsplit;           // workgroups sharing one query block's key range (1 or 2)
+  float* scratch;       // nsplit > 1: per (block, split) fp32 partial, kSlotFloats each
+  int* counters;        // nsplit > 1: arrival counter per query block
 };
+
+// Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
+constexpr int kSlotFloats = kQRows * 128 + 2 * kQRows;
 
 // Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
 // this kind, in KV-head-major order.
@@ -187,12 +199,15 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 
   const Geom& g = a.g;
   // Longest query blocks first; heads of one block adjacent.
-  const int per_b = a.n_heads * a.n_qblocks;
+  const int per_b = a.n_heads * a.n_qblocks * a.nsplit;
   const int b = blockIdx.x / per_b;
   const int rem = blockIdx.x % per_b;
-  const int qb = a.n_qblocks - 1 - rem / a.n_heads;
+  const int split = rem % a.nsplit;
+  const int hq = rem / a.nsplit;
+  const int qb = a.n_qblocks - 1 - hq / a.n_heads;
+  const int head_idx = hq % a.n_heads;
   int kvh;
-  const int h = kind_head(a, rem % a.n_heads, &kvh);
+  const int h = kind_head(a, head_idx, &kvh);
   const int64_t cache = int64_t(b) * (STREAMING ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -243,8 +258,14 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       if (n1 < 0) n1 = 0;
     }
   }
-  const int64_t ntiles = n0 + n1;
-  auto tile_start = [&](int64_t ti) -> int64_t { return (ti < n0 ? ti : s1_start + (ti - n0)) * kTileKeys; };
+  // a split takes a contiguous share of the tiles (the diagonal ones go to the last split)
+  const int64_t all_tiles = n0 + n1;
+  const int64_t t_begin = all_tiles * split / a.nsplit;
+  const int64_t ntiles = all_tiles * (split + 1) / a.nsplit - t_begin;
+  auto tile_start = [&](int64_t tj) -> int64_t {
+    const int64_t ti = t_begin + tj;
+    return (ti < n0 ? ti : s1_start + (ti - n0)) * kTileKeys;
+  };
   auto tile_mode = [&](int64_t kb) -> int {
     if (!STREAMING) return kCopy;
     const int64_t lim = g.S < a.t0 ? g.S : a.t0;  // positions below this sit in their own sink slot
@@ -289,37 +310,39 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
         const u32x4 kop = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
         s = mfma32(kop, qop[st], s);
       }
-      // lane's 16 scores: register 4j + i is key base + 16(j>>1) + 8*half + 4(j&1) + i
-      const bool need_mask = STREAMING || base + 31 > wave_q_lo;
-      float mx = kNegInf;
+      // lane's 16 scores: register 4j + i is key base + 16(j>>1) + 8*half + 4(j&1) + i.
+      // Masked keys become -inf; the running max is kept on raw scores (the scale is
+      // positive) and the scale is folded into the exponent's FMA.
+      if (STREAMING || base + 31 > wave_q_lo) {
+        const int rel0 = static_cast<int>(base - i_pos);  // key - query position for register 0
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t key = base + 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
-          float v = s[4 * j + i] * sl2;
-          if (need_mask) {
-            bool vis = key <= i_pos;
-            if (STREAMING) vis = vis && (key < g.S || i_pos - key < g.R);
-            v = vis ? v : kNegInf;
+          for (int i = 0; i < 4; ++i) {
+            const int rel = rel0 + 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
+            bool vis = rel <= 0;
+            if (STREAMING) vis = vis && (-rel < g.R || static_cast<int>(base - g.S) + (rel - rel0) < 0);
+            s[4 * j + i] = vis ? s[4 * j + i] : kNegInf;
           }
-          s[4 * j + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
       const float mn = fmaxf(m, mx);
       const float mref = mn == kNegInf ? 0.0f : mn;
-      const float alpha = exp2f(m - mref);
+      if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] *= alpha;
+      }
       m = mn;
-      float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s[e] = exp2f(s[e] - mref);
-        ps += s[e];
+        s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
+        l += s[e];
       }
-      l = l * alpha + ps;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] *= alpha;
       // P^T operand for k-step u: keys base + 16u + 8*half + 0..7 = registers 8u .. 8u+7
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -343,6 +366,45 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
   l += __shfl_xor(l, 32);
+  if (a.nsplit > 1) {
+    // Every split publishes its partial; the last one to arrive merges them all.
+    const int pair = (b * a.n_heads + head_idx) * a.n_qblocks + qb;
+    const int ql = 32 * wave + col;
+    float* mine = a.scratch + (int64_t(pair) * a.nsplit + split) * kSlotFloats;
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_coherent(mine + ql * 128 + 32 * jd + 8 * j + 4 * half + i, o[jd][4 * j + i]);
+    if (half == 0) {
+      store_coherent(mine + kQRows * 128 + ql, m);
+      store_coherent(mine + kQRows * 128 + kQRows + ql, l);
+    }
+    if (!last_arrival(a.counters + pair, a.nsplit)) return;
+    float M = m;
+    for (int s2 = 0; s2 < a.nsplit; ++s2) {
+      if (s2 == split) continue;
+      M = fmaxf(M, load_coherent(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats + kQRows * 128 + ql));
+    }
+    const float w0 = __builtin_amdgcn_exp2f(m - M);  // an empty split has m = -inf: weight 0
+    l *= w0;
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) o[jd] *= w0;
+    for (int s2 = 0; s2 < a.nsplit; ++s2) {
+      if (s2 == split) continue;
+      const float* other = a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats;
+      const float w = __builtin_amdgcn_exp2f(load_coherent(other + kQRows * 128 + ql) - M);
+      l = fmaf(w, load_coherent(other + kQRows * 128 + kQRows + ql), l);
+#pragma unroll
+      for (int jd = 0; jd < 4; ++jd)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[jd][4 * j + i] = fmaf(w, load_coherent(other + ql * 128 + 32 * jd + 8 * j + 4 * half + i), o[jd][4 * j + i]);
+    }
+  }
   if (q_valid) {
     const float inv = 1.0f / l;
     uint16_t* orow = a.out + ((int64_t(b) * a.T + my_q) * g.Hq + h) * 128;
@@ -361,7 +423,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 }  // namespace
 
 static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
-                                      void* out, int T, int64_t t0, int streaming, hipStream_t st) {
+                                      void* out, int T, int64_t t0, int streaming, int nsplit, float* scratch,
+                                      int* counters, hipStream_t st) {
   PrefillArgs a;
   a.g = g;
   a.lv = lv;
@@ -374,7 +437,10 @@ static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const 
   a.streaming = streaming;
   a.n_heads = (streaming ? lv.n_str : lv.n_ret) * g.G;
   a.n_qblocks = (T + kQRows - 1) / kQRows;
-  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks;
+  a.nsplit = nsplit;
+  a.scratch = scratch;
+  a.counters = counters;
+  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks * nsplit;
   if (blocks == 0) return hipSuccess;
   const unsigned lds = 2 * (kKBytes + kVBytes);
   if (streaming)
@@ -385,13 +451,25 @@ static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const 
 }
 
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T, int64_t t0,
-                               hipStream_t st) {
-  return launch_prefill_kind(g, lv, q, nullptr, nullptr, out, T, t0, 0, st);
+                               float* scratch, int64_t scratch_floats, int* counters, int num_cu, hipStream_t st) {
+  // Split a query block's keys over two workgroups when the grid alone would leave
+  // fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own MFMA,
+  // LDS and barrier latencies) and the keys and scratch allow it.
+  const int64_t pairs = int64_t(g.B) * lv.n_ret * g.G * ((T + kQRows - 1) / kQRows);
+  int nsplit = 1;
+  if (pairs < 2 * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
+      pairs * 2 * kSlotFloats <= scratch_floats)
+    nsplit = 2;
+  if (const char* e = std::getenv("DUO_PREFILL_SPLIT")) {
+    const int f = std::atoi(e);
+    if (f == 1 || (f == 2 && pairs <= kPrefillCounters && pairs * 2 * kSlotFloats <= scratch_floats)) nsplit = f;
+  }
+  return launch_prefill_kind(g, lv, q, nullptr, nullptr, out, T, t0, 0, nsplit, scratch, counters, st);
 }
 
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
                                       void* out, int T, int64_t t0, hipStream_t st) {
-  return launch_prefill_kind(g, lv, q, k, v, out, T, t0, 1, st);
+  return launch_prefill_kind(g, lv, q, k, v, out, T, t0, 1, 1, nullptr, nullptr, st);
 }
 
 }  // namespace duo

@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -69,17 +70,29 @@ def words(seed: int, stream: int, counters: np.ndarray) -> np.ndarray:
         return _mix64(key + (c + np.uint64(1)) * GAMMA)
 
 
+def _fill(seed: int, stream: int, flat_c: np.ndarray, flat_o: np.ndarray, a: int) -> None:
+    m16 = np.uint64(0xFFFF)
+    w = words(seed, stream, flat_c[a:a + _CHUNK])
+    s = (w & m16) + ((w >> np.uint64(16)) & m16) + ((w >> np.uint64(32)) & m16) + (w >> np.uint64(48))
+    flat_o[a:a + _CHUNK] = (s.astype(np.int64) - CENTER).astype(np.float32) * SCALE_F32
+
+
 def values_f32(seed: int, stream: int, counters: np.ndarray) -> np.ndarray:
-    """fp32 values for the given counters (any shape)."""
+    """fp32 values for the given counters (any shape).  Large requests are split over
+    threads (NumPy releases the GIL inside these array operations)."""
     counters = np.asarray(counters, dtype=np.uint64)
     out = np.empty(counters.shape, dtype=np.float32)
     flat_c = counters.reshape(-1)
     flat_o = out.reshape(-1)
-    m16 = np.uint64(0xFFFF)
-    for a in range(0, flat_c.size, _CHUNK):
-        w = words(seed, stream, flat_c[a:a + _CHUNK])
-        s = (w & m16) + ((w >> np.uint64(16)) & m16) + ((w >> np.uint64(32)) & m16) + (w >> np.uint64(48))
-        flat_o[a:a + _CHUNK] = (s.astype(np.int64) - CENTER).astype(np.float32) * SCALE_F32
+    starts = range(0, flat_c.size, _CHUNK)
+    if flat_c.size <= 2 * _CHUNK:
+        for a in starts:
+            _fill(seed, stream, flat_c, flat_o, a)
+        return out
+    import concurrent.futures as cf
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda a: _fill(seed, stream, flat_c, flat_o, a), starts))
     return out
 
 

@@ -70,8 +70,9 @@ def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask
         if int4:
             for rows in (batch * nr * cap, batch * nr * cap, batch * ns * nslot, batch * ns * nslot):
                 off = al(off + rows * 4, 256)
-    off = al(off + batch * hq * 1024 * (D + 2) * 4, 256)
+    off = al(off + batch * hq * 2048 * (D + 2) * 4, 256)
     off = al(off + batch * hkv * 4, 256)
+    off = al(off + 65536 * 4, 256)
     return off
 
 

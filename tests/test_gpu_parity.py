@@ -137,6 +137,21 @@ def test_poisoned_workspace_is_cleared_by_init(torch_cuda, name):
     compare(f"{name} decode (poisoned)", to_f64(dec), ref[L:], TOL[w.io_dtype])
 
 
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa_bf16", "all_retrieval_bf16"])
+def test_split_key_prefill_matches_oracle(torch_cuda, monkeypatch, name):
+    """Query blocks whose key range is split over two workgroups (merged by the last to
+    finish) give the same result; forced on small ragged chunks here."""
+    monkeypatch.setenv("DUO_PREFILL_SPLIT", "2")
+    w = SMALL[name]
+    chunks = CHUNKS[name]
+    say(f"split prefill {name} chunks={chunks}")
+    kv, pre, dec, total = run_layer(w, chunks, 2)
+    L = sum(chunks)
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare(f"{name} split prefill", to_f64(pre), ref[:L], TOL[w.io_dtype])
+    compare(f"{name} split decode", to_f64(dec), ref[L:], TOL[w.io_dtype])
+
+
 def test_int4_decode_matches_oracle(torch_cuda):
     w = W("int4_gqa", 22, 8, 4, 128, "bf16", 4, 32, 700, 10, 2, fmt="int4")
     say("int4 decode")
