@@ -34,15 +34,55 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {
+    "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
+    "prefill_retrieval_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "prefill_streaming_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(kernel):
+    import hashlib
+    path = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/traffic.json), or None when none was taken for this kernel and workload or
+    the kernel's source has changed since."""
+    try:
+        entries = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    for e in entries:
+        if e.get("kernel") == kernel and e.get("workload") == workload and e.get("source") == source_digest(kernel):
+            return e.get("bytes_per_launch")
+    return None
+
+
+def copy_probe():
+    """A plain device copy of a known size (1 GiB read + 1 GiB written), so counter runs
+    can calibrate FETCH_SIZE / WRITE_SIZE against known bytes."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def esize(w):
     return 4 if w.io_dtype == "f32" else 2
 
 
-def decode_bytes(w, t):
+def decode_bytes(w, t, layer=0):
     """Algorithmic HBM bytes of one decode-attention launch at query position t, one
     layer: K+V of every visible key counted once per KV head (GQA sharing), plus Q and O.
     int4 vectors cost 64 code bytes + 4 bytes of scale/zero."""
-    mask = w.mask(0)
+    mask = w.mask(layer)
     nr = int(mask.sum())
     ns = w.n_kv_heads - nr
     vec = 68 if w.kv_format == "int4" else w.head_dim * esize(w)
@@ -77,9 +117,8 @@ def run(args):
     torch.cuda.set_device(dev)
     io = B.DUO_DTYPE_F32 if w.io_dtype == "f32" else B.DUO_DTYPE_BF16
     tdt = torch.float32 if w.io_dtype == "f32" else torch.bfloat16
-    has_prefill = w.prefill_chunk > 0
-    if not has_prefill:
-        raise SystemExit("bench.py times workloads with a chunked prefill; decode-only stacks use --workload with prefill")
+    if w.prefill_chunk == 0:
+        return run_stack(args, w)
     total = w.context + w.decode_steps
     chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
     if sum(chunks) < w.context:
@@ -178,9 +217,18 @@ def run(args):
                           "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
                           "avg_launch_us": round(pre_s_ms * 1e3 / len(chunks), 2), "ms_per_step": round(pre_s_ms, 4),
                           "traffic": None})
+    for r in rooflines:
+        r["traffic"] = measured_traffic(r["kernel"], w.name)
     dominant = max(rooflines, key=lambda r: r["ms_per_step"]) if rooflines else None
 
-    prefill_ms = pre_r_ms + pre_s_ms + app_ms * len(chunks) / max(1, len(chunks) + w.decode_steps)
+    # append launches: two per prefill chunk (retrieval caches first, streaming caches
+    # last); a decode step appends inside its attention launch on the MFMA path, or in
+    # one extra launch otherwise
+    n_app = totals["append"][1] / args.steps
+    per_app = app_ms / n_app if n_app else 0.0
+    pre_app = min(n_app, 2 * len(chunks))
+    dec_app_launches = max(0.0, n_app - pre_app) / w.decode_steps
+    prefill_ms = pre_r_ms + pre_s_ms + per_app * pre_app
     res = {
         "metric": METRIC,
         "value": round(tokens / (ms_per_step * 1e-3), 1),
@@ -210,14 +258,120 @@ def run(args):
         "roofline_all": rooflines,
         "cpu_baseline": None,
     }
-    # decode step including its append, from the decode-phase share of append launches
-    n_app = totals["append"][1] / args.steps
-    if n_app:
-        per_app = app_ms / n_app
-        res["components"]["decode_append_plus_attention_us_per_step"] = round(
-            (dec_ms / w.decode_steps + per_app) * 1e3, 3)
+    # decode step including its append (fused into the decode launch on the MFMA path)
+    res["components"]["decode_append_plus_attention_us_per_step"] = round(
+        (dec_ms / w.decode_steps + per_app * dec_app_launches) * 1e3, 3)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, total, args.cpu_seconds)
+    return res
+
+
+def run_stack(args, w):
+    """Decode-only stack (32 layers): every layer's caches are filled to `context` tokens
+    with duo_kv_append (untimed; int4 caches quantise on the way in), then one step =
+    one decode token through all layers (append/evict + attention per layer)."""
+    import numpy as np
+    import torch
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    steps_total = args.warmup + args.steps
+    w = w.scaled(decode_steps=steps_total)
+    io = B.DUO_DTYPE_BF16
+    kvf = B.DUO_KV_INT4_G128 if w.kv_format == "int4" else B.DUO_KV_SAME_AS_IO
+    cfg = B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent, w.max_context,
+                        io, kvf, w.masks().astype(np.uint8))
+    ws = torch.empty(B.duo_kv_bytes(cfg), dtype=torch.uint8, device=dev)
+    h = B.duo_kv_init(cfg, ws)
+    fill_chunk = 65536
+    kbuf = torch.empty((fill_chunk, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vbuf = torch.empty_like(kbuf)
+    t_fill = time.perf_counter()
+    for layer in range(w.n_layers):
+        for c0 in range(0, w.context, fill_chunk):
+            T = min(fill_chunk, w.context - c0)
+            n = T * w.n_kv_heads * w.head_dim
+            B.duo_synth_fill(kbuf, io, w.seed, layer * 4 + 1, c0 * w.n_kv_heads * w.head_dim, n)
+            B.duo_synth_fill(vbuf, io, w.seed, layer * 4 + 2, c0 * w.n_kv_heads * w.head_dim, n)
+            B.duo_kv_append(h, layer, kbuf[:T], vbuf[:T], T)
+    torch.cuda.synchronize()
+    log(f"stack fill: {w.n_layers} layers x {w.context} tokens in {time.perf_counter() - t_fill:.1f}s")
+    del kbuf, vbuf
+
+    def gen(layer, kind, H):
+        t = torch.empty((steps_total, H, w.head_dim), dtype=torch.bfloat16, device=dev)
+        B.duo_synth_fill(t, io, w.seed, layer * 4 + I.KIND_STREAM[kind], w.context * H * w.head_dim, t.numel())
+        return t
+
+    Qs = [gen(l, "q", w.n_q_heads) for l in range(w.n_layers)]
+    Ks = [gen(l, "k", w.n_kv_heads) for l in range(w.n_layers)]
+    Vs = [gen(l, "v", w.n_kv_heads) for l in range(w.n_layers)]
+    out = torch.empty((w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s):
+        for layer in range(w.n_layers):
+            B.duo_decode(h, layer, Qs[layer][s], Ks[layer][s], Vs[layer][s], out)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    B.duo_profile_collect(h)
+    B.duo_profile_enable(h, True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for s in range(args.warmup, steps_total):
+        step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    prof = B.duo_profile_collect(h)
+    dec_ms = prof["decode"][0] / args.steps
+    app_ms = prof["append"][0] / args.steps
+    dec_bytes = 0
+    for s in range(args.warmup, steps_total):
+        t = w.context + s
+        for layer in range(w.n_layers):
+            dec_bytes += decode_bytes(w, t, layer)
+    dec_bytes /= args.steps
+    a = dec_bytes / (dec_ms * 1e-3) / 1e9
+    roof = {"kernel": "decode_attention", "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(prof["decode"][0] * 1e3 / max(1, prof["decode"][1]), 3),
+            "ms_per_step": round(dec_ms, 4), "traffic": measured_traffic("decode_attention", w.name)}
+    res = {
+        "metric": METRIC,
+        "value": round(1.0 / (ms_per_step * 1e-3), 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": 1, "seq_len": w.context, "n_layers": w.n_layers,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "retrieval_kv_heads_per_layer": int(w.mask(0).sum()), "sink": w.sink, "recent": w.recent,
+                   "kv_format": w.kv_format, "parallelism": "single_gpu"},
+        "components": {"decode_us_per_step": round(ms_per_step * 1e3, 2),
+                       "decode_attention_us_per_step": round(dec_ms * 1e3, 2),
+                       "append_us_per_step": round(app_ms * 1e3, 2),
+                       "workspace_gb": round(ws.numel() / 1e9, 2),
+                       "wall_s": round(wall, 3)},
+        "roofline": roof,
+        "roofline_all": [roof],
+        "cpu_baseline": None,
+    }
+    B.duo_kv_free(h)
     return res
 
 
@@ -271,11 +425,15 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_mha_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    print(json.dumps(run(args)), flush=True)
+    res = run(args)
+    if args.copy_probe:
+        copy_probe()
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

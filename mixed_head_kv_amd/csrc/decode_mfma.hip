@@ -39,6 +39,10 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+constexpr int kWaves = 8;                 // wavefronts per decode workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStride = 32 * kWaves;      // keys per round of the workgroup
+
 struct Tile {
   u32x4 k0[4], k1[4];  // K rows for the two 16-key MFMA tiles, 4 k-steps each
   u32x4 v[8];          // V^T operand for the 8 d-blocks
@@ -53,15 +57,17 @@ struct Tile {
 __device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                  int64_t cache_row0, int64_t base, int r, int grp, int64_t new_row,
                                  const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
+  // K: the tile's 16-byte chunks are stored in operand order, one contiguous KB per
+  // load instruction (chunk (t*4 + s)*64 + lane)
+  const int lane = grp * 16 + r;
   const int64_t key0 = base + 8 * (r >> 2) + (r & 3);
-  const uint16_t* k0p = key0 == new_row ? k_new : K + (cache_row0 + key0) * 128;
-  const uint16_t* k1p = key0 + 4 == new_row ? k_new : K + (cache_row0 + key0 + 4) * 128;
-  const u32x4* k0 = reinterpret_cast<const u32x4*>(k0p + 32 * grp);
-  const u32x4* k1 = reinterpret_cast<const u32x4*>(k1p + 32 * grp);
+  const u32x4* kt = reinterpret_cast<const u32x4*>(K + ((cache_row0 + base) >> 5) * 4096) + lane;
+  const u32x4* kn = reinterpret_cast<const u32x4*>(k_new + 32 * grp);
+  const bool n0 = key0 == new_row, n1 = key0 + 4 == new_row;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    t.k0[s] = __builtin_nontemporal_load(k0 + s);
-    t.k1[s] = __builtin_nontemporal_load(k1 + s);
+    t.k0[s] = __builtin_nontemporal_load(n0 ? kn + s : kt + s * 64);
+    t.k1[s] = __builtin_nontemporal_load(n1 ? kn + s : kt + (4 + s) * 64);
   }
   const int64_t b8 = base + 8 * grp;
   const u32x4* vb = reinterpret_cast<const u32x4*>(V + (cache_row0 + b8) * 128) + r;
@@ -69,77 +75,100 @@ __device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K, const 
   for (int j = 0; j < 8; ++j) t.v[j] = __builtin_nontemporal_load(vb + 16 * j);
 }
 
-// Replace the V element of row `new_row` (inside this lane's 8-key block) by v_new.
-__device__ inline void patch_v(Tile& t, int64_t base, int r, int grp, int64_t new_row,
-                               const uint16_t* __restrict__ v_new) {
+// Replace the V element of row `new_row` (inside this lane's 8-key block) by the new
+// token's values vn[j] = v_new[16j + r], preloaded before the loop.
+__device__ inline void patch_v(Tile& t, int64_t base, int grp, int64_t new_row, const uint32_t* vn) {
   const int64_t e = new_row - (base + 8 * grp);
   if (e < 0 || e >= 8) return;
   const int w = static_cast<int>(e >> 1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t x = v_new[16 * j + r];
     const uint32_t word = t.v[j][w];
-    t.v[j][w] = (e & 1) ? ((word & 0xffffu) | (x << 16)) : ((word & 0xffff0000u) | x);
+    t.v[j][w] = (e & 1) ? ((word & 0xffffu) | (vn[j] << 16)) : ((word & 0xffff0000u) | vn[j]);
   }
 }
 
-// Merge of the split partials of one KV head (run by the last workgroup to finish):
-// every (m_s, l_s) is loaded at once into LDS, the weights 2^(m_s - M) are formed per
-// query, then each thread sums its output elements over the splits with independent
-// loads in flight.  `scratch` holds G * nsplit * 2 floats.
+// Merge of the split partials of one KV head (run by the last workgroup to finish).
+// Each output element is owned by up to four threads; a thread walks its splits in
+// batches of 32 whose (m, l, o) loads are all issued together, merging online with a
+// running maximum, so a batch costs one memory round trip.  The owners of an element
+// combine through LDS (`scratch`, 3 floats per thread).
 __device__ void merge_splits_wide(const Geom& g, const DecodePlan& p, int b, int kvh, int nsplit, float* scratch,
                                   uint16_t* __restrict__ out) {
-  const int G = g.G;
-  float* w = scratch;                 // [G][nsplit] weights, first m then 2^(m - M)
-  float* lsum = scratch + G * nsplit; // [G][nsplit] l
-  for (int e = threadIdx.x; e < G * nsplit; e += 256) {
-    const int i = e / nsplit, s = e % nsplit;
-    const float* pp = partial_ptr(g, p, b, kvh * G + i, s);
-    w[e] = load_coherent(pp);
-    lsum[e] = load_coherent(pp + 1);
-  }
-  __syncthreads();
-  __shared__ float s_M[DUO_MAX_GROUP], s_L[DUO_MAX_GROUP];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = wave; i < G; i += 4) {
-    float M = kNegInf;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, w[i * nsplit + s]);
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.0f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float x = exp2f(w[i * nsplit + s] - M);
-      w[i * nsplit + s] = x;
-      L = fmaf(x, lsum[i * nsplit + s], L);
-    }
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (lane == 0) s_L[i] = L;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * 128; e += 256) {
-    const int i = e >> 7, d = e & 127;
-    const float* base = partial_ptr(g, p, b, kvh * G + i, 0) + 2 + d;
-    const int64_t stride = 130;
-    float acc = 0.0f;
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
-      float x[8];
+  constexpr int kBatch = 32;
+  const int nout = g.G * 128;
+  const int tpo = nout >= kThreads ? 1 : (kThreads / nout >= 4 ? 4 : kThreads / nout);  // owners per element
+  const int per_pass = kThreads / tpo;
+  const int part = threadIdx.x / per_pass;
+  for (int e0 = 0; e0 < nout; e0 += per_pass) {
+    const int e = e0 + threadIdx.x % per_pass;
+    float M = kNegInf, L = 0.0f, acc = 0.0f;
+    if (e < nout) {
+      const int i = e >> 7, d = e & 127;
+      for (int s0 = part; s0 < nsplit; s0 += kBatch * tpo) {
+        float mm[kBatch], ll[kBatch], oo[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = load_coherent(base + (s + u) * stride);
+        for (int u = 0; u < kBatch; ++u) {
+          const int s = s0 + u * tpo;
+          if (s < nsplit) {
+            const float* pp = partial_ptr(g, p, b, kvh * g.G + i, s);
+            mm[u] = load_coherent(pp);
+            ll[u] = load_coherent(pp + 1);
+            oo[u] = load_coherent(pp + 2 + d);
+          } else {
+            mm[u] = kNegInf;
+            ll[u] = 0.0f;
+            oo[u] = 0.0f;
+          }
+        }
+        float cm = M;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(w[i * nsplit + s + u], x[u], acc);
+        for (int u = 0; u < kBatch; ++u) cm = fmaxf(cm, mm[u]);
+        const float ref = cm == kNegInf ? 0.0f : cm;
+        const float sc = __builtin_amdgcn_exp2f(M - ref);
+        L *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float w = __builtin_amdgcn_exp2f(mm[u] - ref);
+          L = fmaf(w, ll[u], L);
+          acc = fmaf(w, oo[u], acc);
+        }
+        M = cm;
+      }
     }
-    for (; s < nsplit; ++s) acc = fmaf(w[i * nsplit + s], load_coherent(base + s * stride), acc);
-    out[(int64_t(b) * g.Hq + kvh * G + i) * 128 + d] = f32_to_bf16(acc / s_L[i]);
+    if (tpo > 1) {
+      __syncthreads();
+      scratch[3 * threadIdx.x] = M;
+      scratch[3 * threadIdx.x + 1] = L;
+      scratch[3 * threadIdx.x + 2] = acc;
+      __syncthreads();
+      if (part == 0) {
+        for (int q2 = 1; q2 < tpo; ++q2) {
+          const int o = 3 * (threadIdx.x + q2 * per_pass);
+          const float M2 = scratch[o], L2 = scratch[o + 1], A2 = scratch[o + 2];
+          const float Mx = fmaxf(M, M2);
+          const float ref = Mx == kNegInf ? 0.0f : Mx;
+          const float w1 = __builtin_amdgcn_exp2f(M - ref), w2 = __builtin_amdgcn_exp2f(M2 - ref);
+          L = L * w1 + L2 * w2;
+          acc = acc * w1 + A2 * w2;
+          M = Mx;
+        }
+      }
+    }
+    if (part == 0 && e < nout)
+      out[(int64_t(b) * g.Hq + kvh * g.G + (e >> 7)) * 128 + (e & 127)] = f32_to_bf16(acc / L);
   }
 }
 
-__global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, DecodePlan p,
+__global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, DecodePlan p,
                                                        const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ float s_o[4][16][129];  // also the merge scratch (G * nsplit * 2 floats)
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+  __shared__ float s_o[kWaves][16][129];  // also the merge scratch
 
   const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int r = lane & 15, grp = lane >> 4;
   const int G = g.G;
   const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
@@ -156,7 +185,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, De
     uint16_t* Kw = reinterpret_cast<uint16_t*>(c.k);
     uint16_t* Vw = reinterpret_cast<uint16_t*>(c.v);
     const int d = threadIdx.x;
-    Kw[(row0 + new_row) * 128 + d] = k_new[d];
+    Kw[k_chunk_tiled(row0 + new_row, d >> 3) + (d & 7)] = k_new[d];
     Vw[v_index(it.cache, c.rows, new_row, 128, d)] = v_new[d];
   }
 
@@ -176,51 +205,75 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, De
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const float sl2 = g.scale_log2;
-  int64_t base = it.key0 + 32 * wave;
-  Tile cur, nxt;
-  if (base < it.key1) load_tile(cur, K, V, row0, base, r, grp, new_row, k_new, v_new);
-  for (; base < it.key1; base += 128) {
-    const int64_t next = base + 128;
-    if (next < it.key1) load_tile(nxt, K, V, row0, next, r, grp, new_row, k_new, v_new);
-    if (new_row >= base && new_row < base + 32) patch_v(cur, base, r, grp, new_row, v_new);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  // Each wavefront takes every fourth 32-key tile of the range and keeps a ring of
+  // kRing tiles in flight: the slot just consumed is refilled with the tile kRing
+  // steps ahead, so memory latency is covered by several tiles of work.
+  // Each wavefront takes every kWaves-th 32-key tile of the range and keeps a ring of
+  // kRing tiles in flight: the slot just consumed is refilled with the tile kRing
+  // rounds ahead.  Loads are issued unconditionally (a tile past the end re-reads the
+  // wave's first tile, an L2 hit that is never used) so the compiler can count them.
+  constexpr int kRing = 2;
+  Tile ring[kRing];
+  const int64_t first = it.key0 + 32 * wave;
+  const int64_t fallback = first < it.key1 ? first : it.key0;
+  uint32_t vn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bool has_new = new_row >= it.key0 && new_row < it.key1;
+  if (has_new) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      s0 = mfma16(cur.k0[s], qop[s], s0);
-      s1 = mfma16(cur.k1[s], qop[s], s1);
+    for (int j = 0; j < 8; ++j) vn[j] = v_new[16 * j + r];
+  }
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) {
+    const int64_t b = first + kStride * u;
+    load_tile(ring[u], K, V, row0, b < it.key1 ? b : fallback, r, grp, new_row, k_new, v_new);
+  }
+  for (int64_t base0 = first; base0 < it.key1; base0 += kStride * kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int64_t base = base0 + kStride * u;
+      if (base >= it.key1) break;
+      Tile& cur = ring[u];
+      if (has_new && new_row >= base && new_row < base + 32) patch_v(cur, base, grp, new_row, vn);
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        s0 = mfma16(cur.k0[s], qop[s], s0);
+        s1 = mfma16(cur.k1[s], qop[s], s1);
+      }
+      // lane holds scores of keys base + 8*grp + 0..7 for query r; keys past the range
+      // become -inf, the max is kept on raw scores and the scale folded into the FMA
+      float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const int64_t kfirst = base + 8 * grp;
+      if (base + 32 > it.key1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      const float mn = fmaxf(m, mx);
+      const float mref = mn == kNegInf ? 0.0f : mn;
+      if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] *= alpha;
+      }
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
+        l += sc[i];
+      }
+      const u32x4 pb = {pack_bf16(sc[0], sc[1]), pack_bf16(sc[2], sc[3]), pack_bf16(sc[4], sc[5]),
+                        pack_bf16(sc[6], sc[7])};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j]);
+      const int64_t nb = base + kStride * kRing;
+      load_tile(cur, K, V, row0, nb < it.key1 ? nb : fallback, r, grp, new_row, k_new, v_new);
     }
-    // lane holds scores of keys base + 8*grp + 0..7 for query r; keys past the range
-    // become -inf, the max is kept on raw scores and the scale folded into the FMA
-    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    const int64_t kfirst = base + 8 * grp;
-    if (base + 32 > it.key1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == kNegInf ? 0.0f : mn;
-    if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
-      const float alpha = __builtin_amdgcn_exp2f(m - mref);
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] *= alpha;
-    }
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sc[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
-      l += sc[i];
-    }
-    const u32x4 pb = {pack_bf16(sc[0], sc[1]), pack_bf16(sc[2], sc[3]), pack_bf16(sc[4], sc[5]),
-                      pack_bf16(sc[6], sc[7])};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j]);
-    cur = nxt;
   }
 
   // Combine the four wavefronts: lane sums over its group, then across waves in LDS.
@@ -237,14 +290,14 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma(Geom g, LayerView lv, De
   __syncthreads();
 
   const int pairs = G * 128;
-  for (int e = threadIdx.x; e < pairs; e += 256) {
+  for (int e = threadIdx.x; e < pairs; e += kThreads) {
     const int qi = e >> 7, d = e & 127;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][qi]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][qi]);
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
       L = fmaf(wt, s_l[w][qi], L);
       acc = fmaf(wt, s_o[w][qi][d], acc);
@@ -303,10 +356,11 @@ struct Tile4 {
 
 __device__ inline void load_tile4(Tile4& t, const CacheRegion& c, int64_t cache, int64_t base, int r, int grp) {
   const int64_t row0 = cache * c.rows;
-  const int64_t key0 = base + 8 * (r >> 2) + (r & 3);
-  const uint8_t* kc = reinterpret_cast<const uint8_t*>(c.k);
-  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (row0 + key0) * 64 + 16 * grp));
-  const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (row0 + key0 + 4) * 64 + 16 * grp));
+  // K codes: 32-key tiles of 2 KB in operand order, one contiguous KB per instruction
+  const u32x4* kt = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(c.k) + ((row0 + base) >> 5) * 2048) +
+                    grp * 16 + r;
+  const u32x4 a = __builtin_nontemporal_load(kt);
+  const u32x4 b = __builtin_nontemporal_load(kt + 64);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     t.k0[s] = a[s];
@@ -323,13 +377,14 @@ __device__ inline void load_tile4(Tile4& t, const CacheRegion& c, int64_t cache,
   t.vm1 = __builtin_nontemporal_load(vm + 1);
 }
 
-__global__ void __launch_bounds__(256, 2) k_decode_mfma_int4(Geom g, LayerView lv, DecodePlan p,
+__global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, DecodePlan p,
                                                             const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ float s_o[4][16][129];  // also the merge scratch (G * nsplit * 2 floats)
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+  __shared__ float s_o[kWaves][16][129];  // also the merge scratch
 
   const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int r = lane & 15, grp = lane >> 4;
   const int G = g.G;
   const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
@@ -355,79 +410,90 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma_int4(Geom g, LayerView l
   }
   const float q128 = 128.0f * qsum;
 
-  float m = kNegInf, l = 0.0f, asum = 0.0f, zsum = 0.0f;
+  float m = kNegInf, l = 0.0f, zsum = 0.0f;
   f32x4 o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // sum_j p'_j over all 32 keys of a tile, on the matrix core: a row of bf16 ones
+  // times P'^T (every row of the result holds the sum)
+  f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = g.scale_log2;
-  int64_t base = it.key0 + 32 * wave;
-  Tile4 cur, nxt;
-  if (base < it.key1) load_tile4(cur, c, it.cache, base, r, grp);
-  for (; base < it.key1; base += 128) {
-    const int64_t next = base + 128;
-    if (next < it.key1) load_tile4(nxt, c, it.cache, next, r, grp);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kRing = 3;
+  Tile4 ring[kRing];
+  const int64_t first = it.key0 + 32 * wave;
+  const int64_t fallback = first < it.key1 ? first : it.key0;  // unconditional loads, as above
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      s0 = mfma16(codes_to_bf16(cur.k0[s]), qop[s], s0);
-      s1 = mfma16(codes_to_bf16(cur.k1[s]), qop[s], s1);
+  for (int u = 0; u < kRing; ++u) {
+    const int64_t b = first + kStride * u;
+    load_tile4(ring[u], c, it.cache, b < it.key1 ? b : fallback, r, grp);
+  }
+  for (int64_t base0 = first; base0 < it.key1; base0 += kStride * kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int64_t base = base0 + kStride * u;
+      if (base >= it.key1) break;
+      Tile4& cur = ring[u];
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        s0 = mfma16(codes_to_bf16(cur.k0[s]), qop[s], s0);
+        s1 = mfma16(codes_to_bf16(cur.k1[s]), qop[s], s1);
+      }
+      // keys base + 8*grp + i: (scale, zero) pairs in km0 (i < 4) and km1 (i >= 4)
+      float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t mk = i < 4 ? cur.km0[i] : cur.km1[i - 4];
+        sc[i] = fmaf(half_lo(mk), sc[i] - q128, half_hi(mk) * qsum);
+      }
+      const int64_t kfirst = base + 8 * grp;
+      if (base + 32 > it.key1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      const float mn = fmaxf(m, mx);
+      const float mref = mn == kNegInf ? 0.0f : mn;
+      if (__ballot(mn > m)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        l *= alpha;
+        zsum *= alpha;
+        pacc *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] *= alpha;
+      }
+      m = mn;
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pi = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
+        const uint32_t mv = i < 4 ? cur.vm0[i] : cur.vm1[i - 4];
+        l += pi;
+        zsum = fmaf(pi, half_hi(mv), zsum);
+        pw[i] = pi * half_lo(mv);
+      }
+      // P'^T operand in the V codes' key order (0, 2, 4, 6, 1, 3, 5, 7)
+      const u32x4 pb = {pack_bf16(pw[0], pw[2]), pack_bf16(pw[4], pw[6]), pack_bf16(pw[1], pw[3]),
+                        pack_bf16(pw[5], pw[7])};
+      pacc = mfma16(ones, pb, pacc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = mfma16(codes_to_bf16(cur.v[j]), pb, o[j]);
+      const int64_t nb = base + kStride * kRing;
+      load_tile4(cur, c, it.cache, nb < it.key1 ? nb : fallback, r, grp);
     }
-    // keys base + 8*grp + i: (scale, zero) pairs in km0 (i < 4) and km1 (i >= 4)
-    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t mk = i < 4 ? cur.km0[i] : cur.km1[i - 4];
-      sc[i] = fmaf(half_lo(mk), sc[i] - q128, half_hi(mk) * qsum);
-    }
-    const int64_t kfirst = base + 8 * grp;
-    if (base + 32 > it.key1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = kfirst + i < it.key1 ? sc[i] : kNegInf;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == kNegInf ? 0.0f : mn;
-    if (__ballot(mn > m)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mref);
-      l *= alpha;
-      asum *= alpha;
-      zsum *= alpha;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] *= alpha;
-    }
-    m = mn;
-    float pw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pi = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -mref));
-      const uint32_t mv = i < 4 ? cur.vm0[i] : cur.vm1[i - 4];
-      l += pi;
-      zsum = fmaf(pi, half_hi(mv), zsum);
-      pw[i] = pi * half_lo(mv);
-    }
-    // P'^T operand in the V codes' key order (0, 2, 4, 6, 1, 3, 5, 7); asum adds the
-    // bf16-rounded weights exactly as the MFMA sees them
-    const u32x4 pb = {pack_bf16(pw[0], pw[2]), pack_bf16(pw[4], pw[6]), pack_bf16(pw[1], pw[3]),
-                      pack_bf16(pw[5], pw[7])};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) asum += bf16_to_f32(pb[e] & 0xffff) + bf16_to_f32(pb[e] >> 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = mfma16(codes_to_bf16(cur.v[j]), pb, o[j]);
-    cur = nxt;
   }
 
   // Per-query corrections are summed over the lane's group, then applied to its O.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  asum += __shfl_xor(asum, 16);
-  asum += __shfl_xor(asum, 32);
   zsum += __shfl_xor(zsum, 16);
   zsum += __shfl_xor(zsum, 32);
-  const float corr = zsum - 128.0f * asum;
+  const float corr = zsum - 128.0f * pacc[0];  // pacc already sums all 32 keys of each tile
   if (grp == 0) {
     s_m[wave][r] = m;
     s_l[wave][r] = l;
@@ -439,14 +505,14 @@ __global__ void __launch_bounds__(256, 2) k_decode_mfma_int4(Geom g, LayerView l
   __syncthreads();
 
   const int pairs = G * 128;
-  for (int e = threadIdx.x; e < pairs; e += 256) {
+  for (int e = threadIdx.x; e < pairs; e += kThreads) {
     const int qi = e >> 7, d = e & 127;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][qi]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][qi]);
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
       L = fmaf(wt, s_l[w][qi], L);
       acc = fmaf(wt, s_o[w][qi][d], acc);
@@ -474,10 +540,10 @@ hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePl
   const int items = g.B * (lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s);
   if (items == 0) return hipSuccess;
   if (g.kvfmt == DUO_KV_INT4_G128)
-    hipLaunchKernelGGL(k_decode_mfma_int4, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+    hipLaunchKernelGGL(k_decode_mfma_int4, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
                        static_cast<uint16_t*>(out));
   else
-    hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(256), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+    hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
                        static_cast<uint16_t*>(out));
   return hipGetLastError();
 }

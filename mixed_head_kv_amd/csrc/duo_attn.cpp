@@ -221,16 +221,14 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   const int64_t nkeys = t + 1;
   const int64_t heads = int64_t(h->cfg.batch) * h->views[layer].n_ret;
   // Retrieval heads: about one workgroup per CU over all of them, at least 512 keys
-  // per split (a multiple of 64), within the partial buffer and the merge's LDS.
+  // per split (a multiple of 64), within the partial buffer.
   int64_t chunk = 512;
   if (heads > 0) {
     const int64_t per_head = (h->num_cu + heads - 1) / heads;
     const int64_t want = (nkeys + per_head - 1) / per_head;
     if (want > chunk) chunk = want;
   }
-  int64_t max_splits = duo::kMaxSplits;
-  const int64_t merge_cap = duo::kMergeScratchFloats / (2 * h->geom.G);
-  if (h->use_mfma_decode && merge_cap < max_splits) max_splits = merge_cap;
+  const int64_t max_splits = duo::kMaxSplits;
   const int64_t min_chunk = (nkeys + max_splits - 1) / max_splits;
   if (chunk < min_chunk) chunk = min_chunk;
   if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
@@ -296,12 +294,14 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
     std::memset(&v, 0, sizeof(v));
     v.n_ret = y.n_ret;
     v.n_str = y.n_str;
+    // bf16 K with head_dim 128 lives in MFMA-ordered 32-key tiles (int4 K codes always do)
+    const int tiled = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && !int4;
     v.ret = CacheRegion{h->ws + y.ret_k, h->ws + y.ret_v,
                         int4 ? reinterpret_cast<uint16_t*>(h->ws + y.ret_km) : nullptr,
-                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.ret_vm) : nullptr, L.cap};
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.ret_vm) : nullptr, L.cap, tiled};
     v.str = CacheRegion{h->ws + y.str_k, h->ws + y.str_v,
                         int4 ? reinterpret_cast<uint16_t*>(h->ws + y.str_km) : nullptr,
-                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.str_vm) : nullptr, L.nslot};
+                        int4 ? reinterpret_cast<uint16_t*>(h->ws + y.str_vm) : nullptr, L.nslot, tiled};
     int nr = 0, ns = 0;
     for (int kv = 0; kv < cfg->n_kv_heads; ++kv) {
       if (h->mask[size_t(l) * cfg->n_kv_heads + kv]) {

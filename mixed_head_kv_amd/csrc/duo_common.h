@@ -2,14 +2,21 @@
 // libduo_attn.so: workspace geometry, cache addressing, element conversions.
 //
 // Cache layout in HBM (per layer, per sequence b, per KV head of one kind):
-//   retrieval K : row-major rows [cap][D]; row = absolute position.
+//   retrieval K : rows of D values, row = absolute position.  bf16 with D = 128 stores
+//                 them in 32-key tiles (8 KB) whose 16-byte chunks are ordered for the
+//                 MFMA K operand (k_tiled): chunk c = dims 8c..8c+7 of key kk of the tile
+//                 sits at chunk ((t*4 + c%4)*4 + c/4)*16 + r with t = (kk>>2)&1 and
+//                 r = 4*(kk>>3) + (kk&3), so each 1 KB of the tile is exactly what one
+//                 load instruction of a wavefront needs.  Other shapes are row-major.
 //   retrieval V : 8-row tiles stored d-major, [cap/8][D][8]; element (row, d) sits at
 //                 ((row & ~7) * D + d * 8 + (row & 7)).  Eight consecutive keys of one
 //                 dimension are contiguous, which is the operand order the MFMA
 //                 products P*V read (the key index is the contraction index there).
 //   streaming K/V: the same two layouts over `nslot` slots; slot s < sink holds sink
 //                 position s, slot sink + ((p - sink) mod recent) holds recent position p.
-//   int4 (group 128): K codes row-major [cap][D/2] bytes (byte k = codes 2k | 2k+1 << 4),
+//   int4 (group 128): K codes in 32-key tiles of 2 KB (byte b of key kk at
+//                 (t*64 + (b/16)*16 + r)*16 + b%16, same t, r as above; byte b holds
+//                 codes 2b | 2b+1 << 4),
 //                 V codes in 8-row tiles [cap/8][D][8 nibbles = 4 bytes] (nibble r of the
 //                 dword = row r of the tile), and per row a uint16 pair (scale, zero)
 //                 of fp16 bit patterns, [cap][2] for K and for V.
@@ -26,7 +33,6 @@ namespace duo {
 
 constexpr int kMaxSplits = 2048;    // split-K partial slots per query head (decode; prefill reuses the buffer)
 constexpr int kPrefillCounters = 1 << 16;  // arrival counters for split prefill query blocks
-constexpr int kMergeScratchFloats = 4 * 16 * 129;  // LDS the MFMA decode merge may use
 constexpr int kRowAlign = 64;       // cache rows are allocated in multiples of this
 constexpr int kKindRetrieval = 1;
 constexpr int kKindStreaming = 0;
@@ -38,6 +44,7 @@ struct CacheRegion {
   uint16_t* k_meta; // int4: (scale, zero) per row; else null
   uint16_t* v_meta;
   int64_t rows;
+  int k_tiled;      // K rows in MFMA-ordered 32-key tiles (bf16, D = 128)
 };
 
 // Everything a kernel needs to know about one layer of one handle.
@@ -93,8 +100,26 @@ __device__ inline void io_store(void* p, int64_t i, float v) {
 
 // ---- cache addressing ----------------------------------------------------------
 
-__device__ inline int64_t k_index(int64_t cache, int64_t rows, int64_t row, int D, int d) {
-  return (cache * rows + row) * D + d;
+// Element offset of 16-byte chunk c (dims 8c..8c+7) of global K row `grow` in an
+// MFMA-ordered 32-key tile (bf16, D = 128).
+__host__ __device__ inline int64_t k_chunk_tiled(int64_t grow, int c) {
+  const int kk = static_cast<int>(grow & 31);
+  const int t = (kk >> 2) & 1;
+  const int r = ((kk >> 3) << 2) | (kk & 3);
+  return (grow >> 5) * 4096 + static_cast<int64_t>(((t * 4 + (c & 3)) * 4 + (c >> 2)) * 16 + r) * 8;
+}
+
+// Byte offset of code byte b (0..63) of global int4 K row `grow` (32-key tiles of 2 KB).
+__host__ __device__ inline int64_t k_code_byte(int64_t grow, int b) {
+  const int kk = static_cast<int>(grow & 31);
+  const int t = (kk >> 2) & 1;
+  const int r = ((kk >> 3) << 2) | (kk & 3);
+  return (grow >> 5) * 2048 + static_cast<int64_t>((t * 64 + (b >> 4) * 16 + r) * 16 + (b & 15));
+}
+
+__device__ inline int64_t k_index(const CacheRegion& c, int64_t cache, int64_t row, int D, int d) {
+  const int64_t grow = cache * c.rows + row;
+  return c.k_tiled ? k_chunk_tiled(grow, d >> 3) + (d & 7) : grow * D + d;
 }
 __device__ inline int64_t v_index(int64_t cache, int64_t rows, int64_t row, int D, int d) {
   return (cache * rows + (row & ~int64_t(7))) * D + int64_t(d) * 8 + (row & 7);
@@ -111,13 +136,12 @@ __device__ inline float int4_value(uint32_t q, uint16_t s_bits, uint16_t z_bits)
 template <int IO, int KVF>
 __device__ inline float cache_k(const CacheRegion& c, int64_t cache, int64_t row, int D, int d) {
   if constexpr (KVF == DUO_KV_INT4_G128) {
-    const uint8_t* codes = reinterpret_cast<const uint8_t*>(c.k) + (cache * c.rows + row) * (D / 2);
-    uint32_t byte = codes[d >> 1];
+    const uint32_t byte = reinterpret_cast<const uint8_t*>(c.k)[k_code_byte(cache * c.rows + row, d >> 1)];
     uint32_t q = (d & 1) ? (byte >> 4) : (byte & 15u);
     const uint16_t* m = c.k_meta + (cache * c.rows + row) * 2;
     return int4_value(q, m[0], m[1]);
   } else {
-    return io_load<IO>(c.k, k_index(cache, c.rows, row, D, d));
+    return io_load<IO>(c.k, k_index(c, cache, row, D, d));
   }
 }
 

@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) k_append(Geom g, LayerView lv, const T* _
     const int t = source_token(streaming, row, t0, T_, g.S, g.R);
     if (t >= 0) {
       const int64_t src = ((int64_t(b) * T_ + t) * g.Hkv + kvh) * D + d;
-      K[k_index(cache, c.rows, row, D, d)] = k[src];
+      K[k_index(c, cache, row, D, d)] = k[src];
       vbuf[r] = v[src];
       ++nvalid;
     }
@@ -145,7 +145,8 @@ __global__ void __launch_bounds__(256) k_append_bf16(Geom g, LayerView lv, const
       continue;
     }
     const int64_t off = (in0 + int64_t(src[r]) * g.Hkv) * D + 8 * ch;
-    *reinterpret_cast<uint4*>(K + (int64_t(cache) * c.rows + row0 + r) * D + 8 * ch) =
+    const int64_t grow = int64_t(cache) * c.rows + row0 + r;
+    *reinterpret_cast<uint4*>(K + (c.k_tiled ? k_chunk_tiled(grow, ch) : grow * D + 8 * ch)) =
         *reinterpret_cast<const uint4*>(k + off);
     vr[r] = *reinterpret_cast<const uint4*>(v + off);
   }
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256) k_append_int4(Geom g, LayerView lv, const
     const uint32_t vp = *reinterpret_cast<const uint32_t*>(v + src);
     const Q4 qk = quantize_pair(bf16_to_f32(kp & 0xffff), bf16_to_f32(kp >> 16));
     const Q4 qv = quantize_pair(bf16_to_f32(vp & 0xffff), bf16_to_f32(vp >> 16));
-    kc[(cache * c.rows + row) * 64 + lane] = static_cast<uint8_t>(qk.q0 | (qk.q1 << 4));
+    kc[k_code_byte(cache * c.rows + row, lane)] = static_cast<uint8_t>(qk.q0 | (qk.q1 << 4));
     if (lane == 0) {
       uint16_t* km = c.k_meta + (cache * c.rows + row) * 2;
       uint16_t* vm = c.v_meta + (cache * c.rows + row) * 2;
@@ -287,7 +288,7 @@ __global__ void k_read_int4(Geom g, CacheRegion c, int64_t cache, int streaming,
   const int64_t row = streaming ? stream_slot(p, g.S, g.R) : p;
   uint8_t byte;
   if (which == 0) {
-    byte = reinterpret_cast<const uint8_t*>(c.k)[(cache * c.rows + row) * 64 + kb];
+    byte = reinterpret_cast<const uint8_t*>(c.k)[k_code_byte(cache * c.rows + row, kb)];
   } else {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(c.v) + (cache * c.rows + (row & ~int64_t(7))) / 8 * 128;
     const uint32_t lo = (w[2 * kb] >> (4 * (row & 7))) & 15u;

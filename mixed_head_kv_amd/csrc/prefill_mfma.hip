@@ -127,11 +127,11 @@ __device__ inline void stage_load(const PrefillArgs& a, int b, int kvh, int64_t 
       const uint16_t* src = nullptr;
       if (pos >= a.t0) {
         const int64_t t = pos - a.t0;
-        if (t < a.T) src = a.k + (in_row + t * g.Hkv) * 128;
-      } else {
-        src = reinterpret_cast<const uint16_t*>(c.k) + (cache * c.rows + slot_of(pos, g.S, g.R)) * 128;
+        if (t < a.T) src = a.k + (in_row + t * g.Hkv) * 128 + col * 8;
+      } else {  // cache K rows are MFMA-ordered 32-key tiles
+        src = reinterpret_cast<const uint16_t*>(c.k) + k_chunk_tiled(cache * c.rows + slot_of(pos, g.S, g.R), col);
       }
-      st.k[u] = src ? *reinterpret_cast<const u32x4*>(src + col * 8) : u32x4{0, 0, 0, 0};
+      st.k[u] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
     }
     // V: task = (key pair kp in 0..31, 8-dim chunk dc in 0..15); two tasks per thread,
     // each two 16-byte rows (keys 2kp and 2kp + 1, dims 8dc .. 8dc+7).
@@ -161,14 +161,28 @@ __device__ inline void stage_load(const PrefillArgs& a, int b, int kvh, int64_t 
   }
 }
 
+// LDS K tiles are row-major with 16-byte chunks XOR-swizzled by row.  A copied tile
+// arrives in the cache's MFMA-ordered 32-key layout: its chunk p of 32-key tile q holds
+// dims 8*(4*grp + s) of key 32q + 8*(r>>2) + (r&3) + 4t, where p = (t*4 + s)*64 + grp*16 + r.
+__device__ inline int lds_k_offset(int row, int col16) { return row * 256 + ((col16 ^ (row & 15)) * 16); }
+
 template <bool STREAMING>
 __device__ inline void stage_store(int mode, const Stage& st, char* ldsK, char* ldsV) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int ch = tid + 256 * u;
-    const int row = ch >> 4;
-    *reinterpret_cast<u32x4*>(ldsK + row * 256 + (((ch & 15) ^ (row & 15)) * 16)) = st.k[u];
+    int row, col16;
+    if (mode == kCopy) {
+      const int p = ch & 511, inst = p >> 6, lane = p & 63;
+      const int r = lane & 15, grp = lane >> 4;
+      row = 32 * (ch >> 9) + 8 * (r >> 2) + (r & 3) + 4 * (inst >> 2);
+      col16 = 4 * grp + (inst & 3);
+    } else {
+      row = ch >> 4;
+      col16 = ch & 15;
+    }
+    *reinterpret_cast<u32x4*>(ldsK + lds_k_offset(row, col16)) = st.k[u];
   }
   if (!STREAMING || mode == kCopy) {
 #pragma unroll
@@ -210,7 +224,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   const int h = kind_head(a, head_idx, &kvh);
   const int64_t cache = int64_t(b) * (STREAMING ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
   const int q_first = qb * kQRows;                        // chunk-relative
   const int q_last = min(q_first + kQRows, a.T) - 1;

@@ -48,6 +48,45 @@ def host_history(w: I.Workload, layer: int, kind: str, L: int) -> np.ndarray:
     return OA.upcast(raw, w.io_dtype)
 
 
+def head_history(w: I.Workload, layer: int, kind: str, g: int, positions) -> np.ndarray:
+    """K or V rows [n, D] (float64) of KV head g at the given positions, as the cache
+    holds them (int4: the oracle codec's dequantised values).  Processed in slices so a
+    3.3M-token head fits in host memory."""
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.empty((len(positions), w.head_dim), dtype=np.float64)
+    step = 1 << 18
+    for a in range(0, len(positions), step):
+        raw = I.synth_head(w.seed, layer, kind, positions[a:a + step], g, w.n_kv_heads, w.head_dim, w.io_dtype)
+        if w.kv_format == "int4":
+            codes, s, z = OQ.quantize(raw)
+            out[a:a + step] = OQ.dequantize(codes, s, z)
+        else:
+            out[a:a + step] = OA.upcast(raw, w.io_dtype)
+    return out
+
+
+def oracle_decode_rows(w: I.Workload, layer: int, t: int, kv_heads, q) -> dict:
+    """Oracle decode output at position t for the query heads of the given KV heads.
+    q: [Hq, D] stored query values (upcast here).  Returns {query head: [D]}."""
+    qf = OA.upcast(q, w.io_dtype)
+    mask = w.mask(layer)
+    out = {}
+    for g in kv_heads:
+        if mask[g]:
+            pos = np.arange(t + 1)
+        else:
+            pos = np.array([j for j in range(min(w.sink, t + 1))] +
+                           [j for j in range(max(w.sink, t - w.recent + 1), t + 1)])
+        K = np.zeros((t + 1, w.head_dim))
+        V = np.zeros((t + 1, w.head_dim))
+        K[pos] = head_history(w, layer, "k", g, pos)
+        V[pos] = head_history(w, layer, "v", g, pos)
+        for i in range(w.group):
+            h = g * w.group + i
+            out[h] = OA.head_attention(qf[h][None], [t], K, V, bool(mask[g]), w.sink, w.recent)[0]
+    return out
+
+
 def q_rows(w: I.Workload, layer: int, rows) -> np.ndarray:
     """Q [len(rows), Hq, D] at arbitrary absolute positions (stored dtype)."""
     rows = np.asarray(rows, dtype=np.uint64)
@@ -56,6 +95,22 @@ def q_rows(w: I.Workload, layer: int, rows) -> np.ndarray:
     x = I.values_f32(w.seed, layer * 4 + I.KIND_STREAM["q"], counters)
     x = I.f32_to_bf16_bits(x) if w.io_dtype == "bf16" else x
     return x.reshape(len(rows), w.n_q_heads, w.head_dim)
+
+
+def fill_stack(w: I.Workload, kv, chunk: int = 65536):
+    """Fill every layer's caches with positions [0, context) via duo_kv_append."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    kbuf = torch.empty((chunk, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    for layer in range(w.n_layers):
+        for c0 in range(0, w.context, chunk):
+            T = min(chunk, w.context - c0)
+            n = T * w.n_kv_heads * w.head_dim
+            B.duo_synth_fill(kbuf, B.DUO_DTYPE_BF16, w.seed, layer * 4 + 1, c0 * w.n_kv_heads * w.head_dim, n)
+            B.duo_synth_fill(vbuf, B.DUO_DTYPE_BF16, w.seed, layer * 4 + 2, c0 * w.n_kv_heads * w.head_dim, n)
+            kv.append(layer, kbuf[:T], vbuf[:T])
+    torch.cuda.synchronize()
 
 
 def to_f64(t) -> np.ndarray:

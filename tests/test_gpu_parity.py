@@ -9,7 +9,8 @@ from mixed_head_kv_amd import inputs as I
 from oracle import attention as OA
 from oracle import int4 as OQ
 
-from parity_util import TOL, compare, device_synth, host_history, oracle_rows, q_rows, run_layer, say, to_f64
+from parity_util import (TOL, compare, device_synth, fill_stack, host_history, oracle_decode_rows, oracle_rows,
+                         q_rows, run_layer, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -239,3 +240,78 @@ def test_llama2_7b_mha_32k_layer(torch_cuda):
     compare("32k decode", to_f64(dec), ref_dec, TOL["bf16"])
     ref_pre = oracle_rows(w, 0, rows, total)
     compare("32k prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
+
+
+def test_llama3_8b_gqa_128k_layer(torch_cuda):
+    """32 query / 8 KV heads (4 retrieval), head_dim 128, bf16, 16 prefill chunks of 8192
+    and 256 decode steps.  Checked: every decode output of the first and last 8 steps
+    (all heads); prefill rows: first and last 16 rows of every chunk, +-4 rows around
+    every chunk boundary and window edge, 24 seeded rows per chunk (all heads)."""
+    w = I.WORKLOADS["llama3_8b_gqa_128k"]
+    say("llama3_8b_gqa_128k")
+    chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    rng = np.random.default_rng(1)
+    rows = set()
+    for c in range(len(chunks)):
+        a, b = c * w.prefill_chunk, (c + 1) * w.prefill_chunk
+        rows |= set(range(a, a + 16)) | set(range(b - 16, b))
+        for e in (a, a + w.recent - 1, a + w.recent):
+            rows |= set(range(max(0, e - 4), min(w.context, e + 4)))
+        rows |= set(rng.integers(a, b, 24).tolist())
+    rows = np.array(sorted(rows))
+    steps = list(range(8)) + list(range(w.decode_steps - 8, w.decode_steps))
+    ref_dec = oracle_rows(w, 0, np.array([w.context + s for s in steps]), total)
+    compare("128k decode (first/last 8 steps)", to_f64(dec[steps]), ref_dec, TOL["bf16"])
+    ref_pre = oracle_rows(w, 0, rows, total)
+    compare("128k prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
+    assert np.isfinite(to_f64(dec)).all() and np.isfinite(to_f64(pre)).all()
+
+
+def _stack_decode_check(torch_cuda, name, steps, check_heads):
+    from mixed_head_kv_amd.binding import DuoKV
+    w = I.WORKLOADS[name].scaled(decode_steps=steps)
+    say(f"{name}: fill {w.n_layers} layers x {w.context} tokens")
+    kv = DuoKV.for_workload(w)
+    fill_stack(w, kv)
+    outs = {}
+    for s in range(steps):
+        t = w.context + s
+        for layer in range(w.n_layers):
+            q = device_synth(w, layer, "q", t, 1)[0]
+            k = device_synth(w, layer, "k", t, 1)[0]
+            v = device_synth(w, layer, "v", t, 1)[0]
+            o = kv.decode(layer, q, k, v)
+            if layer in check_heads and s == steps - 1:
+                outs[layer] = (to_f64(o), q.cpu())
+            elif s == steps - 1:
+                assert torch_cuda.isfinite(o.float()).all()
+    for layer, heads in check_heads.items():
+        got, q = outs[layer]
+        qb = q.view(torch_cuda.int16).numpy().view(np.uint16)
+        say(f"  oracle: layer {layer} KV heads {heads}")
+        ref = oracle_decode_rows(w, layer, w.context + steps - 1, heads, qb)
+        hs = sorted(ref)
+        compare(f"{name} layer {layer} decode", got[hs], np.stack([ref[h] for h in hs]), TOL["bf16"])
+    kv.close()
+
+
+def test_llama3_8b_gqa_32layer_1m_stack(torch_cuda):
+    """32-layer GQA stack, 1,048,576-token bf16 caches filled by kv_append, 2 decode steps
+    through all layers; the last step checked on layer 0 (all 8 KV heads) and layer 31
+    (one retrieval and one streaming KV head), every other layer checked finite."""
+    w = I.WORKLOADS["llama3_8b_gqa_32layer_1m"]
+    m31 = w.mask(31)
+    heads31 = [int(np.nonzero(m31)[0][0]), int(np.nonzero(~m31)[0][0])]
+    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_1m", 2, {0: list(range(8)), 31: heads31})
+
+
+def test_llama3_8b_gqa_32layer_int4_3p3m_stack(torch_cuda):
+    """32-layer GQA stack, 3,300,000-token int4 caches (quantised by kv_append), 2 decode
+    steps through all layers; the last step checked on layer 0 (two retrieval and two
+    streaming KV heads) and layer 31 (one of each); every other layer checked finite."""
+    w = I.WORKLOADS["llama3_8b_gqa_32layer_int4_3p3m"]
+    m0, m31 = w.mask(0), w.mask(31)
+    h0 = [int(x) for x in np.nonzero(m0)[0][:2]] + [int(x) for x in np.nonzero(~m0)[0][:2]]
+    h31 = [int(np.nonzero(m31)[0][0]), int(np.nonzero(~m31)[0][0])]
+    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_int4_3p3m", 2, {0: h0, 31: h31})
