@@ -417,7 +417,101 @@ def cpu_baseline(w, total, budget_s):
             "host_cpus": os.cpu_count()}
 
 
+# --- rocprofv3 output summaries (host only; no GPU) ---------------------------------
+
+PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
+                    "prefill_retrieval_attention": ["k_prefill_mfma<false>"],
+                    "prefill_streaming_attention": ["k_prefill_mfma<true>"]}
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+
+
+def _short(name):
+    name = name.split("(")[0]
+    return name.replace("duo::(anonymous namespace)::", "").replace("void ", "")
+
+
+def summarize_stats(d):
+    """Text table of a `rocprofv3 --kernel-trace --stats` run: calls, mean and total time
+    per kernel, as the profiler reports them."""
+    import csv
+    rows = []
+    for f in _csvs(d, "kernel_stats.csv"):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"{'kernel':<58} {'calls':>7} {'avg_us':>10} {'total_ms':>10} {'pct':>6}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name'])[:58]:<58} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>10.3f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+    return "\n".join(lines)
+
+
+def summarize_traffic(fetch_dir, write_dir, workload):
+    """Per-launch HBM bytes of the path's kernels from two `rocprofv3 --pmc` runs of
+    `bench.py --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled
+    by what the same counter reads for the probe's 1 GiB device copy.  Updates the
+    entries of profiles/traffic.json for this workload and returns a text summary."""
+    import collections
+    import csv
+
+    def load(d, counter):
+        per = collections.defaultdict(float)
+        for f in _csvs(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    per[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+        return per
+
+    out, lines = {}, []
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = load(d, counter)
+        copies = [v for (_, n), v in vals.items() if "copy" in n.lower() or "elementwise" in n.lower()]
+        ref = max(copies)
+        factor = (1 << 30) / 1024.0 / ref
+        lines.append(f"{counter}: the 1 GiB copy reads {ref:.0f} KiB -> scale factor {factor:.4f}")
+        out[counter] = {"factor": factor}
+        for k, pats in PROFILED_KERNELS.items():
+            xs = [v for (_, n), v in vals.items() if any(p in n for p in pats)]
+            if xs:
+                out[counter][k] = (len(xs), sum(xs) / len(xs))
+    try:
+        entries = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        entries = []
+    for k in PROFILED_KERNELS:
+        if k not in out["FETCH_SIZE"] or k not in out["WRITE_SIZE"]:
+            continue
+        n, fk = out["FETCH_SIZE"][k]
+        fb = fk * 1024 * out["FETCH_SIZE"]["factor"]
+        wb = out["WRITE_SIZE"][k][1] * 1024 * out["WRITE_SIZE"]["factor"]
+        entries = [e for e in entries if not (e["kernel"] == k and e["workload"] == workload)]
+        entries.append({"kernel": k, "workload": workload, "source": source_digest(k),
+                        "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                        "bytes_per_launch": round(fb + wb), "launches": n,
+                        "fetch_factor": round(out["FETCH_SIZE"]["factor"], 4),
+                        "write_factor": round(out["WRITE_SIZE"]["factor"], 4)})
+        lines.append(f"{k}: {n} launches, mean per launch: fetch {fb / 1e6:.3f} MB + write {wb / 1e6:.3f} MB "
+                     f"= {(fb + wb) / 1e6:.3f} MB (scaled)")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(sorted(entries, key=lambda e: (e["workload"], e["kernel"])), f, indent=1)
+    return "\n".join(lines)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] in ("--summarize-stats", "--summarize-traffic"):
+        sp = argparse.ArgumentParser()
+        sp.add_argument("dirs", nargs="+")
+        sp.add_argument("--workload", default="llama2_7b_mha_32k")
+        a = sp.parse_args(sys.argv[2:])
+        if sys.argv[1] == "--summarize-stats":
+            print(summarize_stats(a.dirs[0]))
+        else:
+            print(summarize_traffic(a.dirs[0], a.dirs[1], a.workload))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)

@@ -191,14 +191,14 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
   dim3 grid((T + 63) / 64, g.Hq, g.B);
   if (g.io == DUO_DTYPE_F32) {
     if (g.D == 64)
-      hipLaunchKernelGGL((k_prefill_valu<DUO_DTYPE_F32, 64>), grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+      launch(k_prefill_valu<DUO_DTYPE_F32, 64>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
     else
-      hipLaunchKernelGGL((k_prefill_valu<DUO_DTYPE_F32, 128>), grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+      launch(k_prefill_valu<DUO_DTYPE_F32, 128>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
   } else {
     if (g.D == 64)
-      hipLaunchKernelGGL((k_prefill_valu<DUO_DTYPE_BF16, 64>), grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+      launch(k_prefill_valu<DUO_DTYPE_BF16, 64>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
     else
-      hipLaunchKernelGGL((k_prefill_valu<DUO_DTYPE_BF16, 128>), grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+      launch(k_prefill_valu<DUO_DTYPE_BF16, 128>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
   }
   return hipGetLastError();
 }
@@ -209,7 +209,7 @@ hipError_t launch_decode_valu(const Geom& g, const LayerView& lv, const DecodePl
   if (items == 0) return hipSuccess;
   dim3 grid(items);
 #define DUO_DECODE_VALU(IO, KVF, D) \
-  hipLaunchKernelGGL((k_decode_valu<IO, KVF, D>), grid, dim3(256), 0, st, g, lv, p, q, out)
+  launch(k_decode_valu<IO, KVF, D>, grid, dim3(256), 0, st, g, lv, p, q, out)
   if (g.kvfmt == DUO_KV_INT4_G128) {
     DUO_DECODE_VALU(DUO_DTYPE_BF16, DUO_KV_INT4_G128, 128);
   } else if (g.io == DUO_DTYPE_F32) {

@@ -540,10 +540,10 @@ hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePl
   const int items = g.B * (lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s);
   if (items == 0) return hipSuccess;
   if (g.kvfmt == DUO_KV_INT4_G128)
-    hipLaunchKernelGGL(k_decode_mfma_int4, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+    launch(k_decode_mfma_int4, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
                        static_cast<uint16_t*>(out));
   else
-    hipLaunchKernelGGL(k_decode_mfma, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
+    launch(k_decode_mfma, dim3(items), dim3(kThreads), 0, st, g, lv, p, static_cast<const uint16_t*>(q),
                        static_cast<uint16_t*>(out));
   return hipGetLastError();
 }

@@ -162,6 +162,13 @@ struct duo_handle {
   }
 };
 
+namespace duo {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace duo
+
 namespace {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -177,23 +184,31 @@ hipEvent_t take_event(duo_handle* h) {
   return e;
 }
 
-// Brackets one kernel launch with events when the handle is profiling.
+// Times the one kernel launch made inside its scope when the handle is profiling: the
+// launcher stamps the event pair at the dispatch's own begin and end.
 struct KernelMark {
   duo_handle* h;
   int cls;
-  hipStream_t st;
-  hipEvent_t start = nullptr;
-  KernelMark(duo_handle* h_, int cls_, hipStream_t st_) : h(h_), cls(cls_), st(st_) {
-    if (h->profiling && (start = take_event(h)) != nullptr) (void)hipEventRecord(start, st);
+  hipEvent_t start = nullptr, stop = nullptr;
+  KernelMark(duo_handle* h_, int cls_, hipStream_t) : h(h_), cls(cls_) {
+    if (!h->profiling) return;
+    start = take_event(h);
+    stop = start ? take_event(h) : nullptr;
+    if (start && stop) {
+      duo::launch_events() = duo::LaunchEvents{start, stop};
+    } else {
+      if (start) h->event_pool.push_back(start);
+      start = nullptr;
+    }
   }
   ~KernelMark() {
     if (!start) return;
-    hipEvent_t stop = take_event(h);
-    if (stop && hipEventRecord(stop, st) == hipSuccess) {
+    if (duo::launch_events().start == nullptr) {  // the launch took the pair
       h->marks.push_back(duo_handle::Mark{cls, start, stop});
-    } else {
+    } else {                                       // nothing was launched
+      duo::launch_events() = duo::LaunchEvents{};
       h->event_pool.push_back(start);
-      if (stop) h->event_pool.push_back(stop);
+      h->event_pool.push_back(stop);
     }
   }
 };

@@ -2,9 +2,33 @@
 // hipError_t of its launch; arguments are validated by the caller (duo_attn.cpp).
 #pragma once
 
+#include <hip/hip_ext.h>
+
+#include <utility>
+
 #include "duo_common.h"
 
 namespace duo {
+
+// Kernel timing.  When a caller of the library's API profiles, it parks a start/stop
+// event pair here just before the launcher runs; the launcher hands them to
+// hipExtLaunchKernelGGL, which stamps them when the dispatch itself begins and ends
+// (no marker packets of their own, so the timed interval is the kernel's execution and
+// the stream gets no extra commands).  One pair serves one launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();  // per host thread
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args&&... args) {
+  LaunchEvents& ev = launch_events();
+  const LaunchEvents use = ev;  // null events: a plain launch
+  ev = LaunchEvents{};
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, st, use.start, use.stop, 0u, std::forward<Args>(args)...);
+  return hipGetLastError();
+}
 
 // Fused append/evict of T tokens at positions [t0, t0 + T) into every cache of the
 // layer: retrieval heads store every row, streaming heads keep sinks and the last

@@ -349,7 +349,7 @@ hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, cons
   if (g.kvfmt == DUO_KV_INT4_G128) {
     const int tiles = ret_tiles > str_tiles ? ret_tiles : str_tiles;
     dim3 grid((tiles + 3) / 4, ny);
-    hipLaunchKernelGGL(k_append_int4, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
+    launch(k_append_int4, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), T, t0, which, first, ret_tiles, str_tiles);
   } else {
     const int tiles = ret_tiles > str_tiles ? ret_tiles : str_tiles;
@@ -359,17 +359,17 @@ hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, cons
       const int ring_have = ring_lo >= g.S ? static_cast<int>((ring_lo - g.S) % g.R) : 0;
       const int64_t tasks = int64_t(tiles) * (g.D / 8);
       dim3 grid(static_cast<unsigned>((tasks + 255) / 256), ny);
-      hipLaunchKernelGGL(k_append_bf16, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
+      launch(k_append_bf16, grid, dim3(256), 0, st, g, lv, static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), T, t0, which, first, ret_tiles, str_tiles, ring_lo, ring_have);
       return hipGetLastError();
     }
     const int per_block = 256 / g.D;
     dim3 grid((tiles + per_block - 1) / per_block, ny);
     if (g.io == DUO_DTYPE_F32)
-      hipLaunchKernelGGL(k_append<float>, grid, dim3(per_block * g.D), 0, st, g, lv, static_cast<const float*>(k),
+      launch(k_append<float>, grid, dim3(per_block * g.D), 0, st, g, lv, static_cast<const float*>(k),
                          static_cast<const float*>(v), T, t0, which, first, ret_tiles, str_tiles);
     else
-      hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(per_block * g.D), 0, st, g, lv,
+      launch(k_append<uint16_t>, grid, dim3(per_block * g.D), 0, st, g, lv,
                          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), T, t0, which, first,
                          ret_tiles, str_tiles);
   }
@@ -381,13 +381,13 @@ hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool 
   const int64_t total = int64_t(n) * g.D;
   dim3 grid(static_cast<unsigned>((total + 255) / 256));
   if (g.kvfmt == DUO_KV_INT4_G128)
-    hipLaunchKernelGGL((k_read<DUO_DTYPE_BF16, DUO_KV_INT4_G128>), grid, dim3(256), 0, st, g, c, cache,
+    launch(k_read<DUO_DTYPE_BF16, DUO_KV_INT4_G128>, grid, dim3(256), 0, st, g, c, cache,
                        int(streaming), pos0, n, which, out);
   else if (g.io == DUO_DTYPE_F32)
-    hipLaunchKernelGGL((k_read<DUO_DTYPE_F32, DUO_KV_SAME_AS_IO>), grid, dim3(256), 0, st, g, c, cache,
+    launch(k_read<DUO_DTYPE_F32, DUO_KV_SAME_AS_IO>, grid, dim3(256), 0, st, g, c, cache,
                        int(streaming), pos0, n, which, out);
   else
-    hipLaunchKernelGGL((k_read<DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO>), grid, dim3(256), 0, st, g, c, cache,
+    launch(k_read<DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO>, grid, dim3(256), 0, st, g, c, cache,
                        int(streaming), pos0, n, which, out);
   return hipGetLastError();
 }
@@ -395,14 +395,14 @@ hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool 
 hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,
                             int n, int which, uint8_t* codes, uint16_t* meta, hipStream_t st) {
   const int64_t total = int64_t(n) * 64;
-  hipLaunchKernelGGL(k_read_int4, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, g, c, cache,
+  launch(k_read_int4, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, g, c, cache,
                      int(streaming), pos0, n, which, codes, meta);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_i32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
+  launch(k_zero_i32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 
@@ -411,7 +411,7 @@ hipError_t launch_zero_bytes(void* p, uint64_t n_bytes, hipStream_t st) {
   if (n == 0) return hipSuccess;
   uint64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_zero_16b, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n);
+  launch(k_zero_16b, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n);
   return hipGetLastError();
 }
 
@@ -422,10 +422,10 @@ hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, ui
   uint64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (dtype == DUO_DTYPE_F32)
-    hipLaunchKernelGGL(k_synth<DUO_DTYPE_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+    launch(k_synth<DUO_DTYPE_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        static_cast<float*>(out), key, c0, n);
   else
-    hipLaunchKernelGGL(k_synth<DUO_DTYPE_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+    launch(k_synth<DUO_DTYPE_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        static_cast<uint16_t*>(out), key, c0, n);
   return hipGetLastError();
 }

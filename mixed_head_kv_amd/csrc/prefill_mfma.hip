@@ -166,6 +166,32 @@ __device__ inline void stage_load(const PrefillArgs& a, int b, int kvh, int64_t 
 // dims 8*(4*grp + s) of key 32q + 8*(r>>2) + (r&3) + 4t, where p = (t*4 + s)*64 + grp*16 + r.
 __device__ inline int lds_k_offset(int row, int col16) { return row * 256 + ((col16 ^ (row & 15)) * 16); }
 
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Retrieval tiles go HBM -> LDS directly (global_load_lds_dwordx4): each wavefront
+// instruction fills one contiguous KB of LDS, lane L writing bytes 16L .. 16L + 15, so
+// no registers hold the tile in flight.  The K KB `inst` holds rows 4 inst .. 4 inst + 3
+// of the swizzled row-major tile, its lane L the chunk (row 4 inst + L/16, physical
+// chunk L mod 16), gathered from the cache's MFMA-ordered 32-key tiles; V's d-major
+// 8-key blocks are copied as they are.  `wave` is uniform; the caller waits (vmcnt)
+// and synchronises before reading.
+__device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb, char* ldsK, char* ldsV, int wave,
+                                int lane) {
+  const uint16_t* Kc = reinterpret_cast<const uint16_t*>(c.k);
+  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2;
+  const int64_t grow0 = cache * c.rows + kb;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int inst = wave * 4 + u;
+    const int row = inst * 4 + (lane >> 4);
+    const int col16 = (lane & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(Kc + k_chunk_tiled(grow0 + row, col16),
+                                     (lds_void_ptr)(ldsK + inst * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(V + inst * 1024 + lane * 16, (lds_void_ptr)(ldsV + inst * 1024),
+                                     16, 0, 0);
+  }
+}
+
 template <bool STREAMING>
 __device__ inline void stage_store(int mode, const Stage& st, char* ldsK, char* ldsV) {
   const int tid = threadIdx.x;
@@ -293,9 +319,13 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   Stage stage;
   if (ntiles > 0) {
     const int64_t kb = tile_start(0);
-    const int mode = tile_mode(kb);
-    stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
-    stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
+    if constexpr (STREAMING) {
+      const int mode = tile_mode(kb);
+      stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
+      stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
+    } else {
+      tile_dma(a.lv.ret, cache, kb, lds, lds + kKBytes, wave, lane);
+    }
   }
   __syncthreads();
 
@@ -305,10 +335,15 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     const int64_t kb = tile_start(ti);
     const bool more = ti + 1 < ntiles;
     int next_mode = kCopy;
-    if (more) {
+    if (more) {  // the next tile is in flight during the compute
       const int64_t nkb = tile_start(ti + 1);
-      next_mode = tile_mode(nkb);
-      stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);  // in flight during the compute
+      if constexpr (STREAMING) {
+        next_mode = tile_mode(nkb);
+        stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);
+      } else {
+        char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
+        tile_dma(a.lv.ret, cache, nkb, nK, nK + kKBytes, wave, lane);
+      }
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -319,12 +354,24 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       const int pk = 16 * (rho >> 4) + 8 * ((rho >> 2) & 1) + 4 * ((rho >> 3) & 1) + (rho & 3);
       const int krow_i = 32 * sub + pk;
       const char* krow = ldsK + krow_i * 256;
+      // all eight K operands in flight at once, then the eight products
+      u32x4 kop[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        kop[st] = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
+      // V^T operands of this half tile (used after the softmax): rows d = 32 jd + col,
+      // keys 32 sub + 16 u + 8 half .. +7, one 16-byte block row each
+      u32x4 vop[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jd = 0; jd < 4; ++jd)
+          vop[u][jd] = *reinterpret_cast<const u32x4*>(ldsV + ((32 * sub + 16 * u + 8 * half) >> 3) * 2048 +
+                                                      col * 16 + jd * 32 * 16);
+      if constexpr (!STREAMING) __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
       f32x16 s = {};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
-        s = mfma32(kop, qop[st], s);
-      }
+      for (int st = 0; st < 8; ++st) s = mfma32(kop[st], qop[st], s);
       // lane's 16 scores: register 4j + i is key base + 16(j>>1) + 8*half + 4(j&1) + i.
       // Masked keys become -inf; the running max is kept on raw scores (the scale is
       // positive) and the scale is folded into the exponent's FMA.
@@ -363,20 +410,15 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       for (int u = 0; u < 2; ++u) {
         const u32x4 pb = {pack_bf16(s[8 * u + 0], s[8 * u + 1]), pack_bf16(s[8 * u + 2], s[8 * u + 3]),
                           pack_bf16(s[8 * u + 4], s[8 * u + 5]), pack_bf16(s[8 * u + 6], s[8 * u + 7])};
-        // V^T rows d = 32 jd + col, keys 32 sub + 16u + 8 half .. +7: one 16-byte block row
-        const char* vblk = ldsV + ((32 * sub + 16 * u + 8 * half) >> 3) * 2048 + col * 16;
 #pragma unroll
-        for (int jd = 0; jd < 4; ++jd) {
-          const u32x4 vop = *reinterpret_cast<const u32x4*>(vblk + jd * 32 * 16);
-          o[jd] = mfma32(vop, pb, o[jd]);
-        }
+        for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[u][jd], pb, o[jd]);
       }
     }
-    if (more) {
+    if (STREAMING && more) {
       char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
       stage_store<STREAMING>(next_mode, stage, nK, nK + kKBytes);
     }
-    __syncthreads();
+    __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
   }
 
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
@@ -459,9 +501,9 @@ static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const 
   if (blocks == 0) return hipSuccess;
   const unsigned lds = 2 * (kKBytes + kVBytes);
   if (streaming)
-    hipLaunchKernelGGL(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
+    launch(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
   else
-    hipLaunchKernelGGL(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
+    launch(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
