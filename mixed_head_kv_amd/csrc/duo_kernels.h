@@ -21,13 +21,13 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();  // per host thread
 
+// Launch errors are left for the caller's hipGetLastError().
 template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args&&... args) {
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args&&... args) {
   LaunchEvents& ev = launch_events();
   const LaunchEvents use = ev;  // null events: a plain launch
   ev = LaunchEvents{};
   hipExtLaunchKernelGGL(kernel, grid, block, lds, st, use.start, use.stop, 0u, std::forward<Args>(args)...);
-  return hipGetLastError();
 }
 
 // Fused append/evict of T tokens at positions [t0, t0 + T) into every cache of the

@@ -51,6 +51,14 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// acc + lo + hi of a bf16 pair (one v_dot2 against (1, 1); the products are exact).
+__device__ inline float sum_bf16_pair(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
+}
+
+constexpr float kSlack = 8.0f;  // log2 units
+
 struct PrefillArgs {
   Geom g;
   LayerView lv;
@@ -176,19 +184,28 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // 8-key blocks are copied as they are.  `wave` is uniform; the caller waits (vmcnt)
 // and synchronises before reading.
 __device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb, char* ldsK, char* ldsV, int wave,
-                                int lane) {
-  const uint16_t* Kc = reinterpret_cast<const uint16_t*>(c.k);
-  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2;
-  const int64_t grow0 = cache * c.rows + kb;
+                                int lane, const int (&koff)[4]) {
+  // kb and the cache's first row are multiples of 32: the tile's 32-key cache tiles are
+  // whole, and each lane's element offset inside them is loop-invariant (koff)
+  const uint16_t* Kt = reinterpret_cast<const uint16_t*>(c.k) + ((cache * c.rows + kb) >> 5) * 4096;
+  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2 + wave * 4096 + lane * 16;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int inst = wave * 4 + u;
-    const int row = inst * 4 + (lane >> 4);
+    __builtin_amdgcn_global_load_lds(Kt + koff[u], (lds_void_ptr)(ldsK + inst * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(V + u * 1024, (lds_void_ptr)(ldsV + inst * 1024), 16, 0, 0);
+  }
+}
+
+// Element offsets (inside a 64-key tile of the MFMA-ordered K cache) of the chunks lane
+// `lane` of wavefront `wave` moves: LDS row 4 inst + L/16, physical chunk L mod 16 of the
+// swizzled tile, inst = 4 wave + u.
+__device__ inline void tile_dma_offsets(int wave, int lane, int (&koff)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = (wave * 4 + u) * 4 + (lane >> 4);
     const int col16 = (lane & 15) ^ (row & 15);
-    __builtin_amdgcn_global_load_lds(Kc + k_chunk_tiled(grow0 + row, col16),
-                                     (lds_void_ptr)(ldsK + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(V + inst * 1024 + lane * 16, (lds_void_ptr)(ldsV + inst * 1024),
-                                     16, 0, 0);
+    koff[u] = static_cast<int>(k_chunk_tiled(row, col16));
   }
 }
 
@@ -231,6 +248,111 @@ __device__ inline void stage_store(int mode, const Stage& st, char* ldsK, char* 
       *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * 16) = odd;
     }
   }
+}
+
+// K operand of k-step st for the S^T product of a 32-key half tile starting at LDS row
+// `row0`: lane (col, half) supplies key row0 + pi(col) and dims 64 half + 8 st .. +7, where
+// pi(8j + 4h + i) = 16(j>>1) + 8h + 4(j&1) + i is the permuted key order that leaves each
+// lane holding the probabilities of 8 consecutive keys.
+__device__ inline int k_perm(int col) {
+  return 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
+}
+
+// V^T operand (d-block jd, k-step u) of a 32-key half tile at LDS key `key0`: rows
+// d = 32 jd + col, keys key0 + 16 u + 8 half .. +7, one 16-byte row of a d-major block.
+__device__ inline u32x4 v_operand(const char* ldsV, int key0, int u, int jd, int col, int half) {
+  return *reinterpret_cast<const u32x4*>(ldsV + ((key0 + 16 * u + 8 * half) >> 3) * 2048 + col * 16 + jd * 512);
+}
+
+// Pack 16 probabilities (registers 8u .. 8u+7 form the P^T operand of k-step u) and add
+// them to the row sum (the same bf16 values the product uses).
+__device__ inline void pack_probs(const f32x16& p, u32x4 (&pb)[2], float& l) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    pb[u] = u32x4{pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
+                  pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) l = sum_bf16_pair(pb[u][w], l);
+  }
+}
+
+// A 64-key tile whose keys are all visible to every query of the wavefront (no mask).
+// Both 32-key score blocks are formed first (the second block's MFMAs run while the
+// first block's maximum is taken), one running-max update serves the tile, and the
+// exponentials of the second block are issued between the MFMAs of the first block's
+// P*V product, so the vector ALU and the matrix cores work at the same time.
+__device__ __forceinline__ void interior_tile(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
+                                              f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half) {
+  const int pk = k_perm(col);
+  const int sw = pk & 15;  // row swizzle (rows pk and 32 + pk share it)
+  u32x4 kop[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    kop[st] = *reinterpret_cast<const u32x4*>(ldsK + pk * 256 + (((8 * half + st) ^ sw) * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) s0 = mfma32(kop[st], qop[st], s0);
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    kop[st] = *reinterpret_cast<const u32x4*>(ldsK + (32 + pk) * 256 + (((8 * half + st) ^ sw) * 16));
+  u32x4 v0[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) v0[4 * u + jd] = v_operand(ldsV, 0, u, jd, col, half);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < 8; ++st) s1 = mfma32(kop[st], qop[st], s1);
+  float mx = s0[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s0[e]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s1[e]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  if (__ballot(mx > m + kSlack)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] *= alpha;
+    m = mn;
+  }
+  const float mref = m;  // finite: the tile's keys are visible
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -mref));
+  u32x4 pb0[2], pb1[2];
+  pack_probs(s0, pb0, l);
+  __builtin_amdgcn_sched_barrier(0);
+  // P*V of the first block, with the second block's exponentials in between
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 * u + jd], pb0[u], o[jd]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -mref));
+  pack_probs(s1, pb1, l);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) v0[4 * u + jd] = v_operand(ldsV, 32, u, jd, col, half);  // after its MFMA
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 * u + jd], pb1[u], o[jd]);
 }
 
 template <bool STREAMING>
@@ -317,6 +439,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   const float sl2 = g.scale_log2;
 
   Stage stage;
+  int koff[4];
+  if constexpr (!STREAMING) tile_dma_offsets(wave, lane, koff);
   if (ntiles > 0) {
     const int64_t kb = tile_start(0);
     if constexpr (STREAMING) {
@@ -324,7 +448,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
       stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
     } else {
-      tile_dma(a.lv.ret, cache, kb, lds, lds + kKBytes, wave, lane);
+      tile_dma(a.lv.ret, cache, kb, lds, lds + kKBytes, wave, lane, koff);
     }
   }
   __syncthreads();
@@ -342,9 +466,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
         stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);
       } else {
         char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-        tile_dma(a.lv.ret, cache, nkb, nK, nK + kKBytes, wave, lane);
+        tile_dma(a.lv.ret, cache, nkb, nK, nK + kKBytes, wave, lane, koff);
       }
     }
+    if (!STREAMING && kb + kTileKeys - 1 <= wave_q_lo) {
+      interior_tile(ldsK, ldsV, qop, o, m, l, sl2, col, half);
+    } else {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int64_t base = kb + 32 * sub;
@@ -391,28 +518,32 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      const float mn = fmaxf(m, mx);
-      const float mref = mn == kNegInf ? 0.0f : mn;
-      if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      // The reference max m may lag the true running max by up to kSlack (log2 units):
+      // weights are then at most 2^kSlack, harmless in fp32 and bf16, and the rescale
+      // (which touches all of O) runs only when some lane's max outgrows m + kSlack.
+      if (__ballot(mx > m + kSlack)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
         l *= alpha;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] *= alpha;
+        m = mn;
       }
-      m = mn;
+      const float mref = m == kNegInf ? 0.0f : m;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
-        l += s[e];
-      }
-      // P^T operand for k-step u: keys base + 16u + 8*half + 0..7 = registers 8u .. 8u+7
+      for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
+      // P^T operand for k-step u: keys base + 16u + 8*half + 0..7 = registers 8u .. 8u+7;
+      // the row sum adds the same bf16 weights the product uses (v_dot2 with ones)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const u32x4 pb = {pack_bf16(s[8 * u + 0], s[8 * u + 1]), pack_bf16(s[8 * u + 2], s[8 * u + 3]),
                           pack_bf16(s[8 * u + 4], s[8 * u + 5]), pack_bf16(s[8 * u + 6], s[8 * u + 7])};
 #pragma unroll
         for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[u][jd], pb, o[jd]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) l = sum_bf16_pair(pb[w], l);
       }
+    }
     }
     if (STREAMING && more) {
       char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
