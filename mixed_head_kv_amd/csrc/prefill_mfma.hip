@@ -276,13 +276,38 @@ __device__ inline void pack_probs(const f32x16& p, u32x4 (&pb)[2], float& l) {
   }
 }
 
-// A 64-key tile whose keys are all visible to every query of the wavefront (no mask).
-// Both 32-key score blocks are formed first (the second block's MFMAs run while the
-// first block's maximum is taken), one running-max update serves the tile, and the
-// exponentials of the second block are issued between the MFMAs of the first block's
-// P*V product, so the vector ALU and the matrix cores work at the same time.
-__device__ __forceinline__ void interior_tile(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
-                                              f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half) {
+// Scores of keys a query may not see become -inf, in place: register 4j + i of a
+// 32-key block starting at `base` is key base + 16(j>>1) + 8 half + 4(j&1) + i.  A key
+// is visible to query position i_pos when it is not after it and (streaming heads) it is
+// a sink (< S) or inside the recent window (i_pos - key < R).
+template <bool STREAMING>
+__device__ inline void mask_block(f32x16& s, int64_t base, int64_t i_pos, int half, int S, int R) {
+  const int rel0 = static_cast<int>(base - i_pos);  // key - query position for register 0
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int off = 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
+      const int rel = rel0 + off;
+      bool vis = rel <= 0;
+      if (STREAMING) vis = vis && (-rel < R || static_cast<int>(base - S) + off < 0);
+      s[4 * j + i] = vis ? s[4 * j + i] : kNegInf;
+    }
+}
+
+// One 64-key tile for the wavefront's 32 queries.  Both 32-key score blocks are formed
+// first (the second block's MFMAs run while the first block's maximum is taken), the
+// scores outside the mask are set to -inf in place when the tile needs it (a uniform
+// branch that touches only the score registers, so O stays in one register set), one
+// running-max update serves the tile, and the exponentials of the second block are
+// issued between the MFMAs of the first block's P*V, so the vector ALU and the matrix
+// cores work at the same time.  The running max m may lag the true one by up to kSlack
+// (log2 units): weights are then at most 2^kSlack, harmless in fp32 and bf16, and the
+// rescale (which touches all of O) runs only when some lane's max outgrows m + kSlack.
+template <bool STREAMING>
+__device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
+                                             f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half,
+                                             bool masked, int64_t kb, int64_t i_pos, int S, int R) {
   const int pk = k_perm(col);
   const int sw = pk & 15;  // row swizzle (rows pk and 32 + pk share it)
   u32x4 kop[8];
@@ -304,15 +329,13 @@ __device__ __forceinline__ void interior_tile(const char* ldsK, const char* ldsV
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < 8; ++st) s1 = mfma32(kop[st], qop[st], s1);
+  if (masked) {
+    mask_block<STREAMING>(s0, kb, i_pos, half, S, R);
+    mask_block<STREAMING>(s1, kb + 32, i_pos, half, S, R);
+  }
   float mx = s0[0];
 #pragma unroll
   for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s0[e]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s1[e]);
   mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
@@ -324,7 +347,7 @@ __device__ __forceinline__ void interior_tile(const char* ldsK, const char* ldsV
     for (int j = 0; j < 4; ++j) o[j] *= alpha;
     m = mn;
   }
-  const float mref = m;  // finite: the tile's keys are visible
+  const float mref = m == kNegInf ? 0.0f : m;  // -inf only while every key so far is masked
 #pragma unroll
   for (int e = 0; e < 16; ++e) s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -mref));
   u32x4 pb0[2], pb1[2];
@@ -469,81 +492,56 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
         tile_dma(a.lv.ret, cache, nkb, nK, nK + kKBytes, wave, lane, koff);
       }
     }
-    if (!STREAMING && kb + kTileKeys - 1 <= wave_q_lo) {
-      interior_tile(ldsK, ldsV, qop, o, m, l, sl2, col, half);
+    if constexpr (!STREAMING) {
+      if (kb <= wave_q_hi) {  // (a tile wholly after the wavefront's queries is skipped)
+        const bool inside = kb + kTileKeys - 1 <= wave_q_lo;  // every key visible to every query
+        tile_compute<false>(ldsK, ldsV, qop, o, m, l, sl2, col, half, !inside, kb, i_pos, g.S, g.R);
+      }
     } else {
+      // Streaming heads hold their next tile in registers during the compute, so they take
+      // the half tiles one at a time (fewer live registers).
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int64_t base = kb + 32 * sub;
-      if (base > wave_q_hi) continue;  // every key of this half tile is after the wave's queries
-      // S^T: row rho of the K operand is key base + pi(rho), pi(8j + 4h + i) = 16(j>>1) + 8h + 4(j&1) + i
-      const int rho = col;
-      const int pk = 16 * (rho >> 4) + 8 * ((rho >> 2) & 1) + 4 * ((rho >> 3) & 1) + (rho & 3);
-      const int krow_i = 32 * sub + pk;
-      const char* krow = ldsK + krow_i * 256;
-      // all eight K operands in flight at once, then the eight products
-      u32x4 kop[8];
+      for (int sub = 0; sub < 2; ++sub) {
+        const int64_t base = kb + 32 * sub;
+        if (base > wave_q_hi) continue;  // every key of this half tile is after the wave's queries
+        const int pk = k_perm(col);
+        const int krow_i = 32 * sub + pk;
+        const char* krow = ldsK + krow_i * 256;
+        u32x4 kop[8];
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-        kop[st] = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
-      // V^T operands of this half tile (used after the softmax): rows d = 32 jd + col,
-      // keys 32 sub + 16 u + 8 half .. +7, one 16-byte block row each
-      u32x4 vop[2][4];
+        for (int st = 0; st < 8; ++st)
+          kop[st] = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
+        u32x4 vop[8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int jd = 0; jd < 4; ++jd)
-          vop[u][jd] = *reinterpret_cast<const u32x4*>(ldsV + ((32 * sub + 16 * u + 8 * half) >> 3) * 2048 +
-                                                      col * 16 + jd * 32 * 16);
-      if constexpr (!STREAMING) __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-      f32x16 s = {};
+          for (int jd = 0; jd < 4; ++jd) vop[4 * u + jd] = v_operand(ldsV, 32 * sub, u, jd, col, half);
+        f32x16 s = {};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) s = mfma32(kop[st], qop[st], s);
-      // lane's 16 scores: register 4j + i is key base + 16(j>>1) + 8*half + 4(j&1) + i.
-      // Masked keys become -inf; the running max is kept on raw scores (the scale is
-      // positive) and the scale is folded into the exponent's FMA.
-      if (STREAMING || base + 31 > wave_q_lo) {
-        const int rel0 = static_cast<int>(base - i_pos);  // key - query position for register 0
+        for (int st = 0; st < 8; ++st) s = mfma32(kop[st], qop[st], s);
+        mask_block<true>(s, base, i_pos, half, g.S, g.R);
+        float mx = s[0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        if (__ballot(mx > m + kSlack)) {
+          const float mn = fmaxf(m, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
+          l *= alpha;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rel = rel0 + 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
-            bool vis = rel <= 0;
-            if (STREAMING) vis = vis && (-rel < g.R || static_cast<int>(base - g.S) + (rel - rel0) < 0);
-            s[4 * j + i] = vis ? s[4 * j + i] : kNegInf;
-          }
+          for (int j = 0; j < 4; ++j) o[j] *= alpha;
+          m = mn;
+        }
+        const float mref = m == kNegInf ? 0.0f : m;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
+        u32x4 pb[2];
+        pack_probs(s, pb, l);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[4 * u + jd], pb[u], o[jd]);
       }
-      float mx = s[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      // The reference max m may lag the true running max by up to kSlack (log2 units):
-      // weights are then at most 2^kSlack, harmless in fp32 and bf16, and the rescale
-      // (which touches all of O) runs only when some lane's max outgrows m + kSlack.
-      if (__ballot(mx > m + kSlack)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
-        l *= alpha;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= alpha;
-        m = mn;
-      }
-      const float mref = m == kNegInf ? 0.0f : m;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
-      // P^T operand for k-step u: keys base + 16u + 8*half + 0..7 = registers 8u .. 8u+7;
-      // the row sum adds the same bf16 weights the product uses (v_dot2 with ones)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pb = {pack_bf16(s[8 * u + 0], s[8 * u + 1]), pack_bf16(s[8 * u + 2], s[8 * u + 3]),
-                          pack_bf16(s[8 * u + 4], s[8 * u + 5]), pack_bf16(s[8 * u + 6], s[8 * u + 7])};
-#pragma unroll
-        for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[u][jd], pb, o[jd]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) l = sum_bf16_pair(pb[w], l);
-      }
-    }
     }
     if (STREAMING && more) {
       char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
