@@ -59,6 +59,26 @@ __device__ inline float sum_bf16_pair(uint32_t pair, float acc) {
 
 constexpr float kSlack = 8.0f;  // log2 units
 
+// max(x of this lane, x of lane ^ 32): one v_permlane32_swap instead of an LDS permute.
+__device__ inline float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Largest of 32 scores as a shallow tree of v_max3 (independent partial maxima).
+__device__ inline float max32(const f32x16& a, const f32x16& b) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+  t[5] = fmaxf(fmaxf(a[15], b[0]), b[1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[6 + i] = fmaxf(fmaxf(b[2 + 3 * i], b[3 + 3 * i]), b[4 + 3 * i]);
+  t[10] = b[14];
+  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(fmaxf(t[9], t[10]), b[15]);
+  return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+}
+
 struct PrefillArgs {
   Geom g;
   LayerView lv;
@@ -333,12 +353,7 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
     mask_block<STREAMING>(s0, kb, i_pos, half, S, R);
     mask_block<STREAMING>(s1, kb + 32, i_pos, half, S, R);
   }
-  float mx = s0[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s0[e]);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s1[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  const float mx = max_across_halves(max32(s0, s1)) * sl2;
   if (__ballot(mx > m + kSlack)) {
     const float mn = fmaxf(m, mx);
     const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
@@ -348,34 +363,54 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
     m = mn;
   }
   const float mref = m == kNegInf ? 0.0f : m;  // -inf only while every key so far is masked
+  // Four quarter steps (8 keys of each lane per step): the exponentials and packing of a
+  // step are issued while the MFMAs of the previous step run.
+  u32x4 pb[4];
+  auto probs = [&](const f32x16& sc, int h, u32x4& out) {
+    float p[8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -mref));
-  u32x4 pb0[2], pb1[2];
-  pack_probs(s0, pb0, l);
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[8 * h + e], sl2, -mref));
+    out = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) l = sum_bf16_pair(out[w], l);
+  };
+  probs(s0, 0, pb[0]);
   __builtin_amdgcn_sched_barrier(0);
-  // P*V of the first block, with the second block's exponentials in between
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[jd], pb[0], o[jd]);
+  probs(s0, 1, pb[1]);
 #pragma unroll
-    for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 * u + jd], pb0[u], o[jd]);
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -mref));
-  pack_probs(s1, pb1, l);
+  for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 + jd], pb[1], o[jd]);
+  probs(s1, 0, pb[2]);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int jd = 0; jd < 4; ++jd) v0[jd] = v_operand(ldsV, 32, 0, jd, col, half);  // after its MFMA
 #pragma unroll
-    for (int jd = 0; jd < 4; ++jd) v0[4 * u + jd] = v_operand(ldsV, 32, u, jd, col, half);  // after its MFMA
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[jd], pb[2], o[jd]);
+  probs(s1, 1, pb[3]);
 #pragma unroll
-    for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 * u + jd], pb1[u], o[jd]);
+  for (int jd = 0; jd < 4; ++jd) v0[4 + jd] = v_operand(ldsV, 32, 1, jd, col, half);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 + jd], pb[3], o[jd]);
 }
 
 template <bool STREAMING>
@@ -461,18 +496,48 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   };
   const float sl2 = g.scale_log2;
 
+  if constexpr (!STREAMING) {
+    // Retrieval: tiles [t_begin, t_begin + ntiles) of the cache.  The leading tiles hold
+    // only keys before the block's first query (visible to every query): they run in a
+    // loop with the mask compiled out; the few tiles on the diagonal follow.
+    int koff[4];
+    tile_dma_offsets(wave, lane, koff);
+    const int64_t kb_first = t_begin * kTileKeys;
+    const int64_t first_q = a.t0 + q_first;
+    int64_t n_inner = first_q >= kb_first + kTileKeys - 1 ? (first_q - (kb_first + kTileKeys - 1)) / kTileKeys + 1 : 0;
+    if (n_inner > ntiles) n_inner = ntiles;
+    if (ntiles > 0) tile_dma(a.lv.ret, cache, kb_first, lds, lds + kKBytes, wave, lane, koff);
+    __syncthreads();
+    auto prefetch = [&](int64_t ti) {  // the next tile is in flight during the compute
+      if (ti + 1 < ntiles) {
+        char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
+        tile_dma(a.lv.ret, cache, kb_first + (ti + 1) * kTileKeys, nK, nK + kKBytes, wave, lane, koff);
+      }
+    };
+    int64_t ti = 0;
+    for (; ti < n_inner; ++ti) {
+      const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
+      prefetch(ti);
+      tile_compute<false>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, 0, 0, 0, 0);
+      __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
+    }
+    for (; ti < ntiles; ++ti) {
+      const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
+      const int64_t kb = kb_first + ti * kTileKeys;
+      prefetch(ti);
+      if (kb <= wave_q_hi) {  // (a tile wholly after the wavefront's queries is skipped)
+        const bool inside = kb + kTileKeys - 1 <= wave_q_lo;  // every key visible to every query
+        tile_compute<false>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !inside, kb, i_pos, g.S, g.R);
+      }
+      __syncthreads();
+    }
+  } else {
   Stage stage;
-  int koff[4];
-  if constexpr (!STREAMING) tile_dma_offsets(wave, lane, koff);
   if (ntiles > 0) {
     const int64_t kb = tile_start(0);
-    if constexpr (STREAMING) {
-      const int mode = tile_mode(kb);
-      stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
-      stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
-    } else {
-      tile_dma(a.lv.ret, cache, kb, lds, lds + kKBytes, wave, lane, koff);
-    }
+    const int mode = tile_mode(kb);
+    stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
+    stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
   }
   __syncthreads();
 
@@ -484,20 +549,9 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     int next_mode = kCopy;
     if (more) {  // the next tile is in flight during the compute
       const int64_t nkb = tile_start(ti + 1);
-      if constexpr (STREAMING) {
-        next_mode = tile_mode(nkb);
-        stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);
-      } else {
-        char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-        tile_dma(a.lv.ret, cache, nkb, nK, nK + kKBytes, wave, lane, koff);
-      }
+      next_mode = tile_mode(nkb);
+      stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);
     }
-    if constexpr (!STREAMING) {
-      if (kb <= wave_q_hi) {  // (a tile wholly after the wavefront's queries is skipped)
-        const bool inside = kb + kTileKeys - 1 <= wave_q_lo;  // every key visible to every query
-        tile_compute<false>(ldsK, ldsV, qop, o, m, l, sl2, col, half, !inside, kb, i_pos, g.S, g.R);
-      }
-    } else {
       // Streaming heads hold their next tile in registers during the compute, so they take
       // the half tiles one at a time (fewer live registers).
 #pragma unroll
@@ -542,12 +596,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 #pragma unroll
           for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[4 * u + jd], pb[u], o[jd]);
       }
-    }
-    if (STREAMING && more) {
+    if (more) {
       char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
       stage_store<STREAMING>(next_mode, stage, nK, nK + kKBytes);
     }
-    __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
+    __syncthreads();
+  }
   }
 
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
