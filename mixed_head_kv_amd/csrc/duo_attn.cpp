@@ -234,12 +234,21 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   p.v_new = nullptr;
   p.new_slot = duo::stream_slot(t, h->cfg.sink, h->cfg.recent);
   const int64_t nkeys = t + 1;
-  const int64_t heads = int64_t(h->cfg.batch) * h->views[layer].n_ret;
-  // Retrieval heads: about one workgroup per CU over all of them, at least 512 keys
-  // per split (a multiple of 64), within the partial buffer.
+  const int64_t batch = h->cfg.batch;
+  // Streaming heads: one split each (no merge) unless the window is long.
+  const int64_t nslots = nkeys < h->cfg.sink + h->cfg.recent ? nkeys : int64_t(h->cfg.sink) + h->cfg.recent;
+  p.chunk_s = int(align_up(uint64_t(nslots < 2048 ? nslots : 2048), 64));
+  p.nsplit_s = int((nslots + p.chunk_s - 1) / p.chunk_s);
+  // Retrieval heads: the decode workgroup fills a CU, so the splits share what the
+  // streaming workgroups leave of one workgroup per CU (at least 512 keys per split, a
+  // multiple of 64, within the partial buffer).
+  const int64_t heads = batch * h->views[layer].n_ret;
+  const int64_t str_wgs = batch * h->views[layer].n_str * p.nsplit_s;
   int64_t chunk = 512;
   if (heads > 0) {
-    const int64_t per_head = (h->num_cu + heads - 1) / heads;
+    int64_t slots = h->num_cu - str_wgs;
+    if (slots < heads) slots = heads;
+    const int64_t per_head = slots / heads;
     const int64_t want = (nkeys + per_head - 1) / per_head;
     if (want > chunk) chunk = want;
   }
@@ -250,9 +259,6 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   chunk = int64_t(align_up(uint64_t(chunk), 64));
   p.chunk_r = int(chunk);
   p.nsplit_r = int((nkeys + chunk - 1) / chunk);
-  const int64_t nslots = nkeys < h->cfg.sink + h->cfg.recent ? nkeys : int64_t(h->cfg.sink) + h->cfg.recent;
-  p.chunk_s = 128;
-  p.nsplit_s = int((nslots + p.chunk_s - 1) / p.chunk_s);
   return p;
 }
 
