@@ -99,6 +99,17 @@ struct PrefillArgs {
 // Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
 constexpr int kSlotFloats = kQRows * 128 + 2 * kQRows;
 
+// Split partials move with buffer instructions carrying the sc1 cache-policy bit
+// (device-coherent: written through / read past the XCD-local L2), so a partial written
+// on one XCD is read correctly on another.  0x00020000 is the gfx9 buffer-descriptor
+// word 3 for raw (untyped) dword access; num_records bounds every access to the slot.
+constexpr int kCoherent = 16;  // sc1
+__device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(float* slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(slot, 0, kSlotFloats * 4, 0x00020000);
+}
+// Byte offset of float4 chunk `c` (dims 4c .. 4c + 3) of query `ql` in a partial.
+__device__ inline int o_chunk_offset(int c, int ql) { return (c * kQRows + ql) * 16; }
+
 // Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
 // this kind, in KV-head-major order.
 __device__ inline int kind_head(const PrefillArgs& a, int idx, int* kvh) {
@@ -607,25 +618,34 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
   l += __shfl_xor(l, 32);
   if (a.nsplit > 1) {
-    // Every split publishes its partial; the last one to arrive merges them all.
+    // Every split publishes its partial; the last one to arrive merges them all.  A
+    // partial is O as float4 chunks [32 dim chunks][128 queries] (a wavefront's lanes
+    // cover 512 contiguous bytes per store), then m[128] and l[128], all moved with
+    // 16-byte device-coherent buffer accesses.
     const int pair = (b * a.n_heads + head_idx) * a.n_qblocks + qb;
     const int ql = 32 * wave + col;
     float* mine = a.scratch + (int64_t(pair) * a.nsplit + split) * kSlotFloats;
+    {
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(mine);
 #pragma unroll
-    for (int jd = 0; jd < 4; ++jd)
+      for (int jd = 0; jd < 4; ++jd)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_coherent(mine + ql * 128 + 32 * jd + 8 * j + 4 * half + i, o[jd][4 * j + i]);
-    if (half == 0) {
-      store_coherent(mine + kQRows * 128 + ql, m);
-      store_coherent(mine + kQRows * 128 + kQRows + ql, l);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = {__float_as_uint(o[jd][4 * j + 0]), __float_as_uint(o[jd][4 * j + 1]),
+                           __float_as_uint(o[jd][4 * j + 2]), __float_as_uint(o[jd][4 * j + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o_chunk_offset(8 * jd + 2 * j + half, ql), 0, kCoherent);
+        }
+      if (half == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, (kQRows * 128 + ql) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, (kQRows * 128 + kQRows + ql) * 4, 0, kCoherent);
+      }
     }
     if (!last_arrival(a.counters + pair, a.nsplit)) return;
     float M = m;
     for (int s2 = 0; s2 < a.nsplit; ++s2) {
       if (s2 == split) continue;
-      M = fmaxf(M, load_coherent(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats + kQRows * 128 + ql));
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats);
+      M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)));
     }
     const float w0 = __builtin_amdgcn_exp2f(m - M);  // an empty split has m = -inf: weight 0
     l *= w0;
@@ -633,16 +653,19 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     for (int jd = 0; jd < 4; ++jd) o[jd] *= w0;
     for (int s2 = 0; s2 < a.nsplit; ++s2) {
       if (s2 == split) continue;
-      const float* other = a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats;
-      const float w = __builtin_amdgcn_exp2f(load_coherent(other + kQRows * 128 + ql) - M);
-      l = fmaf(w, load_coherent(other + kQRows * 128 + kQRows + ql), l);
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats);
+      const float w = __builtin_amdgcn_exp2f(
+          __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)) - M);
+      l = fmaf(w, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + kQRows + ql) * 4, 0,
+                                                                         kCoherent)), l);
 #pragma unroll
       for (int jd = 0; jd < 4; ++jd)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o_chunk_offset(8 * jd + 2 * j + half, ql), 0, kCoherent);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            o[jd][4 * j + i] = fmaf(w, load_coherent(other + ql * 128 + 32 * jd + 8 * j + 4 * half + i), o[jd][4 * j + i]);
+          for (int i = 0; i < 4; ++i) o[jd][4 * j + i] = fmaf(w, __uint_as_float(v[i]), o[jd][4 * j + i]);
+        }
     }
   }
   if (q_valid) {
