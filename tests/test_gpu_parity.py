@@ -315,3 +315,49 @@ def test_llama3_8b_gqa_32layer_int4_3p3m_stack(torch_cuda):
     h0 = [int(x) for x in np.nonzero(m0)[0][:2]] + [int(x) for x in np.nonzero(~m0)[0][:2]]
     h31 = [int(np.nonzero(m31)[0][0]), int(np.nonzero(~m31)[0][0])]
     _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_int4_3p3m", 2, {0: h0, 31: h31})
+
+
+def _ramped_inputs(w, total, growth):
+    """Seeded Q, K, V with every key scaled by 1 + growth * t / total (bf16-rounded on the
+    host): scores grow along the sequence, so the running maximum keeps rising."""
+    ramp = (1.0 + growth * np.arange(total) / total)[:, None, None].astype(np.float32)
+    qf = I.values_f32(w.seed, 0, np.arange(total * w.n_q_heads * w.head_dim, dtype=np.uint64))
+    kf = I.values_f32(w.seed, 1, np.arange(total * w.n_kv_heads * w.head_dim, dtype=np.uint64))
+    vf = I.values_f32(w.seed, 2, np.arange(total * w.n_kv_heads * w.head_dim, dtype=np.uint64))
+    q = I.f32_to_bf16_bits(qf.reshape(total, w.n_q_heads, w.head_dim))
+    k = I.f32_to_bf16_bits(kf.reshape(total, w.n_kv_heads, w.head_dim) * ramp)
+    v = I.f32_to_bf16_bits(vf.reshape(total, w.n_kv_heads, w.head_dim))
+    return q, k, v
+
+
+@pytest.mark.parametrize("split", [None, "2"])
+def test_growing_scores_exercise_the_rescale(torch_cuda, monkeypatch, split):
+    """Keys grow 5x in magnitude along the sequence, so the running max outgrows the
+    reference by more than the lazy-rescale slack many times (prefill, split-key prefill
+    and decode); results must still match the oracle."""
+    import torch
+    from mixed_head_kv_amd.binding import DuoKV
+    if split:
+        monkeypatch.setenv("DUO_PREFILL_SPLIT", split)
+    w = W("ramp_gqa", 31, 16, 4, 128, "bf16", 4, 64, 1536, 6, 2)
+    chunks = [512, 1024]
+    total = sum(chunks) + w.decode_steps
+    say(f"growing scores split={split}")
+    q, k, v = _ramped_inputs(w, total, 4.0)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    Q, K, V = dev(q), dev(k), dev(v)
+    kv = DuoKV.for_workload(w)
+    pre, t = [], 0
+    for T in chunks:
+        pre.append(kv.prefill(0, Q[t:t + T], K[t:t + T], V[t:t + T]))
+        t += T
+    dec = []
+    for _ in range(w.decode_steps):
+        dec.append(kv.decode(0, Q[t], K[t], V[t]))
+        t += 1
+    torch.cuda.synchronize()
+    up = lambda a: OA.upcast(a, "bf16")
+    ref = OA.layer_attention(up(q), np.arange(total), up(k), up(v), w.mask(0), w.sink, w.recent)
+    L = sum(chunks)
+    compare("ramp prefill", to_f64(torch.cat(pre, 0)), ref[:L], TOL["bf16"])
+    compare("ramp decode", to_f64(torch.stack(dec, 0)), ref[L:], TOL["bf16"])
