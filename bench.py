@@ -430,8 +430,8 @@ def _csvs(d, suffix):
 
 
 def _short(name):
-    name = name.split("(")[0]
-    return name.replace("duo::(anonymous namespace)::", "").replace("void ", "")
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
 
 
 def summarize_stats(d):
