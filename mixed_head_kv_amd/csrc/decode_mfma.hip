@@ -48,44 +48,34 @@ struct Tile {
   u32x4 v[8];          // V^T operand for the 8 d-blocks
 };
 
-// Loads the 32-key tile starting at cache row `base`.  Lane l (row r = l % 16, group
-// g = l / 16) reads key base + 8*(r/4) + (r%4) (tile 0) and that + 4 (tile 1), dims
-// 32g .. 32g+31, and the V^T rows d = 16j + r of the 8-key block base + 8g.  The K
-// row `new_row` (the token being appended in this step, or -1) is read from k_new
-// instead of the cache; its V element is patched in by patch_v at the point of use,
-// so nothing here waits on the loads it issues.
-__device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                 int64_t cache_row0, int64_t base, int r, int grp, int64_t new_row,
-                                 const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
-  // K: the tile's 16-byte chunks are stored in operand order, one contiguous KB per
-  // load instruction (chunk (t*4 + s)*64 + lane)
+// Buffer descriptor word 3 for raw (untyped) dword access on gfx9, and the
+// non-temporal (streaming) cache policy for the tile loads.
+constexpr int kRawBuffer = 0x00020000;
+constexpr int kStreaming = 2;  // nt
+
+// The split's K and V as bounds-checked buffers: a load past the split's last 32-key
+// tile returns zeros without touching memory, so the ring can prefetch unconditionally
+// (the compiler then counts every load) at no traffic cost.
+struct SplitBuffers {
+  __amdgpu_buffer_rsrc_t k, v;
+};
+
+// Loads the 32-key tile starting at key `base` (offset `rel` = base - key0 inside the
+// split).  Lane l (row r = l % 16, group g = l / 16) holds key base + 8*(r/4) + (r%4)
+// (tile 0) and that + 4 (tile 1), dims 32g .. 32g+31, and the V^T rows d = 16j + r of
+// the 8-key block base + 8g.  K tiles are stored in operand order: chunk
+// (t*4 + s)*64 + lane is one contiguous KB per load instruction.
+__device__ inline void load_tile(Tile& t, const SplitBuffers& sb, int rel, int r, int grp) {
   const int lane = grp * 16 + r;
-  const int64_t key0 = base + 8 * (r >> 2) + (r & 3);
-  const u32x4* kt = reinterpret_cast<const u32x4*>(K + ((cache_row0 + base) >> 5) * 4096) + lane;
-  const u32x4* kn = reinterpret_cast<const u32x4*>(k_new + 32 * grp);
-  const bool n0 = key0 == new_row, n1 = key0 + 4 == new_row;
+  const int kofs = (rel >> 5) * 8192 + lane * 16;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    t.k0[s] = __builtin_nontemporal_load(n0 ? kn + s : kt + s * 64);
-    t.k1[s] = __builtin_nontemporal_load(n1 ? kn + s : kt + (4 + s) * 64);
+    t.k0[s] = __builtin_amdgcn_raw_buffer_load_b128(sb.k, kofs + s * 1024, 0, kStreaming);
+    t.k1[s] = __builtin_amdgcn_raw_buffer_load_b128(sb.k, kofs + (4 + s) * 1024, 0, kStreaming);
   }
-  const int64_t b8 = base + 8 * grp;
-  const u32x4* vb = reinterpret_cast<const u32x4*>(V + (cache_row0 + b8) * 128) + r;
+  const int vofs = (rel + 8 * grp) * 256 + r * 16;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) t.v[j] = __builtin_nontemporal_load(vb + 16 * j);
-}
-
-// Replace the V element of row `new_row` (inside this lane's 8-key block) by the new
-// token's values vn[j] = v_new[16j + r], preloaded before the loop.
-__device__ inline void patch_v(Tile& t, int64_t base, int grp, int64_t new_row, const uint32_t* vn) {
-  const int64_t e = new_row - (base + 8 * grp);
-  if (e < 0 || e >= 8) return;
-  const int w = static_cast<int>(e >> 1);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t word = t.v[j][w];
-    t.v[j][w] = (e & 1) ? ((word & 0xffffu) | (vn[j] << 16)) : ((word & 0xffff0000u) | vn[j]);
-  }
+  for (int j = 0; j < 8; ++j) t.v[j] = __builtin_amdgcn_raw_buffer_load_b128(sb.v, vofs + j * 256, 0, kStreaming);
 }
 
 // Merge of the split partials of one KV head (run by the last workgroup to finish).
@@ -179,14 +169,20 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
   const uint16_t* k_new = p.k_new ? p.k_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
   const uint16_t* v_new = p.v_new ? p.v_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
-  if (new_row >= it.key0 && new_row < it.key1 && threadIdx.x < 128) {
-    // no workgroup reads this row from the cache in this launch: the one that covers it
-    // takes it from the inputs, so the cache write can go out at once
-    uint16_t* Kw = reinterpret_cast<uint16_t*>(c.k);
-    uint16_t* Vw = reinterpret_cast<uint16_t*>(c.v);
-    const int d = threadIdx.x;
-    Kw[k_chunk_tiled(row0 + new_row, d >> 3) + (d & 7)] = k_new[d];
-    Vw[v_index(it.cache, c.rows, new_row, 128, d)] = v_new[d];
+  const bool has_new = new_row >= it.key0 && new_row < it.key1;  // uniform
+  if (has_new) {
+    // The workgroup whose range holds the new row writes it to the cache first and
+    // waits for the stores to land in its XCD's L2 before any of its wavefronts load
+    // the tile: those loads then see the new token like any other row.
+    if (threadIdx.x < 128) {
+      uint16_t* Kw = reinterpret_cast<uint16_t*>(c.k);
+      uint16_t* Vw = reinterpret_cast<uint16_t*>(c.v);
+      const int d = threadIdx.x;
+      Kw[k_chunk_tiled(row0 + new_row, d >> 3) + (d & 7)] = k_new[d];
+      Vw[v_index(it.cache, c.rows, new_row, 128, d)] = v_new[d];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // Q^T operand: column r = query head kvh*G + r (zero beyond G), dims 32g + 8s .. +7.
@@ -205,35 +201,31 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const float sl2 = g.scale_log2;
-  // Each wavefront takes every fourth 32-key tile of the range and keeps a ring of
-  // kRing tiles in flight: the slot just consumed is refilled with the tile kRing
-  // steps ahead, so memory latency is covered by several tiles of work.
   // Each wavefront takes every kWaves-th 32-key tile of the range and keeps a ring of
   // kRing tiles in flight: the slot just consumed is refilled with the tile kRing
-  // rounds ahead.  Loads are issued unconditionally (a tile past the end re-reads the
-  // wave's first tile, an L2 hit that is never used) so the compiler can count them.
+  // rounds ahead (past the range: a bounds-checked load of zeros, no memory traffic).
   constexpr int kRing = 2;
+  const int ntile32 = static_cast<int>((it.key1 - it.key0 + 31) >> 5);
+  SplitBuffers sb;
+  sb.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K + ((row0 + it.key0) >> 5) * 4096), 0,
+                                           ntile32 * 8192, kRawBuffer);
+  sb.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V + (row0 + it.key0) * 128), 0, ntile32 * 8192,
+                                           kRawBuffer);
   Tile ring[kRing];
-  const int64_t first = it.key0 + 32 * wave;
-  const int64_t fallback = first < it.key1 ? first : it.key0;
-  uint32_t vn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const bool has_new = new_row >= it.key0 && new_row < it.key1;
-  if (has_new) {
+  const int rel0 = 32 * wave;
+  // this wavefront's tiles, processed kRing per iteration with no early exit (a tile
+  // past the range is all zeros and fully masked: it adds nothing)
+  const int64_t span = it.key1 - it.key0 - rel0;
+  const int n_tiles = span > 0 ? static_cast<int>((span + kStride - 1) / kStride) : 0;
+  const int n_iter = __builtin_amdgcn_readfirstlane((n_tiles + kRing - 1) / kRing);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vn[j] = v_new[16 * j + r];
-  }
-#pragma unroll
-  for (int u = 0; u < kRing; ++u) {
-    const int64_t b = first + kStride * u;
-    load_tile(ring[u], K, V, row0, b < it.key1 ? b : fallback, r, grp, new_row, k_new, v_new);
-  }
-  for (int64_t base0 = first; base0 < it.key1; base0 += kStride * kRing) {
+  for (int u = 0; u < kRing; ++u) load_tile(ring[u], sb, rel0 + kStride * u, r, grp);
+  for (int iter = 0; iter < n_iter; ++iter) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      const int64_t base = base0 + kStride * u;
-      if (base >= it.key1) break;
+      const int rel = rel0 + kStride * (kRing * iter + u);
+      const int64_t base = it.key0 + rel;
       Tile& cur = ring[u];
-      if (has_new && new_row >= base && new_row < base + 32) patch_v(cur, base, grp, new_row, vn);
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -271,8 +263,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
                         pack_bf16(sc[6], sc[7])};
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = mfma16(cur.v[j], pb, o[j]);
-      const int64_t nb = base + kStride * kRing;
-      load_tile(cur, K, V, row0, nb < it.key1 ? nb : fallback, r, grp, new_row, k_new, v_new);
+      load_tile(cur, sb, rel + kStride * kRing, r, grp);
     }
   }
 

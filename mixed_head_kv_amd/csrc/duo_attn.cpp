@@ -256,6 +256,8 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   const int64_t min_chunk = (nkeys + max_splits - 1) / max_splits;
   if (chunk < min_chunk) chunk = min_chunk;
   if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
+  // a split's K and V are addressed with 32-bit byte offsets (256 bytes per key)
+  if (chunk > (int64_t(1) << 22)) chunk = int64_t(1) << 22;
   chunk = int64_t(align_up(uint64_t(chunk), 64));
   p.chunk_r = int(chunk);
   p.nsplit_r = int((nkeys + chunk - 1) / chunk);
