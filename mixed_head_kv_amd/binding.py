@@ -104,13 +104,23 @@ def make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, sink, recent, 
 
 
 def _stream(stream=None):
+    """A torch stream, a raw hipStream_t (int or c_void_p), or None for torch's current."""
+    if isinstance(stream, ctypes.c_void_p):
+        return stream
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address, or a raw address given as an int; None stays NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
 
 
 # ---- the C entry points, same names ------------------------------------------------
