@@ -154,7 +154,7 @@ __device__ void merge_splits_wide(const Geom& g, const DecodePlan& p, int b, int
 __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, DecodePlan p,
                                                        const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
   __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][129];  // also the merge scratch
+  __shared__ __attribute__((aligned(16))) float s_o[kWaves][16][132];  // (16-byte rows) also the merge scratch
 
   const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
   const int lane = threadIdx.x & 63;
@@ -267,17 +267,19 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
     }
   }
 
-  // Combine the four wavefronts: lane sums over its group, then across waves in LDS.
+  // Combine the wavefronts: lane sums over its group, then across waves in LDS (only
+  // the G real query columns are written).
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (grp == 0) {
-    s_m[wave][r] = m;
-    s_l[wave][r] = l;
+  if (r < G) {
+    if (grp == 0) {
+      s_m[wave][r] = m;
+      s_l[wave][r] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<f32x4*>(&s_o[wave][r][16 * j + 4 * grp]) = o[j];
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][r][16 * j + 4 * grp + i] = o[j][i];
   __syncthreads();
 
   const int pairs = G * 128;
@@ -289,7 +291,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
+      const float wt = s_l[w][qi] > 0.0f ? __builtin_amdgcn_exp2f(s_m[w][qi] - M) : 0.0f;
       L = fmaf(wt, s_l[w][qi], L);
       acc = fmaf(wt, s_o[w][qi][d], acc);
     }
@@ -371,7 +373,7 @@ __device__ inline void load_tile4(Tile4& t, const CacheRegion& c, int64_t cache,
 __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, DecodePlan p,
                                                             const uint16_t* __restrict__ q, uint16_t* __restrict__ out) {
   __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][129];  // also the merge scratch
+  __shared__ __attribute__((aligned(16))) float s_o[kWaves][16][132];  // (16-byte rows) also the merge scratch
 
   const DecodeItem it = decode_item(g, lv, p, blockIdx.x);
   const int lane = threadIdx.x & 63;
@@ -485,14 +487,15 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
   zsum += __shfl_xor(zsum, 16);
   zsum += __shfl_xor(zsum, 32);
   const float corr = zsum - 128.0f * pacc[0];  // pacc already sums all 32 keys of each tile
-  if (grp == 0) {
-    s_m[wave][r] = m;
-    s_l[wave][r] = l;
+  if (r < G) {  // only the G real query columns
+    if (grp == 0) {
+      s_m[wave][r] = m;
+      s_l[wave][r] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<f32x4*>(&s_o[wave][r][16 * j + 4 * grp]) = o[j] + f32x4{corr, corr, corr, corr};
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][r][16 * j + 4 * grp + i] = o[j][i] + corr;
   __syncthreads();
 
   const int pairs = G * 128;
@@ -504,7 +507,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = s_l[w][qi] > 0.0f ? exp2f(s_m[w][qi] - M) : 0.0f;
+      const float wt = s_l[w][qi] > 0.0f ? __builtin_amdgcn_exp2f(s_m[w][qi] - M) : 0.0f;
       L = fmaf(wt, s_l[w][qi], L);
       acc = fmaf(wt, s_o[w][qi][d], acc);
     }
