@@ -42,6 +42,7 @@ KERNEL_SOURCES = {
     "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
     "prefill_retrieval_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "prefill_streaming_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "prefill_streaming_staging": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -107,6 +108,29 @@ def prefill_flops(w, t0, T, retrieval=True):
     cap = w.sink + w.recent
     pairs = sum(min(i + 1, cap) for i in range(t0, t0 + T))
     return 4 * w.head_dim * pairs * int((~mask).sum()) * G
+
+
+STAGE_TOKENS = 4096  # queries per streaming-head prefill launch (the library's staging capacity)
+
+
+def stage_bytes(w, t0, T):
+    """Algorithmic HBM bytes of staging the streaming-head keys of one prefill chunk
+    [t0, t0+T), per launch of at most STAGE_TOKENS queries: the rows written (sink rows,
+    window rows from R-1 positions before the first query, the queries' own rows, each
+    rounded up to 64) plus the K+V rows read (sinks and window positions that hold a key)."""
+    al = lambda x: (x + 63) // 64 * 64
+    ns = w.n_kv_heads - int(w.mask(0).sum())
+    vec = 2 * w.head_dim * esize(w)  # K + V of one row
+    sp, win = al(w.sink), al(w.recent - 1)
+    total = 0
+    tc = min(STAGE_TOKENS, al(w.max_context))
+    for q0 in range(0, T, tc):
+        nq = min(tc, T - q0)
+        u0 = t0 + q0
+        written = sp + win + al(nq)
+        read = min(w.sink, u0 + nq) + (u0 + nq - max(w.sink, u0 - win, t0 - w.recent, 0))
+        total += ns * vec * (written + read)
+    return total
 
 
 def run(args):
@@ -207,14 +231,16 @@ def run(args):
     app_ms = totals["append"][0] / args.steps
     pre_r_ms = totals["prefill_retrieval"][0] / args.steps
     pre_s_ms = totals["prefill_streaming"][0] / args.steps
+    stage_ms = totals["prefill_stage"][0] / args.steps
 
     # algorithmic work per step
     dec_bytes = sum(decode_bytes(w, t) for t in range(w.context, total))
-    fl_r = fl_s = 0
+    fl_r = fl_s = st_bytes = 0
     t = 0
     for T in chunks:
         fl_r += prefill_flops(w, t, T, True)
         fl_s += prefill_flops(w, t, T, False)
+        st_bytes += stage_bytes(w, t, T)
         t += T
 
     rooflines = []
@@ -237,8 +263,15 @@ def run(args):
         rooflines.append({"kernel": "prefill_streaming_attention", "bound": "mfma", "achieved": round(a, 2),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "avg_launch_us": round(pre_s_ms * 1e3 / len(chunks), 2), "ms_per_step": round(pre_s_ms, 4),
+                          "avg_launch_us": round(pre_s_ms * 1e3 / totals["prefill_streaming"][1] * args.steps, 2),
+                          "ms_per_step": round(pre_s_ms, 4),
                           "traffic": None})
+    if totals["prefill_stage"][1]:
+        a = st_bytes / (stage_ms * 1e-3) / 1e9
+        rooflines.append({"kernel": "prefill_streaming_staging", "bound": "hbm", "achieved": round(a, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                          "avg_launch_us": round(stage_ms * 1e3 / totals["prefill_stage"][1] * args.steps, 2),
+                          "ms_per_step": round(stage_ms, 4), "traffic": None})
     for r in rooflines:
         r["traffic"] = measured_traffic(r["kernel"], w.name)
     dominant = max(rooflines, key=lambda r: r["ms_per_step"]) if rooflines else None
@@ -250,7 +283,7 @@ def run(args):
     per_app = app_ms / n_app if n_app else 0.0
     pre_app = min(n_app, 2 * len(chunks))
     dec_app_launches = max(0.0, n_app - pre_app) / w.decode_steps
-    prefill_ms = pre_r_ms + pre_s_ms + per_app * pre_app
+    prefill_ms = pre_r_ms + pre_s_ms + stage_ms + per_app * pre_app
     res = {
         "metric": METRIC,
         "value": round(tokens / (ms_per_step * 1e-3), 1),
@@ -456,7 +489,8 @@ def cpu_baseline(w, total, budget_s):
 
 PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
                     "prefill_retrieval_attention": ["k_prefill_mfma<false>"],
-                    "prefill_streaming_attention": ["k_prefill_mfma<true>"]}
+                    "prefill_streaming_attention": ["k_prefill_mfma<true>"],
+                    "prefill_streaming_staging": ["k_stage_streaming"]}
 
 
 def _csvs(d, suffix):

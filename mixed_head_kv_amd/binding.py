@@ -30,7 +30,7 @@ DUO_KV_INT4_G128 = 1
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
            "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect"]
-KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode"]
+KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage"]
 
 
 class DuoError(RuntimeError):

@@ -59,6 +59,11 @@ struct Layout {
   int64_t nslot = 0; // streaming slots per cache
   std::vector<LayerLayout> layers;
   uint64_t partials = 0, counters = 0, prefill_counters = 0, total = 0;
+  // streaming-head prefill staging (bf16, head_dim 128, bf16 caches only)
+  int stage_tokens = 0;       // queries per staged launch
+  int64_t stage_rows = 0;     // rows per streaming cache
+  int stage_caches = 0;       // batch * most streaming heads of any layer
+  uint64_t stage_k = 0, stage_v = 0;
 };
 
 int validate_config(const duo_config* c) {
@@ -128,6 +133,16 @@ bool make_layout(const duo_config* c, Layout* L) {
   off = align_up(off + B * c->n_kv_heads * 4, kAlign);
   L->prefill_counters = off;
   off = align_up(off + uint64_t(duo::kPrefillCounters) * 4, kAlign);
+  if (c->io_dtype == DUO_DTYPE_BF16 && D == 128 && !int4) {
+    int n_str = 0;
+    for (const LayerLayout& y : L->layers) n_str = y.n_str > n_str ? y.n_str : n_str;
+    L->stage_tokens = int(L->cap < duo::kStageTokens ? L->cap : duo::kStageTokens);
+    L->stage_rows = duo::stage_sink_rows(c->sink) + duo::stage_window_rows(c->recent) + L->stage_tokens;
+    L->stage_caches = int(B) * n_str;
+    const uint64_t bytes = uint64_t(L->stage_caches) * uint64_t(L->stage_rows) * D * 2;
+    L->stage_k = off; off = align_up(off + bytes, kAlign);
+    L->stage_v = off; off = align_up(off + bytes, kAlign);
+  }
   L->total = off;
   return true;
 }
@@ -143,6 +158,8 @@ struct duo_handle {
   Geom geom;
   std::vector<LayerView> views;
   std::vector<int64_t> len;
+  CacheRegion stage{};   // streaming-head prefill staging (MFMA path)
+  int stage_tokens = 0;
   float* partials = nullptr;
   int64_t partial_floats = 0;
   int* counters = nullptr;
@@ -339,6 +356,8 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
     }
   }
   h->len.assign(cfg->n_layers, 0);
+  h->stage = CacheRegion{h->ws + L.stage_k, h->ws + L.stage_v, nullptr, nullptr, L.stage_rows, 1};
+  h->stage_tokens = L.stage_tokens;
   h->partials = reinterpret_cast<float*>(h->ws + L.partials);
   h->counters = reinterpret_cast<int*>(h->ws + L.counters);
   h->prefill_counters = reinterpret_cast<int*>(h->ws + L.prefill_counters);
@@ -413,11 +432,21 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
                                    h->prefill_counters, h->num_cu, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill attention (retrieval)");
-    {
-      KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
-      e = duo::launch_prefill_stream_mfma(h->geom, lv, q, k, v, out, n_tokens, t0, st);
+    // streaming heads, at most stage_tokens queries per launch pair: their keys are
+    // staged in the cache layout, then attended
+    for (int q0 = 0; lv.n_str > 0 && q0 < n_tokens; q0 += h->stage_tokens) {
+      const int nq = n_tokens - q0 < h->stage_tokens ? n_tokens - q0 : h->stage_tokens;
+      {
+        KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
+        e = duo::launch_stage_streaming(h->geom, lv, h->stage, k, v, n_tokens, t0, q0, nq, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
+      {
+        KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
+        e = duo::launch_prefill_stream_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, q0, nq, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
     }
-    if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
     {
       KernelMark m(h, DUO_KERNEL_APPEND, st);
       e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 2, st);

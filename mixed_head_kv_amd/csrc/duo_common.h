@@ -34,6 +34,7 @@ namespace duo {
 constexpr int kMaxSplits = 2048;    // split-K partial slots per query head (decode; prefill reuses the buffer)
 constexpr int kPrefillCounters = 1 << 16;  // arrival counters for split prefill query blocks
 constexpr int kRowAlign = 64;       // cache rows are allocated in multiples of this
+constexpr int kStageTokens = 4096;  // queries per streaming-head prefill launch (staging capacity)
 constexpr int kKindRetrieval = 1;
 constexpr int kKindStreaming = 0;
 
@@ -156,6 +157,12 @@ __device__ inline float cache_v(const CacheRegion& c, int64_t cache, int64_t row
     return io_load<IO>(c.v, v_index(cache, c.rows, row, D, d));
   }
 }
+
+// Streaming-head prefill staging (one region per streaming cache, shared by the layers):
+// sink rows [0, Sp), then window rows covering the W positions before a launch's first
+// query (W >= R - 1, so every window key of its queries is there) and its queries.
+__host__ __device__ inline int stage_sink_rows(int S) { return (S + kRowAlign - 1) / kRowAlign * kRowAlign; }
+__host__ __device__ inline int stage_window_rows(int R) { return (R - 1 + kRowAlign - 1) / kRowAlign * kRowAlign; }
 
 // Streaming slot of an absolute position that the constant-length cache holds.
 __host__ __device__ inline int64_t stream_slot(int64_t p, int S, int R) {

@@ -50,10 +50,17 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
                                int64_t t0, float* scratch, int64_t scratch_floats, int* counters, int num_cu,
                                hipStream_t st);
 
-// Streaming-head (sink + window) prefill on bf16 MFMA (D = 128); reads the streaming
-// caches as they stood before the chunk plus the chunk inputs.
-hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const void* q, const void* k,
-                                      const void* v, void* out, int T, int64_t t0, hipStream_t st);
+// Streaming-head prefill on bf16 MFMA (D = 128), one launch pair per at most
+// kStageTokens queries (chunk rows [q0, q0 + nq)): launch_stage_streaming copies the
+// keys those queries may see (sinks, and the window from R - 1 positions before q0 on)
+// into `stage`, from the chunk inputs and from the streaming caches as they stood before
+// the chunk; launch_prefill_stream_mfma then runs the sink + window attention over them.
+// `stage` holds at least stage_sink_rows(S) + stage_window_rows(R) + nq rounded up to a
+// multiple of 64 rows per streaming cache, in the cache layout.
+hipError_t launch_stage_streaming(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
+                                  const void* v, int T, int64_t t0, int q0, int nq, hipStream_t st);
+hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
+                                      void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);
 
 struct DecodePlan {
   int64_t t;          // query position

@@ -3,19 +3,20 @@
 //   retrieval heads: causal attention of the chunk's queries over every key [0, i],
 //     read from the retrieval cache (the chunk is appended to it first);
 //   streaming heads: the Lambda-shaped mask of sinks [0, S) plus the recent window
-//     (i - R, i], visiting only the key tiles that hold sinks or window keys; keys
-//     before the chunk come from the constant-length cache as it stood before the
-//     chunk, keys of the chunk from its K/V inputs.
+//     (i - R, i], over keys staged (k_stage_streaming) into the same cache layout: the
+//     sink rows, then the window rows of the launch's queries, taken from the chunk
+//     inputs and from the constant-length cache as it stood before the chunk.
 // Source: hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with
 // Retrieval and Streaming Heads", abstract (full attention for retrieval heads, recent
 // tokens and sinks for streaming heads, lower pre-filling latency) and its technical-
 // approach section; cn.bg3.co article, 研究背景 section (pre-filling cost of full
 // attention grows quadratically with the context).
 //
-// Workgroup: 4 wavefronts x 32 queries of one query head.  Keys move through LDS in
-// 64-key tiles, double-buffered (K rows with their 16-byte chunks XOR-swizzled by the
-// row index so the permuted row reads hit distinct banks; V in d-major 8-key blocks).  Per
-// 32-key half tile each wavefront runs, with v_mfma_f32_32x32x16_bf16,
+// Workgroup: 4 wavefronts x 32 queries of one query head.  Keys move HBM -> LDS with
+// direct loads in 64-key tiles, double-buffered (K rows with their 16-byte chunks
+// XOR-swizzled by the row index so the permuted row reads hit distinct banks; V in
+// d-major 8-key blocks).  Per 32-key half tile each wavefront runs, with
+// v_mfma_f32_32x32x16_bf16,
 //   S^T[32 keys x 32 queries] = K * Q^T    (8 k-steps over head_dim)
 //   O^T[32 d x 32 queries]   += V^T * P^T  (4 d-blocks x 2 k-steps)
 // Rows of the K operand are read in the permuted key order that leaves each lane
@@ -83,17 +84,18 @@ struct PrefillArgs {
   Geom g;
   LayerView lv;
   const uint16_t* q;    // [B, T, Hq, 128]
-  const uint16_t* k;    // chunk inputs [B, T, Hkv, 128] (streaming heads)
-  const uint16_t* v;
   uint16_t* out;        // [B, T, Hq, 128]
-  int T;
-  int64_t t0;
-  int streaming;        // 0: retrieval heads, 1: streaming heads
+  int T;                // tokens of the chunk (row stride of q and out)
+  int64_t t0;           // position of chunk row 0
+  int q0, nq;           // this launch's queries: chunk rows [q0, q0 + nq)
   int n_heads;          // query heads of this kind per sequence
   int n_qblocks;
   int nsplit;           // workgroups sharing one query block's key range (1 or 2)
   float* scratch;       // nsplit > 1: per (block, split) fp32 partial, kSlotFloats each
   int* counters;        // nsplit > 1: arrival counter per query block
+  CacheRegion stage;    // streaming heads: the staged keys, one region per streaming cache
+  int stage_sink_rows;  // streaming heads: staged sink rows (before the window rows)
+  int64_t stage_p0;     // streaming heads: position held by the first window row
 };
 
 // Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
@@ -112,98 +114,13 @@ __device__ inline int o_chunk_offset(int c, int ql) { return (c * kQRows + ql) *
 
 // Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
 // this kind, in KV-head-major order.
+template <bool STREAMING>
 __device__ inline int kind_head(const PrefillArgs& a, int idx, int* kvh) {
   const int G = a.g.G;
-  const int kv = a.streaming ? a.lv.str_kv[idx / G] : a.lv.ret_kv[idx / G];
+  const int kv = STREAMING ? a.lv.str_kv[idx / G] : a.lv.ret_kv[idx / G];
   *kvh = kv;
   return kv * G + idx % G;
 }
-
-// One 64-key tile moves HBM -> registers -> LDS in two phases so the next tile's loads
-// are in flight while the current tile is computed.  Each thread carries four 16-byte
-// K chunks and four 16-byte V units.  Modes (uniform per tile):
-//   kCopy   : 64 contiguous cache rows (retrieval rows, or streaming sink slots that
-//             equal their positions): K rows and d-major V blocks copied as they are;
-//   kInput  : 64 positions inside the chunk: K rows from the input; V rows of key pairs
-//             (2k, 2k+1) x 8 dims, transposed into the d-major blocks on the LDS store;
-//   kGather : anything else (window keys that straddle the chunk start, or sinks mixed
-//             with ring slots): every key looked up in the chunk or its cache slot.
-enum { kCopy = 0, kInput = 1, kGather = 2 };
-
-struct Stage {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-__device__ inline int64_t slot_of(int64_t pos, int S, int R) {
-  return pos < S ? pos : S + static_cast<int>(pos - S) % R;
-}
-
-template <bool STREAMING>
-__device__ inline void stage_load(const PrefillArgs& a, int b, int kvh, int64_t cache, int64_t kb, int mode,
-                                  Stage& st) {
-  const int tid = threadIdx.x;
-  const Geom& g = a.g;
-  const CacheRegion& c = STREAMING ? a.lv.str : a.lv.ret;
-  if (mode == kCopy) {
-    const char* K = c.k + ((cache * c.rows + kb) * 128) * 2;
-    const char* V = c.v + ((cache * c.rows + kb) * 128) * 2;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ch = tid + 256 * u;  // 16-byte chunk of the 16 KB tile
-      st.k[u] = *reinterpret_cast<const u32x4*>(K + ch * 16);
-      st.v[u] = *reinterpret_cast<const u32x4*>(V + ch * 16);
-    }
-    return;
-  }
-  if constexpr (STREAMING) {
-    const int64_t in_row = (int64_t(b) * a.T) * g.Hkv + kvh;  // + t * Hkv gives the input row of chunk token t
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ch = tid + 256 * u;
-      const int row = ch >> 4, col = ch & 15;
-      const int64_t pos = kb + row;
-      const uint16_t* src = nullptr;
-      if (pos >= a.t0) {
-        const int64_t t = pos - a.t0;
-        if (t < a.T) src = a.k + (in_row + t * g.Hkv) * 128 + col * 8;
-      } else {  // cache K rows are MFMA-ordered 32-key tiles
-        src = reinterpret_cast<const uint16_t*>(c.k) + k_chunk_tiled(cache * c.rows + slot_of(pos, g.S, g.R), col);
-      }
-      st.k[u] = src ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-    }
-    // V: task = (key pair kp in 0..31, 8-dim chunk dc in 0..15); two tasks per thread,
-    // each two 16-byte rows (keys 2kp and 2kp + 1, dims 8dc .. 8dc+7).
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int task = tid + 256 * u;
-      const int kp = task >> 4, dc = task & 15;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t pos = kb + 2 * kp + e;
-        u32x4 val = {0, 0, 0, 0};
-        if (pos >= a.t0) {
-          const int64_t t = pos - a.t0;
-          if (t < a.T) val = *reinterpret_cast<const u32x4*>(a.v + (in_row + t * g.Hkv) * 128 + 8 * dc);
-        } else if (mode == kGather) {
-          const uint16_t* V = reinterpret_cast<const uint16_t*>(c.v);
-          const int64_t slot = slot_of(pos, g.S, g.R);
-          uint16_t x[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = V[v_index(cache, c.rows, slot, 128, 8 * dc + i)];
-          val = u32x4{uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16),
-                      uint32_t(x[4]) | (uint32_t(x[5]) << 16), uint32_t(x[6]) | (uint32_t(x[7]) << 16)};
-        }
-        st.v[2 * u + e] = val;
-      }
-    }
-  }
-}
-
-// LDS K tiles are row-major with 16-byte chunks XOR-swizzled by row.  A copied tile
-// arrives in the cache's MFMA-ordered 32-key layout: its chunk p of 32-key tile q holds
-// dims 8*(4*grp + s) of key 32q + 8*(r>>2) + (r&3) + 4t, where p = (t*4 + s)*64 + grp*16 + r.
-__device__ inline int lds_k_offset(int row, int col16) { return row * 256 + ((col16 ^ (row & 15)) * 16); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -240,47 +157,6 @@ __device__ inline void tile_dma_offsets(int wave, int lane, int (&koff)[4]) {
   }
 }
 
-template <bool STREAMING>
-__device__ inline void stage_store(int mode, const Stage& st, char* ldsK, char* ldsV) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ch = tid + 256 * u;
-    int row, col16;
-    if (mode == kCopy) {
-      const int p = ch & 511, inst = p >> 6, lane = p & 63;
-      const int r = lane & 15, grp = lane >> 4;
-      row = 32 * (ch >> 9) + 8 * (r >> 2) + (r & 3) + 4 * (inst >> 2);
-      col16 = 4 * grp + (inst & 3);
-    } else {
-      row = ch >> 4;
-      col16 = ch & 15;
-    }
-    *reinterpret_cast<u32x4*>(ldsK + lds_k_offset(row, col16)) = st.k[u];
-  }
-  if (!STREAMING || mode == kCopy) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(ldsV + (tid + 256 * u) * 16) = st.v[u];
-    return;
-  }
-  // transpose key pairs into d-major 8-key blocks: dword (d, keys 2kp, 2kp+1)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int task = tid + 256 * u;
-    const int kp = task >> 4, dc = task & 15;
-    const u32x4 lo = st.v[2 * u], hi = st.v[2 * u + 1];
-    char* dst = ldsV + ((2 * kp) >> 3) * 2048 + (8 * dc) * 16 + ((2 * kp) & 7) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
-      const uint32_t even = __builtin_amdgcn_perm(hi[w], lo[w], 0x05040100u);
-      const uint32_t odd = __builtin_amdgcn_perm(hi[w], lo[w], 0x07060302u);
-      *reinterpret_cast<uint32_t*>(dst + (2 * w) * 16) = even;
-      *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * 16) = odd;
-    }
-  }
-}
-
 // K operand of k-step st for the S^T product of a 32-key half tile starting at LDS row
 // `row0`: lane (col, half) supplies key row0 + pi(col) and dims 64 half + 8 st .. +7, where
 // pi(8j + 4h + i) = 16(j>>1) + 8h + 4(j&1) + i is the permuted key order that leaves each
@@ -307,38 +183,49 @@ __device__ inline void pack_probs(const f32x16& p, u32x4 (&pb)[2], float& l) {
   }
 }
 
-// Scores of keys a query may not see become -inf, in place: register 4j + i of a
-// 32-key block starting at `base` is key base + 16(j>>1) + 8 half + 4(j&1) + i.  A key
-// is visible to query position i_pos when it is not after it and (streaming heads) it is
-// a sink (< S) or inside the recent window (i_pos - key < R).
-template <bool STREAMING>
+// Scores of keys a query may not see become -inf, in place.  Register 4j + i of a
+// 32-key block starting at position `base` holds key base + 8 half + c with
+// c = 16(j>>1) + 4(j&1) + i; the query of the lane sits at position i_pos.  Visibility
+// (the mask of the page's streaming heads splits into two disjoint key sets):
+//   kMaskCausal : key <= i                      (retrieval heads)
+//   kMaskSink   : key <= i and key < S          (streaming heads, sink rows)
+//   kMaskWindow : key <= i, i - key < R, key >= S  (streaming heads, window rows)
+// Each condition is a bound on c, computed once per block in 64-bit and clamped.
+enum { kMaskCausal = 0, kMaskSink = 1, kMaskWindow = 2 };
+
+__device__ inline int clamp_off(int64_t x) { return static_cast<int>(x < -1 ? -1 : (x > 64 ? 64 : x)); }
+
+template <int KIND>
 __device__ inline void mask_block(f32x16& s, int64_t base, int64_t i_pos, int half, int S, int R) {
-  const int rel0 = static_cast<int>(base - i_pos);  // key - query position for register 0
+  const int h8 = 8 * half;
+  int c_hi = clamp_off(i_pos - base);  // key <= i
+  int c_lo = -1;
+  if (KIND == kMaskSink) c_hi = min(c_hi, clamp_off(S - base) - 1);                              // key < S
+  if (KIND == kMaskWindow) c_lo = max(clamp_off(i_pos - R - base) + 1, clamp_off(S - base));  // i - key < R, key >= S
+  c_hi -= h8;
+  c_lo -= h8;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int off = 16 * (j >> 1) + 8 * half + 4 * (j & 1) + i;
-      const int rel = rel0 + off;
-      bool vis = rel <= 0;
-      if (STREAMING) vis = vis && (-rel < R || static_cast<int>(base - S) + off < 0);
-      s[4 * j + i] = vis ? s[4 * j + i] : kNegInf;
+      const int c = 16 * (j >> 1) + 4 * (j & 1) + i;
+      s[4 * j + i] = (c <= c_hi && c >= c_lo) ? s[4 * j + i] : kNegInf;
     }
 }
 
 // One 64-key tile for the wavefront's 32 queries.  Both 32-key score blocks are formed
 // first (the second block's MFMAs run while the first block's maximum is taken), the
-// scores outside the mask are set to -inf in place when the tile needs it (a uniform
+// scores outside the mask are set to -inf in place when the tile needs it (`mask`, a uniform
 // branch that touches only the score registers, so O stays in one register set), one
 // running-max update serves the tile, and the exponentials of the second block are
 // issued between the MFMAs of the first block's P*V, so the vector ALU and the matrix
 // cores work at the same time.  The running max m may lag the true one by up to kSlack
 // (log2 units): weights are then at most 2^kSlack, harmless in fp32 and bf16, and the
 // rescale (which touches all of O) runs only when some lane's max outgrows m + kSlack.
-template <bool STREAMING>
+template <typename MaskFn>
 __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
                                              f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half,
-                                             bool masked, int64_t kb, int64_t i_pos, int S, int R) {
+                                             bool masked, const MaskFn& mask) {
   const int pk = k_perm(col);
   const int sw = pk & 15;  // row swizzle (rows pk and 32 + pk share it)
   u32x4 kop[8];
@@ -360,9 +247,9 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < 8; ++st) s1 = mfma32(kop[st], qop[st], s1);
-  if (masked) {
-    mask_block<STREAMING>(s0, kb, i_pos, half, S, R);
-    mask_block<STREAMING>(s1, kb + 32, i_pos, half, S, R);
+  if (masked) {  // mask(s, off): scores of the 32-key block at tile offset off
+    mask(s0, 0);
+    mask(s1, 32);
   }
   const float mx = max_across_halves(max32(s0, s1)) * sl2;
   if (__ballot(mx > m + kSlack)) {
@@ -438,16 +325,16 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   const int qb = a.n_qblocks - 1 - hq / a.n_heads;
   const int head_idx = hq % a.n_heads;
   int kvh;
-  const int h = kind_head(a, head_idx, &kvh);
+  const int h = kind_head<STREAMING>(a, head_idx, &kvh);
   const int64_t cache = int64_t(b) * (STREAMING ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
-  const int q_first = qb * kQRows;                        // chunk-relative
-  const int q_last = min(q_first + kQRows, a.T) - 1;
+  const int q_first = a.q0 + qb * kQRows;                 // chunk-relative
+  const int q_last = min(q_first + kQRows, a.q0 + a.nq) - 1;
   const int my_q = q_first + 32 * wave + col;             // this lane's query
-  const bool q_valid = my_q < a.T;
+  const bool q_valid = my_q <= q_last;
   const int64_t i_pos = a.t0 + (q_valid ? my_q : q_last); // absolute position
   const int64_t wave_q_hi = a.t0 + min(q_first + 32 * wave + 31, q_last);
   const int64_t wave_q_lo = a.t0 + q_first + 32 * wave;
@@ -469,50 +356,18 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
 
-  // Key tiles to visit.  Retrieval: [0, t0 + q_last].  Streaming: the sink tiles
-  // covering [0, S) and the window tiles covering [max(S, lo - R + 1), hi].
-  const int64_t hi = a.t0 + q_last;
-  int64_t n0, n1 = 0, s1_start = 0;
-  if (!STREAMING) {
-    n0 = (hi + 1 + kTileKeys - 1) / kTileKeys;
-  } else {
-    const int64_t seg0_end = g.S < hi + 1 ? g.S : hi + 1;
-    n0 = (seg0_end + kTileKeys - 1) / kTileKeys;
-    int64_t wlo = a.t0 + q_first - g.R + 1;
-    if (wlo < g.S) wlo = g.S;
-    if (wlo <= hi) {
-      s1_start = wlo / kTileKeys;
-      n1 = hi / kTileKeys - s1_start + 1;
-      if (s1_start < n0) {
-        n1 -= n0 - s1_start;
-        s1_start = n0;
-      }
-      if (n1 < 0) n1 = 0;
-    }
-  }
-  // a split takes a contiguous share of the tiles (the diagonal ones go to the last split)
-  const int64_t all_tiles = n0 + n1;
-  const int64_t t_begin = all_tiles * split / a.nsplit;
-  const int64_t ntiles = all_tiles * (split + 1) / a.nsplit - t_begin;
-  auto tile_start = [&](int64_t tj) -> int64_t {
-    const int64_t ti = t_begin + tj;
-    return (ti < n0 ? ti : s1_start + (ti - n0)) * kTileKeys;
-  };
-  auto tile_mode = [&](int64_t kb) -> int {
-    if (!STREAMING) return kCopy;
-    const int64_t lim = g.S < a.t0 ? g.S : a.t0;  // positions below this sit in their own sink slot
-    if (kb + kTileKeys <= lim) return kCopy;
-    if (kb >= a.t0 && kb + kTileKeys <= a.t0 + a.T) return kInput;
-    return kGather;
-  };
   const float sl2 = g.scale_log2;
+  int koff[4];
+  tile_dma_offsets(wave, lane, koff);
 
   if constexpr (!STREAMING) {
-    // Retrieval: tiles [t_begin, t_begin + ntiles) of the cache.  The leading tiles hold
-    // only keys before the block's first query (visible to every query): they run in a
-    // loop with the mask compiled out; the few tiles on the diagonal follow.
-    int koff[4];
-    tile_dma_offsets(wave, lane, koff);
+    // Retrieval: keys [0, t0 + q_last] of the cache, 64 per tile; a split takes a
+    // contiguous share of the tiles (the diagonal ones go to the last split).  The leading
+    // tiles hold only keys before the block's first query (visible to every query): they
+    // run in a loop with the mask compiled out; the few tiles on the diagonal follow.
+    const int64_t all_tiles = (a.t0 + q_last + kTileKeys) / kTileKeys;
+    const int64_t t_begin = all_tiles * split / a.nsplit;
+    const int64_t ntiles = all_tiles * (split + 1) / a.nsplit - t_begin;
     const int64_t kb_first = t_begin * kTileKeys;
     const int64_t first_q = a.t0 + q_first;
     int64_t n_inner = first_q >= kb_first + kTileKeys - 1 ? (first_q - (kb_first + kTileKeys - 1)) / kTileKeys + 1 : 0;
@@ -525,11 +380,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
         tile_dma(a.lv.ret, cache, kb_first + (ti + 1) * kTileKeys, nK, nK + kKBytes, wave, lane, koff);
       }
     };
+    auto no_mask = [](f32x16&, int) {};
     int64_t ti = 0;
     for (; ti < n_inner; ++ti) {
       const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
       prefetch(ti);
-      tile_compute<false>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, 0, 0, 0, 0);
+      tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask);
       __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
     }
     for (; ti < ntiles; ++ti) {
@@ -538,81 +394,57 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       prefetch(ti);
       if (kb <= wave_q_hi) {  // (a tile wholly after the wavefront's queries is skipped)
         const bool inside = kb + kTileKeys - 1 <= wave_q_lo;  // every key visible to every query
-        tile_compute<false>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !inside, kb, i_pos, g.S, g.R);
+        tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !inside, [&](f32x16& sc, int off) {
+          mask_block<kMaskCausal>(sc, kb + off, i_pos, half, 0, 0);
+        });
       }
       __syncthreads();
     }
   } else {
-  Stage stage;
-  if (ntiles > 0) {
-    const int64_t kb = tile_start(0);
-    const int mode = tile_mode(kb);
-    stage_load<STREAMING>(a, b, kvh, cache, kb, mode, stage);
-    stage_store<STREAMING>(mode, stage, lds, lds + kKBytes);
-  }
-  __syncthreads();
-
-  for (int64_t ti = 0; ti < ntiles; ++ti) {
-    char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
-    char* ldsV = ldsK + kKBytes;
-    const int64_t kb = tile_start(ti);
-    const bool more = ti + 1 < ntiles;
-    int next_mode = kCopy;
-    if (more) {  // the next tile is in flight during the compute
-      const int64_t nkb = tile_start(ti + 1);
-      next_mode = tile_mode(nkb);
-      stage_load<STREAMING>(a, b, kvh, cache, nkb, next_mode, stage);
-    }
-      // Streaming heads hold their next tile in registers during the compute, so they take
-      // the half tiles one at a time (fewer live registers).
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int64_t base = kb + 32 * sub;
-        if (base > wave_q_hi) continue;  // every key of this half tile is after the wave's queries
-        const int pk = k_perm(col);
-        const int krow_i = 32 * sub + pk;
-        const char* krow = ldsK + krow_i * 256;
-        u32x4 kop[8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-          kop[st] = *reinterpret_cast<const u32x4*>(krow + (((8 * half + st) ^ (krow_i & 15)) * 16));
-        u32x4 vop[8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int jd = 0; jd < 4; ++jd) vop[4 * u + jd] = v_operand(ldsV, 32 * sub, u, jd, col, half);
-        f32x16 s = {};
-#pragma unroll
-        for (int st = 0; st < 8; ++st) s = mfma32(kop[st], qop[st], s);
-        mask_block<true>(s, base, i_pos, half, g.S, g.R);
-        float mx = s[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        if (__ballot(mx > m + kSlack)) {
-          const float mn = fmaxf(m, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.0f : mn));
-          l *= alpha;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] *= alpha;
-          m = mn;
-        }
-        const float mref = m == kNegInf ? 0.0f : m;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -mref));
-        u32x4 pb[2];
-        pack_probs(s, pb, l);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(vop[4 * u + jd], pb[u], o[jd]);
-      }
-    if (more) {
-      char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-      stage_store<STREAMING>(next_mode, stage, nK, nK + kKBytes);
-    }
+    // Streaming: the staged sink tiles covering [0, min(S, last query + 1)), then the
+    // staged window tiles covering [max(S, first query - R + 1), last query].  A
+    // wavefront computes a tile when some key of it is visible to one of its queries,
+    // masked unless every key is visible to all of them.
+    const int S = g.S, R = g.R;
+    const int64_t qa = a.t0 + q_first, qz = a.t0 + q_last;
+    const int n_sink = static_cast<int>(((S < qz + 1 ? S : qz + 1) + kTileKeys - 1) / kTileKeys);
+    const int64_t lo = qa - R + 1 > S ? qa - R + 1 : S;
+    const int64_t w_first = (a.stage_sink_rows + lo - a.stage_p0) / kTileKeys;
+    const int n_win = lo <= qz ? static_cast<int>((a.stage_sink_rows + qz - a.stage_p0) / kTileKeys - w_first + 1) : 0;
+    const int ntiles = n_sink + n_win;
+    auto tile_row = [&](int ti) -> int64_t {
+      return ti < n_sink ? int64_t(ti) * kTileKeys : (w_first + (ti - n_sink)) * kTileKeys;
+    };
+    const bool live = q_first + 32 * wave <= q_last;  // the wavefront has queries
+    if (ntiles > 0) tile_dma(a.stage, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
     __syncthreads();
-  }
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
+      if (ti + 1 < ntiles) {  // the next tile is in flight during the compute
+        char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
+        tile_dma(a.stage, cache, tile_row(ti + 1), nK, nK + kKBytes, wave, lane, koff);
+      }
+      const bool sink = ti < n_sink;
+      const int64_t row = tile_row(ti);
+      const int64_t p = sink ? row : a.stage_p0 + (row - a.stage_sink_rows);  // position of the first key
+      const int64_t p_last = p + kTileKeys - 1;
+      bool any, full;
+      if (sink) {
+        any = p < S && p <= wave_q_hi;
+        full = p_last < S && p_last <= wave_q_lo;
+      } else {
+        any = p_last >= S && p <= wave_q_hi && p_last > wave_q_lo - R;
+        full = p >= S && p_last <= wave_q_lo && p > wave_q_hi - R;
+      }
+      if (live && any)
+        tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !full, [&](f32x16& sc, int off) {
+          if (sink)
+            mask_block<kMaskSink>(sc, p + off, i_pos, half, S, R);
+          else
+            mask_block<kMaskWindow>(sc, p + off, i_pos, half, S, R);
+        });
+      __syncthreads();
+    }
   }
 
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
@@ -683,42 +515,124 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   }
 }
 
-}  // namespace
+// Streaming heads: the keys one launch of queries (chunk rows [q0, q0 + nq), positions
+// [u0, u_end)) may see, written into the staging region in the cache layout (MFMA-ordered
+// K tiles, d-major V) so that the attention kernel moves them to LDS with the same
+// direct loads as retrieval keys.  Rows of one streaming cache's staging region:
+//   [0, Sp)                 sink position = row, for row < S,
+//   [Sp, Sp + W + n)        window position p0 + (row - Sp), p0 = u0 - W (W >= R - 1),
+// each copied from the chunk input (position >= t0) or from the constant-length cache
+// as it stood before the chunk (a sink, or one of the last R positions before t0).
+// Rows that no query of the launch may see hold zeros (finite values, weighted by zero).
+//
+// One workgroup per 64 rows of one cache: row-major 16-byte loads (16 lanes per 256-byte
+// row) into LDS, then every store instruction of a wavefront writes one contiguous KB of
+// the cache layout (a 1 KB block of a K tile, or 64 dims x 8 keys of a V block).
+constexpr int kStageRows = 64;
 
-static hipError_t launch_prefill_kind(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
-                                      void* out, int T, int64_t t0, int streaming, int nsplit, float* scratch,
-                                      int* counters, hipStream_t st) {
-  PrefillArgs a;
-  a.g = g;
-  a.lv = lv;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.out = static_cast<uint16_t*>(out);
-  a.T = T;
-  a.t0 = t0;
-  a.streaming = streaming;
-  a.n_heads = (streaming ? lv.n_str : lv.n_ret) * g.G;
-  a.n_qblocks = (T + kQRows - 1) / kQRows;
-  a.nsplit = nsplit;
-  a.scratch = scratch;
-  a.counters = counters;
-  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks * nsplit;
-  if (blocks == 0) return hipSuccess;
-  const unsigned lds = 2 * (kKBytes + kVBytes);
-  if (streaming)
-    launch(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
-  else
-    launch(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, st, a);
-  return hipGetLastError();
+__global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, CacheRegion stage,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int T, int64_t t0,
+                                                         int64_t u_end, int sink_rows, int64_t p0) {
+  __shared__ __attribute__((aligned(16))) uint4 s_k[kStageRows][16];  // chunk c of row r at [r][c ^ (r & 15)]
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kStageRows][128];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;  // b * n_str + streaming index
+  const int b = cache / lv.n_str;
+  const int kvh = lv.str_kv[cache % lv.n_str];
+  const int64_t row0 = int64_t(blockIdx.x) * kStageRows;
+  const CacheRegion& ring = lv.str;
+  const uint16_t* rk = reinterpret_cast<const uint16_t*>(ring.k);
+  const uint16_t* rv = reinterpret_cast<const uint16_t*>(ring.v);
+  const int ch = tid & 15;
+  const int64_t in0 = int64_t(b) * T * g.Hkv + kvh;  // input row of chunk token t: in0 + t * Hkv
+  const uint16_t* kin = k + in0 * 128 + 8 * ch;      // input token 0 of this head, chunk ch
+  const uint16_t* vin = v + in0 * 128 + 8 * ch;
+
+  // Source of each of the thread's 4 rows: 1 = chunk input, 2 = constant-length cache,
+  // 0 = none.  The loads are issued unconditionally from select-chosen addresses (a row
+  // without a source reads input token 0 and discards it), all in flight together.
+  int src[4], rr[4];
+  int64_t slot[4];
+  uint4 kr[4], vr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    rr[u] = (tid >> 4) + 16 * u;
+    const int64_t row = row0 + rr[u];
+    const bool sink = row < sink_rows;
+    const int64_t pos = sink ? row : p0 + (row - sink_rows);
+    const bool wanted = pos < u_end && (sink ? pos < g.S : pos >= g.S);
+    src[u] = !wanted ? 0 : (pos >= t0 ? 1 : ((sink || pos >= t0 - g.R) ? 2 : 0));  // ring: sinks, last R before t0
+    slot[u] = src[u] == 2 ? stream_slot(pos, g.S, g.R) : 0;
+    const int64_t tin = src[u] == 1 ? pos - t0 : 0;
+    const uint16_t* kp = src[u] == 2 ? rk + k_chunk_tiled(int64_t(cache) * ring.rows + slot[u], ch)
+                                     : kin + tin * g.Hkv * 128;
+    kr[u] = *reinterpret_cast<const uint4*>(kp);
+    vr[u] = *reinterpret_cast<const uint4*>(vin + tin * g.Hkv * 128);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (src[u] == 0) kr[u] = make_uint4(0, 0, 0, 0);
+    if (src[u] != 1) vr[u] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (src[u] == 2) {  // V of a cache-held row: eight 2-byte elements of the cache's d-major blocks
+      uint16_t x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = rv[v_index(cache, ring.rows, slot[u], 128, 8 * ch + e)];
+      vr[u] = make_uint4(uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16),
+                         uint32_t(x[4]) | (uint32_t(x[5]) << 16), uint32_t(x[6]) | (uint32_t(x[7]) << 16));
+    }
+    s_k[rr[u]][ch ^ (rr[u] & 15)] = kr[u];
+    *reinterpret_cast<uint4*>(&s_v[rr[u]][8 * ch]) = vr[u];
+  }
+  __syncthreads();
+
+  // K: 16 blocks of 1 KB (two 32-key tiles); block 8 q + 4 t + s, lane (grp, r) holds
+  // dims 8 (4 grp + s) .. +7 of key 32 q + 8 (r >> 2) + (r & 3) + 4 t.
+  uint16_t* sk = reinterpret_cast<uint16_t*>(stage.k) + ((int64_t(cache) * stage.rows + row0) >> 5) * 4096;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int blk = 4 * u + wave;
+    const int r = lane & 15, c = 4 * (lane >> 4) + (blk & 3);
+    const int key = 32 * (blk >> 3) + 8 * (r >> 2) + (r & 3) + 4 * ((blk >> 2) & 1);
+    *reinterpret_cast<uint4*>(sk + (blk * 64 + lane) * 8) = s_k[key][c ^ (key & 15)];
+  }
+  // V: 8 blocks of 8 keys x 128 dims; unit (block b8, dim d) = keys 8 b8 .. +7 of dim d.
+  uint16_t* sv = reinterpret_cast<uint16_t*>(stage.v) + (int64_t(cache) * stage.rows + row0) * 128;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u;
+    const int b8 = idx >> 7, d = idx & 127;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = uint32_t(s_v[8 * b8 + 2 * j][d]) | (uint32_t(s_v[8 * b8 + 2 * j + 1][d]) << 16);
+    *reinterpret_cast<uint4*>(sv + (8 * b8) * 128 + d * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
+
+}  // namespace
 
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T, int64_t t0,
                                float* scratch, int64_t scratch_floats, int* counters, int num_cu, hipStream_t st) {
+  PrefillArgs a = {};
+  a.g = g;
+  a.lv = lv;
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.T = T;
+  a.t0 = t0;
+  a.q0 = 0;
+  a.nq = T;
+  a.n_heads = lv.n_ret * g.G;
+  a.n_qblocks = (T + kQRows - 1) / kQRows;
   // Split a query block's keys over two workgroups when the grid alone would leave
   // fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own MFMA,
   // LDS and barrier latencies) and the keys and scratch allow it.
-  const int64_t pairs = int64_t(g.B) * lv.n_ret * g.G * ((T + kQRows - 1) / kQRows);
+  const int64_t pairs = int64_t(g.B) * a.n_heads * a.n_qblocks;
   int nsplit = 1;
   if (pairs < 2 * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
       pairs * 2 * kSlotFloats <= scratch_floats)
@@ -727,12 +641,49 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
     const int f = std::atoi(e);
     if (f == 1 || (f == 2 && pairs <= kPrefillCounters && pairs * 2 * kSlotFloats <= scratch_floats)) nsplit = f;
   }
-  return launch_prefill_kind(g, lv, q, nullptr, nullptr, out, T, t0, 0, nsplit, scratch, counters, st);
+  a.nsplit = nsplit;
+  a.scratch = scratch;
+  a.counters = counters;
+  const int64_t blocks = pairs * nsplit;
+  if (blocks == 0) return hipSuccess;
+  launch(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  return hipGetLastError();
 }
 
-hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
-                                      void* out, int T, int64_t t0, hipStream_t st) {
-  return launch_prefill_kind(g, lv, q, k, v, out, T, t0, 1, 1, nullptr, nullptr, st);
+hipError_t launch_stage_streaming(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
+                                  const void* v, int T, int64_t t0, int q0, int nq, hipStream_t st) {
+  const int caches = g.B * lv.n_str;
+  if (caches == 0 || nq <= 0) return hipSuccess;
+  const int sink_rows = stage_sink_rows(g.S), window_rows = stage_window_rows(g.R);
+  const int rows_used = sink_rows + window_rows + (nq + kStageRows - 1) / kStageRows * kStageRows;
+  const int64_t u0 = t0 + q0;
+  launch(k_stage_streaming, dim3(static_cast<unsigned>(rows_used / kStageRows), static_cast<unsigned>(caches)),
+         dim3(256), 0, st, g, lv, stage, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), T, t0,
+         u0 + nq, sink_rows, u0 - window_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
+                                      void* out, int T, int64_t t0, int q0, int nq, hipStream_t st) {
+  PrefillArgs a = {};
+  a.g = g;
+  a.lv = lv;
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.T = T;
+  a.t0 = t0;
+  a.q0 = q0;
+  a.nq = nq;
+  a.n_heads = lv.n_str * g.G;
+  a.n_qblocks = (nq + kQRows - 1) / kQRows;
+  a.nsplit = 1;
+  a.stage = stage;
+  a.stage_sink_rows = stage_sink_rows(g.S);
+  a.stage_p0 = t0 + q0 - stage_window_rows(g.R);
+  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks;
+  if (blocks == 0) return hipSuccess;
+  launch(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  return hipGetLastError();
 }
 
 }  // namespace duo

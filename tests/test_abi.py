@@ -73,6 +73,11 @@ def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask
     off = al(off + batch * hq * 2048 * (D + 2) * 4, 256)
     off = al(off + batch * hkv * 4, 256)
     off = al(off + 65536 * 4, 256)
+    if esize == 2 and D == 128 and not int4:  # streaming-head prefill staging, K then V
+        stage_rows = al(S, 64) + al(R - 1, 64) + min(cap, 4096)
+        n_str = max(hkv - int(mask[l].sum()) for l in range(n_layers))
+        for _ in range(2):
+            off = al(off + batch * n_str * stage_rows * D * 2, 256)
     return off
 
 

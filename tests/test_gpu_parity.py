@@ -27,6 +27,7 @@ SMALL = {
     "mha_f32_d64_nosink": W("mha_f32_d64_nosink", 15, 2, 2, 64, "f32", 0, 1, 70, 5, 1),
     "all_streaming_bf16": W("all_streaming_bf16", 16, 4, 2, 128, "bf16", 16, 48, 400, 6, 0),
     "all_retrieval_bf16": W("all_retrieval_bf16", 17, 4, 2, 128, "bf16", 16, 48, 400, 6, 2),
+    "nosink_r1_bf16": W("nosink_r1_bf16", 18, 8, 4, 128, "bf16", 0, 1, 300, 5, 1),
 }
 CHUNKS = {
     "mha_bf16": [100, 156, 1, 300],
@@ -36,6 +37,7 @@ CHUNKS = {
     "mha_f32_d64_nosink": [70],
     "all_streaming_bf16": [40, 360],
     "all_retrieval_bf16": [400],
+    "nosink_r1_bf16": [37, 263],
 }
 
 
@@ -361,3 +363,29 @@ def test_growing_scores_exercise_the_rescale(torch_cuda, monkeypatch, split):
     L = sum(chunks)
     compare("ramp prefill", to_f64(torch.cat(pre, 0)), ref[:L], TOL["bf16"])
     compare("ramp decode", to_f64(torch.stack(dec, 0)), ref[L:], TOL["bf16"])
+
+
+@pytest.mark.parametrize("chunks", [[350, 4550], [4900]])
+def test_streaming_prefill_over_several_staged_launches(torch_cuda, chunks):
+    """A chunk longer than one staged launch (4096 queries) of the streaming heads: the
+    second launch's window starts inside the first launch's queries (and, for the later
+    chunk, reaches back into the constant-length cache).  Every streaming-head output is
+    checked; retrieval heads on 96 sampled rows plus the launch boundary."""
+    w = W("long_chunk", 41, 8, 4, 128, "bf16", 4, 300, sum(chunks), 2, 1)
+    say(f"staged streaming prefill chunks={chunks}")
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    L = sum(chunks)
+    G = w.group
+    mask = w.mask(0)
+    str_heads = [h for h in range(w.n_q_heads) if not mask[h // G]]
+    ret_heads = [h for h in range(w.n_q_heads) if mask[h // G]]
+    ref = oracle_rows(w, 0, np.arange(L), total, heads=str_heads)
+    compare("staged streaming prefill (all rows)", to_f64(pre)[:, str_heads], ref[:, str_heads], TOL["bf16"])
+    boundary = chunks[0] + 4096 if len(chunks) > 1 else 4096
+    rows = np.unique(np.concatenate([np.random.default_rng(5).integers(0, L, 96),
+                                     np.arange(boundary - 4, boundary + 4)]))
+    ref_r = oracle_rows(w, 0, rows, total, heads=ret_heads)
+    compare("staged prefill retrieval heads (sampled)", to_f64(pre[rows])[:, ret_heads], ref_r[:, ret_heads],
+            TOL["bf16"])
+    ref_d = oracle_rows(w, 0, np.arange(L, total), total)
+    compare("decode after staged prefill", to_f64(dec), ref_d, TOL["bf16"])
