@@ -42,7 +42,7 @@ KERNEL_SOURCES = {
     "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
     "prefill_retrieval_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "prefill_streaming_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
-    "prefill_streaming_staging": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "prefill_chunk_tiles": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -113,16 +113,19 @@ def prefill_flops(w, t0, T, retrieval=True):
 STAGE_TOKENS = 4096  # queries per streaming-head prefill launch (the library's staging capacity)
 
 
-def stage_bytes(w, t0, T):
-    """Algorithmic HBM bytes of staging the streaming-head keys of one prefill chunk
-    [t0, t0+T), per launch of at most STAGE_TOKENS queries: the rows written (sink rows,
-    window rows from R-1 positions before the first query, the queries' own rows, each
-    rounded up to 64) plus the K+V rows read (sinks and window positions that hold a key)."""
+def chunk_tile_bytes(w, t0, T):
+    """Algorithmic HBM bytes of the chunk-tile launches of one prefill chunk [t0, t0+T):
+    the chunk's K+V rows read and written once per retrieval KV head (the append), and
+    per streaming KV head and launch of at most STAGE_TOKENS queries the staged rows
+    written (sink rows, window rows from R-1 positions before the first query, the
+    queries' own rows, each rounded up to 64) plus the K+V rows read (sinks and window
+    positions that hold a key)."""
     al = lambda x: (x + 63) // 64 * 64
-    ns = w.n_kv_heads - int(w.mask(0).sum())
+    nr = int(w.mask(0).sum())
+    ns = w.n_kv_heads - nr
     vec = 2 * w.head_dim * esize(w)  # K + V of one row
     sp, win = al(w.sink), al(w.recent - 1)
-    total = 0
+    total = nr * vec * 2 * T
     tc = min(STAGE_TOKENS, al(w.max_context))
     for q0 in range(0, T, tc):
         nq = min(tc, T - q0)
@@ -240,7 +243,7 @@ def run(args):
     for T in chunks:
         fl_r += prefill_flops(w, t, T, True)
         fl_s += prefill_flops(w, t, T, False)
-        st_bytes += stage_bytes(w, t, T)
+        st_bytes += chunk_tile_bytes(w, t, T)
         t += T
 
     rooflines = []
@@ -268,7 +271,7 @@ def run(args):
                           "traffic": None})
     if totals["prefill_stage"][1]:
         a = st_bytes / (stage_ms * 1e-3) / 1e9
-        rooflines.append({"kernel": "prefill_streaming_staging", "bound": "hbm", "achieved": round(a, 1),
+        rooflines.append({"kernel": "prefill_chunk_tiles", "bound": "hbm", "achieved": round(a, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
                           "avg_launch_us": round(stage_ms * 1e3 / totals["prefill_stage"][1] * args.steps, 2),
                           "ms_per_step": round(stage_ms, 4), "traffic": None})
@@ -276,12 +279,12 @@ def run(args):
         r["traffic"] = measured_traffic(r["kernel"], w.name)
     dominant = max(rooflines, key=lambda r: r["ms_per_step"]) if rooflines else None
 
-    # append launches: two per prefill chunk (retrieval caches first, streaming caches
-    # last); a decode step appends inside its attention launch on the MFMA path, or in
-    # one extra launch otherwise
+    # append launches: one per prefill chunk (the streaming caches, last; on the MFMA path
+    # the retrieval rows go in with the chunk-tile launch); a decode step appends inside
+    # its attention launch on the MFMA path, or in one extra launch otherwise
     n_app = totals["append"][1] / args.steps
     per_app = app_ms / n_app if n_app else 0.0
-    pre_app = min(n_app, 2 * len(chunks))
+    pre_app = min(n_app, len(chunks))
     dec_app_launches = max(0.0, n_app - pre_app) / w.decode_steps
     prefill_ms = pre_r_ms + pre_s_ms + stage_ms + per_app * pre_app
     res = {
@@ -490,7 +493,7 @@ def cpu_baseline(w, total, budget_s):
 PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
                     "prefill_retrieval_attention": ["k_prefill_mfma<false>"],
                     "prefill_streaming_attention": ["k_prefill_mfma<true>"],
-                    "prefill_streaming_staging": ["k_stage_streaming"]}
+                    "prefill_chunk_tiles": ["k_chunk_tiles"]}
 
 
 def _csvs(d, suffix):

@@ -27,7 +27,7 @@ extern "C" {
 #define DUO_KERNEL_PREFILL_RETRIEVAL  1  /* causal prefill attention, retrieval heads */
 #define DUO_KERNEL_PREFILL_STREAMING  2  /* sink + window prefill attention, streaming heads */
 #define DUO_KERNEL_DECODE             3  /* split-K decode attention with merge, all heads */
-#define DUO_KERNEL_PREFILL_STAGE      4  /* streaming-head keys staged for prefill attention */
+#define DUO_KERNEL_PREFILL_STAGE      4  /* prefill chunk into retrieval caches + streaming staging */
 #define DUO_KERNEL_CLASSES            5
 
 /* on != 0 starts recording, on == 0 stops (recorded events stay until collected). */

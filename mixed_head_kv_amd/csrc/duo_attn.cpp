@@ -418,29 +418,29 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
   hipStream_t st = as_stream(hip_stream);
   hipError_t e;
   if (h->use_mfma) {
-    // retrieval caches take the chunk first (the retrieval kernel reads keys from the
-    // cache); the streaming kernel reads the streaming caches as they stood before the
-    // chunk, which are updated last.
+    // One launch writes the chunk into the retrieval caches (the retrieval kernel reads
+    // its keys there) and stages the keys of the first streaming-head queries; the
+    // streaming caches, read as they stood before the chunk, are updated last.
+    const int nq0 = lv.n_str > 0 ? (n_tokens < h->stage_tokens ? n_tokens : h->stage_tokens) : 0;
     {
-      KernelMark m(h, DUO_KERNEL_APPEND, st);
-      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 1, st);
+      KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
+      e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, true, 0, nq0, st);
     }
-    if (e != hipSuccess) return hip_fail(e, "prefill append (retrieval)");
+    if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
     {
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
       e = duo::launch_prefill_mfma(h->geom, lv, q, out, n_tokens, t0, h->partials, h->partial_floats,
                                    h->prefill_counters, h->num_cu, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill attention (retrieval)");
-    // streaming heads, at most stage_tokens queries per launch pair: their keys are
-    // staged in the cache layout, then attended
-    for (int q0 = 0; lv.n_str > 0 && q0 < n_tokens; q0 += h->stage_tokens) {
+    // streaming heads, at most stage_tokens queries per launch (the staging capacity)
+    for (int q0 = 0; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
       const int nq = n_tokens - q0 < h->stage_tokens ? n_tokens - q0 : h->stage_tokens;
-      {
+      if (q0 > 0) {
         KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
-        e = duo::launch_stage_streaming(h->geom, lv, h->stage, k, v, n_tokens, t0, q0, nq, st);
+        e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, false, q0, nq, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
       }
-      if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
       {
         KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
         e = duo::launch_prefill_stream_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, q0, nq, st);
@@ -449,7 +449,7 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
     }
     {
       KernelMark m(h, DUO_KERNEL_APPEND, st);
-      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 2, st);
+      e = duo::launch_stream_cache_update(h->geom, lv, k, v, n_tokens, t0, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill append (streaming)");
   } else {

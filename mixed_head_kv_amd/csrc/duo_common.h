@@ -158,6 +158,23 @@ __device__ inline float cache_v(const CacheRegion& c, int64_t cache, int64_t row
   }
 }
 
+// Source token of destination row `row` for a bf16 append, with the ring position
+// precomputed on the host: ring_lo = max(t0, S, t0 + T - R) is the first chunk
+// position that survives in the ring, ring_have = (ring_lo - S) mod R its ring index.
+__host__ __device__ inline int source_token_fast(bool streaming, int64_t row, int64_t t0, int T, int S, int R,
+                                        int64_t ring_lo, int ring_have) {
+  if (!streaming || row < S) {
+    if (streaming && row >= S + R) return -1;
+    const int64_t t = row - t0;
+    return (t >= 0 && t < T) ? static_cast<int>(t) : -1;
+  }
+  if (row >= S + R || ring_lo >= t0 + T) return -1;
+  int d = static_cast<int>(row - S) - ring_have;
+  if (d < 0) d += R;
+  const int64_t p = ring_lo + d;
+  return p < t0 + T ? static_cast<int>(p - t0) : -1;
+}
+
 // Streaming-head prefill staging (one region per streaming cache, shared by the layers):
 // sink rows [0, Sp), then window rows covering the W positions before a launch's first
 // query (W >= R - 1, so every window key of its queries is there) and its queries.

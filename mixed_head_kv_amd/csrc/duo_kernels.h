@@ -50,15 +50,24 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
                                int64_t t0, float* scratch, int64_t scratch_floats, int* counters, int num_cu,
                                hipStream_t st);
 
-// Streaming-head prefill on bf16 MFMA (D = 128), one launch pair per at most
-// kStageTokens queries (chunk rows [q0, q0 + nq)): launch_stage_streaming copies the
-// keys those queries may see (sinks, and the window from R - 1 positions before q0 on)
-// into `stage`, from the chunk inputs and from the streaming caches as they stood before
-// the chunk; launch_prefill_stream_mfma then runs the sink + window attention over them.
-// `stage` holds at least stage_sink_rows(S) + stage_window_rows(R) + nq rounded up to a
-// multiple of 64 rows per streaming cache, in the cache layout.
-hipError_t launch_stage_streaming(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
-                                  const void* v, int T, int64_t t0, int q0, int nq, hipStream_t st);
+// Chunk keys into the layouts the MFMA prefill loads directly (bf16, D = 128), one
+// launch: with `retrieval`, rows [t0, t0 + T) of every retrieval cache (the append);
+// with nq > 0, the keys that the streaming-head queries of chunk rows [q0, q0 + nq) may
+// see (sinks, and the window from R - 1 positions before q0 on), from the chunk inputs
+// and from the streaming caches as they stood before the chunk, into `stage`.  `stage`
+// holds at least stage_sink_rows(S) + stage_window_rows(R) + nq rounded up to a multiple
+// of 64 rows per streaming cache, in the cache layout.
+hipError_t launch_chunk_tiles(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
+                              const void* v, int T, int64_t t0, bool retrieval, int q0, int nq, hipStream_t st);
+
+// The chunk's tokens into the streaming (constant-length) caches, bf16 with D = 128:
+// sinks and the last R positions, the rest kept; the same result as launch_append with
+// which = 2, through the coalesced tile writer.
+hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const void* k, const void* v, int T,
+                                      int64_t t0, hipStream_t st);
+
+// Streaming-head (sink + window) prefill on bf16 MFMA (D = 128) of the queries in chunk
+// rows [q0, q0 + nq) (at most kStageTokens), over the keys staged by launch_chunk_tiles.
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);
 

@@ -10,6 +10,8 @@
 namespace duo {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Source token (index into the chunk) that lands in destination row `row`, or -1.
 // Retrieval rows are absolute positions.  Streaming slot s < S holds sink position s;
 // a ring slot holds the unique position p >= S with p = S + (s - S) mod R that is
@@ -85,23 +87,6 @@ __global__ void __launch_bounds__(256) k_append(Geom g, LayerView lv, const T* _
   }
 }
 
-// Source token of destination row `row` for a bf16 append, with the ring position
-// precomputed on the host: ring_lo = max(t0, S, t0 + T - R) is the first chunk
-// position that survives in the ring, ring_have = (ring_lo - S) mod R its ring index.
-__device__ inline int source_token_fast(bool streaming, int64_t row, int64_t t0, int T, int S, int R,
-                                        int64_t ring_lo, int ring_have) {
-  if (!streaming || row < S) {
-    if (streaming && row >= S + R) return -1;
-    const int64_t t = row - t0;
-    return (t >= 0 && t < T) ? static_cast<int>(t) : -1;
-  }
-  if (row >= S + R || ring_lo >= t0 + T) return -1;
-  int d = static_cast<int>(row - S) - ring_have;
-  if (d < 0) d += R;
-  const int64_t p = ring_lo + d;
-  return p < t0 + T ? static_cast<int>(p - t0) : -1;
-}
-
 // bf16 append, one thread per (8-row tile, 8-dim chunk): eight 16-byte K row pieces are
 // copied as they are, and the 8x8 block of V is transposed in registers (byte
 // permutes) into eight 16-byte runs of the d-major tile layout.  Tiles with rows that
@@ -137,18 +122,26 @@ __global__ void __launch_bounds__(256) k_append_bf16(Geom g, LayerView lv, const
   }
   if (nvalid == 0) return;
   const int64_t in0 = (int64_t(b) * T_) * g.Hkv + kvh;  // input row of token t: in0 + t * Hkv
+  // Every row loads unconditionally (a row without a token reads token 0 and drops it):
+  // loads under a branch whose other side writes the same registers are each waited for
+  // before the next row's, one memory round trip per row.
+  // (The empty asm statements consume the K values where they stand, so the compiler
+  // cannot sink each K load into its row's conditional store.)
+  u32x4 kr[8];
   uint4 vr[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    if (src[r] < 0) {
-      vr[r] = make_uint4(0, 0, 0, 0);
-      continue;
-    }
-    const int64_t off = (in0 + int64_t(src[r]) * g.Hkv) * D + 8 * ch;
-    const int64_t grow = int64_t(cache) * c.rows + row0 + r;
-    *reinterpret_cast<uint4*>(K + (c.k_tiled ? k_chunk_tiled(grow, ch) : grow * D + 8 * ch)) =
-        *reinterpret_cast<const uint4*>(k + off);
+    const int64_t off = (in0 + int64_t(src[r] < 0 ? 0 : src[r]) * g.Hkv) * D + 8 * ch;
+    kr[r] = *reinterpret_cast<const u32x4*>(k + off);
     vr[r] = *reinterpret_cast<const uint4*>(v + off);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(kr[r]));
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (src[r] < 0) continue;
+    const int64_t grow = int64_t(cache) * c.rows + row0 + r;
+    *reinterpret_cast<u32x4*>(K + (c.k_tiled ? k_chunk_tiled(grow, ch) : grow * D + 8 * ch)) = kr[r];
   }
   // V tile: element (row r, dim 8ch + e) goes to tile[8ch + e][r]
   uint16_t* vt = V + (int64_t(cache) * c.rows + row0) * D + 8 * ch * 8;

@@ -515,44 +515,79 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   }
 }
 
-// Streaming heads: the keys one launch of queries (chunk rows [q0, q0 + nq), positions
-// [u0, u_end)) may see, written into the staging region in the cache layout (MFMA-ordered
-// K tiles, d-major V) so that the attention kernel moves them to LDS with the same
-// direct loads as retrieval keys.  Rows of one streaming cache's staging region:
-//   [0, Sp)                 sink position = row, for row < S,
-//   [Sp, Sp + W + n)        window position p0 + (row - Sp), p0 = u0 - W (W >= R - 1),
-// each copied from the chunk input (position >= t0) or from the constant-length cache
-// as it stood before the chunk (a sink, or one of the last R positions before t0).
-// Rows that no query of the launch may see hold zeros (finite values, weighted by zero).
+// Chunk keys into the layouts the attention kernel loads directly (MFMA-ordered K
+// tiles, d-major V), one launch before the attention, two kinds of workgroup:
 //
-// One workgroup per 64 rows of one cache: row-major 16-byte loads (16 lanes per 256-byte
-// row) into LDS, then every store instruction of a wavefront writes one contiguous KB of
-// the cache layout (a 1 KB block of a K tile, or 64 dims x 8 keys of a V block).
+// Retrieval append: rows [t0, t0 + T) of every retrieval cache take the chunk's K/V
+// (hotpaper.ai page, technical approach: retrieval heads keep every token).  Rows of
+// the first and last 64-row tile outside that range are rewritten unchanged: earlier
+// tokens are read back from the cache, rows past the chunk are zero (never written).
+//
+// Streaming cache update (after the chunk's attention): every slot of the constant-length
+// cache that the chunk's tokens reach (a sink, or one of the last R positions) takes its
+// token; the other slots are read back and rewritten unchanged.
+//
+// Streaming staging: the keys one launch of queries (chunk rows [q0, q0 + nq), positions
+// [u0, u_end)) may see, per streaming cache, in a workspace region:
+//   rows [0, Sp)            sink position = row, for row < S,
+//   rows [Sp, Sp + W + n)   window position p0 + (row - Sp), p0 = u0 - W (W >= R - 1),
+// each from the chunk input (position >= t0) or from the constant-length cache as it
+// stood before the chunk (a sink, or one of the last R positions before t0).  Rows no
+// query of the launch may see hold zeros (finite values, weighted by zero).
+//
+// One workgroup per 64 destination rows of one cache: row-major 16-byte loads (16 lanes
+// per 256-byte row) into LDS, then every store instruction of a wavefront writes one
+// contiguous KB of the cache layout (a 1 KB block of a K tile, or 64 dims x 8 keys of a V
+// block).  Storing straight from registers (16 bytes per lane to 64 different lines per
+// instruction) ran at under half the bandwidth.
 constexpr int kStageRows = 64;
 
-__global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, CacheRegion stage,
-                                                         const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v, int T, int64_t t0,
-                                                         int64_t u_end, int sink_rows, int64_t p0) {
+struct ChunkTileArgs {
+  Geom g;
+  LayerView lv;
+  CacheRegion stage;
+  const uint16_t* k;  // chunk inputs [B, T, Hkv, 128]
+  const uint16_t* v;
+  int T;
+  int64_t t0;
+  int ret_caches;     // blockIdx.y < ret_caches: retrieval append of cache y
+  int64_t ret_tile0;  // first 64-row tile holding a chunk row
+  int ret_tiles;
+  int str_mode;       // blockIdx.y >= ret_caches, streaming cache y - ret_caches: 1 staging, 2 update
+  int str_tiles;
+  int64_t ring_lo;    // update: first chunk position kept in the cache (see source_token_fast)
+  int ring_have;      // update: its ring index
+  int64_t u_end;      // staging: end of the launch's query positions
+  int sink_rows;      // staging: Sp
+  int64_t p0;         // staging: position of window row Sp
+};
+
+__global__ void __launch_bounds__(256) k_chunk_tiles(ChunkTileArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_k[kStageRows][16];  // chunk c of row r at [r][c ^ (r & 15)]
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kStageRows][128];
+  const Geom& g = a.g;
+  const bool ret = static_cast<int>(blockIdx.y) < a.ret_caches;
+  if (static_cast<int>(blockIdx.x) >= (ret ? a.ret_tiles : a.str_tiles)) return;  // uniform
+  const bool update = !ret && a.str_mode == 2;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cache = blockIdx.y;  // b * n_str + streaming index
-  const int b = cache / lv.n_str;
-  const int kvh = lv.str_kv[cache % lv.n_str];
-  const int64_t row0 = int64_t(blockIdx.x) * kStageRows;
-  const CacheRegion& ring = lv.str;
-  const uint16_t* rk = reinterpret_cast<const uint16_t*>(ring.k);
-  const uint16_t* rv = reinterpret_cast<const uint16_t*>(ring.v);
+  const int cache = ret ? blockIdx.y : blockIdx.y - a.ret_caches;  // b * n_kind + index
+  const int n_kind = ret ? a.lv.n_ret : a.lv.n_str;
+  const int b = cache / n_kind;
+  const int kvh = ret ? a.lv.ret_kv[cache % n_kind] : a.lv.str_kv[cache % n_kind];
+  const int64_t row0 = (ret ? a.ret_tile0 + blockIdx.x : int64_t(blockIdx.x)) * kStageRows;
+  const CacheRegion& held = ret ? a.lv.ret : a.lv.str;  // rows read back from a cache
+  const CacheRegion& dst = ret ? a.lv.ret : (update ? a.lv.str : a.stage);
+  const uint16_t* hk = reinterpret_cast<const uint16_t*>(held.k);
+  const uint16_t* hv = reinterpret_cast<const uint16_t*>(held.v);
   const int ch = tid & 15;
-  const int64_t in0 = int64_t(b) * T * g.Hkv + kvh;  // input row of chunk token t: in0 + t * Hkv
-  const uint16_t* kin = k + in0 * 128 + 8 * ch;      // input token 0 of this head, chunk ch
-  const uint16_t* vin = v + in0 * 128 + 8 * ch;
+  const int64_t in0 = int64_t(b) * a.T * g.Hkv + kvh;  // input row of chunk token t: in0 + t * Hkv
+  const uint16_t* kin = a.k + in0 * 128 + 8 * ch;      // input token 0 of this head, chunk ch
+  const uint16_t* vin = a.v + in0 * 128 + 8 * ch;
 
-  // Source of each of the thread's 4 rows: 1 = chunk input, 2 = constant-length cache,
+  // Source of each of the thread's 4 rows: 1 = chunk input, 2 = a cache row (`slot`),
   // 0 = none.  The loads are issued unconditionally from select-chosen addresses (a row
-  // without a source reads input token 0 and discards it), all in flight together.
+  // without an input reads input token 0 and discards it), all in flight together.
   int src[4], rr[4];
   int64_t slot[4];
   uint4 kr[4], vr[4];
@@ -560,13 +595,25 @@ __global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, C
   for (int u = 0; u < 4; ++u) {
     rr[u] = (tid >> 4) + 16 * u;
     const int64_t row = row0 + rr[u];
-    const bool sink = row < sink_rows;
-    const int64_t pos = sink ? row : p0 + (row - sink_rows);
-    const bool wanted = pos < u_end && (sink ? pos < g.S : pos >= g.S);
-    src[u] = !wanted ? 0 : (pos >= t0 ? 1 : ((sink || pos >= t0 - g.R) ? 2 : 0));  // ring: sinks, last R before t0
-    slot[u] = src[u] == 2 ? stream_slot(pos, g.S, g.R) : 0;
-    const int64_t tin = src[u] == 1 ? pos - t0 : 0;
-    const uint16_t* kp = src[u] == 2 ? rk + k_chunk_tiled(int64_t(cache) * ring.rows + slot[u], ch)
+    int64_t tin = 0;
+    if (ret) {
+      tin = row - a.t0;
+      src[u] = tin >= 0 ? (tin < a.T ? 1 : 0) : 2;
+      slot[u] = row;
+    } else if (update) {
+      tin = source_token_fast(true, row, a.t0, a.T, g.S, g.R, a.ring_lo, a.ring_have);
+      src[u] = tin >= 0 ? 1 : (row < g.S + g.R ? 2 : 0);
+      slot[u] = row;
+    } else {
+      const bool sink = row < a.sink_rows;
+      const int64_t pos = sink ? row : a.p0 + (row - a.sink_rows);
+      const bool wanted = pos < a.u_end && (sink ? pos < g.S : pos >= g.S);
+      src[u] = !wanted ? 0 : (pos >= a.t0 ? 1 : ((sink || pos >= a.t0 - g.R) ? 2 : 0));  // sinks, last R before t0
+      slot[u] = src[u] == 2 ? stream_slot(pos, g.S, g.R) : 0;
+      tin = pos - a.t0;
+    }
+    if (src[u] != 1) tin = 0;
+    const uint16_t* kp = src[u] == 2 ? hk + k_chunk_tiled(int64_t(cache) * held.rows + slot[u], ch)
                                      : kin + tin * g.Hkv * 128;
     kr[u] = *reinterpret_cast<const uint4*>(kp);
     vr[u] = *reinterpret_cast<const uint4*>(vin + tin * g.Hkv * 128);
@@ -578,10 +625,10 @@ __global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, C
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (src[u] == 2) {  // V of a cache-held row: eight 2-byte elements of the cache's d-major blocks
+    if (src[u] == 2) {  // V of a cache row: eight 2-byte elements of the cache's d-major blocks
       uint16_t x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = rv[v_index(cache, ring.rows, slot[u], 128, 8 * ch + e)];
+      for (int e = 0; e < 8; ++e) x[e] = hv[v_index(cache, held.rows, slot[u], 128, 8 * ch + e)];
       vr[u] = make_uint4(uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16),
                          uint32_t(x[4]) | (uint32_t(x[5]) << 16), uint32_t(x[6]) | (uint32_t(x[7]) << 16));
     }
@@ -592,7 +639,7 @@ __global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, C
 
   // K: 16 blocks of 1 KB (two 32-key tiles); block 8 q + 4 t + s, lane (grp, r) holds
   // dims 8 (4 grp + s) .. +7 of key 32 q + 8 (r >> 2) + (r & 3) + 4 t.
-  uint16_t* sk = reinterpret_cast<uint16_t*>(stage.k) + ((int64_t(cache) * stage.rows + row0) >> 5) * 4096;
+  uint16_t* sk = reinterpret_cast<uint16_t*>(dst.k) + ((int64_t(cache) * dst.rows + row0) >> 5) * 4096;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int blk = 4 * u + wave;
@@ -601,7 +648,7 @@ __global__ void __launch_bounds__(256) k_stage_streaming(Geom g, LayerView lv, C
     *reinterpret_cast<uint4*>(sk + (blk * 64 + lane) * 8) = s_k[key][c ^ (key & 15)];
   }
   // V: 8 blocks of 8 keys x 128 dims; unit (block b8, dim d) = keys 8 b8 .. +7 of dim d.
-  uint16_t* sv = reinterpret_cast<uint16_t*>(stage.v) + (int64_t(cache) * stage.rows + row0) * 128;
+  uint16_t* sv = reinterpret_cast<uint16_t*>(dst.v) + (int64_t(cache) * dst.rows + row0) * 128;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = tid + 256 * u;
@@ -650,16 +697,52 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
   return hipGetLastError();
 }
 
-hipError_t launch_stage_streaming(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
-                                  const void* v, int T, int64_t t0, int q0, int nq, hipStream_t st) {
+hipError_t launch_chunk_tiles(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* k,
+                              const void* v, int T, int64_t t0, bool retrieval, int q0, int nq, hipStream_t st) {
+  ChunkTileArgs a = {};
+  a.g = g;
+  a.lv = lv;
+  a.stage = stage;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.T = T;
+  a.t0 = t0;
+  a.ret_caches = retrieval && T > 0 ? g.B * lv.n_ret : 0;
+  a.ret_tile0 = t0 / kStageRows;
+  a.ret_tiles = static_cast<int>((t0 + T + kStageRows - 1) / kStageRows - a.ret_tile0);
+  const int str_caches = nq > 0 ? g.B * lv.n_str : 0;
+  a.sink_rows = stage_sink_rows(g.S);
+  const int window_rows = stage_window_rows(g.R);
+  a.str_mode = 1;
+  a.str_tiles = str_caches ? (a.sink_rows + window_rows) / kStageRows + (nq + kStageRows - 1) / kStageRows : 0;
+  a.u_end = t0 + q0 + nq;
+  a.p0 = t0 + q0 - window_rows;
+  const int tiles = a.ret_caches && a.ret_tiles > a.str_tiles ? a.ret_tiles : a.str_tiles;
+  if (a.ret_caches + str_caches == 0 || tiles == 0) return hipSuccess;
+  launch(k_chunk_tiles, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(a.ret_caches + str_caches)),
+         dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const void* k, const void* v, int T,
+                                      int64_t t0, hipStream_t st) {
   const int caches = g.B * lv.n_str;
-  if (caches == 0 || nq <= 0) return hipSuccess;
-  const int sink_rows = stage_sink_rows(g.S), window_rows = stage_window_rows(g.R);
-  const int rows_used = sink_rows + window_rows + (nq + kStageRows - 1) / kStageRows * kStageRows;
-  const int64_t u0 = t0 + q0;
-  launch(k_stage_streaming, dim3(static_cast<unsigned>(rows_used / kStageRows), static_cast<unsigned>(caches)),
-         dim3(256), 0, st, g, lv, stage, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), T, t0,
-         u0 + nq, sink_rows, u0 - window_rows);
+  if (caches == 0 || T <= 0) return hipSuccess;
+  ChunkTileArgs a = {};
+  a.g = g;
+  a.lv = lv;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.T = T;
+  a.t0 = t0;
+  a.str_mode = 2;
+  a.str_tiles = static_cast<int>(lv.str.rows / kStageRows);
+  int64_t ring_lo = t0 > g.S ? t0 : g.S;
+  if (ring_lo < t0 + T - g.R) ring_lo = t0 + T - g.R;
+  a.ring_lo = ring_lo;
+  a.ring_have = static_cast<int>((ring_lo - g.S) % g.R);
+  launch(k_chunk_tiles, dim3(static_cast<unsigned>(a.str_tiles), static_cast<unsigned>(caches)), dim3(256), 0, st,
+         a);
   return hipGetLastError();
 }
 

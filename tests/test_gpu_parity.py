@@ -62,12 +62,16 @@ def test_device_synth_matches_host_generator(torch_cuda, dtype):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("via", ["append", "prefill"])
 @pytest.mark.parametrize("name", ["mha_bf16", "gqa_bf16", "mha_f32_d128", "gqa_bf16_d64"])
-def test_append_then_read_is_bit_exact(torch_cuda, name):
+def test_append_then_read_is_bit_exact(torch_cuda, name, via):
+    """Cache contents after the chunks went in through kv_append or through prefill (whose
+    retrieval rows are written by the chunk staging launch, ragged chunk edges included)
+    and a few decode steps (whose append is fused into the decode launch)."""
     w = SMALL[name]
     chunks = CHUNKS[name]
-    say(f"append/read {name} chunks={chunks}")
-    kv, _, _, total = run_layer(w, chunks, 0, append_only_chunks=True)
+    say(f"{via}/read {name} chunks={chunks}")
+    kv, _, _, total = run_layer(w, chunks, 0 if via == "append" else 3, append_only_chunks=via == "append")
     mask = w.mask(0)
     for which, kind in ((0, "k"), (1, "v")):
         hist = host_history(w, 0, kind, total)
