@@ -192,12 +192,17 @@ def test_tiny_workload_exact_config(torch_cuda):
     compare("tiny decode", to_f64(dec), ref[512:], TOL["f32"])
 
 
-def test_outputs_are_bitwise_repeatable(torch_cuda):
+@pytest.mark.parametrize("split", [None, "2"])
+def test_outputs_are_bitwise_repeatable(torch_cuda, monkeypatch, split):
+    """Same inputs, same bits, including when query blocks are split over two workgroups
+    (merged in split order whichever finishes last)."""
+    if split:
+        monkeypatch.setenv("DUO_PREFILL_SPLIT", split)
     w = SMALL["gqa_bf16"]
-    say("repeatability")
-    _, p1, d1, _ = run_layer(w, CHUNKS["gqa_bf16"], 5)
-    _, p2, d2, _ = run_layer(w, CHUNKS["gqa_bf16"], 5)
-    assert torch_cuda.equal(p1, p2) and torch_cuda.equal(d1, d2)
+    say(f"repeatability split={split}")
+    runs = [run_layer(w, CHUNKS["gqa_bf16"], 5) for _ in range(3)]
+    for _, p, d, _ in runs[1:]:
+        assert torch_cuda.equal(runs[0][1], p) and torch_cuda.equal(runs[0][2], d)
 
 
 def test_failed_calls_leave_state_unchanged(torch_cuda):
