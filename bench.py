@@ -40,8 +40,7 @@ def log(*a):
 
 KERNEL_SOURCES = {
     "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
-    "prefill_retrieval_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
-    "prefill_streaming_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "prefill_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "prefill_chunk_tiles": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -238,11 +237,14 @@ def run(args):
 
     # algorithmic work per step
     dec_bytes = sum(decode_bytes(w, t) for t in range(w.context, total))
-    fl_r = fl_s = st_bytes = 0
+    fl_r = fl_s = fl_s_rest = st_bytes = 0
+    tc = min(STAGE_TOKENS, (w.max_context + 63) // 64 * 64)
     t = 0
     for T in chunks:
         fl_r += prefill_flops(w, t, T, True)
         fl_s += prefill_flops(w, t, T, False)
+        # streaming-head queries after the first tc of a chunk run in launches of their own
+        fl_s_rest += prefill_flops(w, t + tc, T - tc, False) if T > tc else 0
         st_bytes += chunk_tile_bytes(w, t, T)
         t += T
 
@@ -254,21 +256,22 @@ def run(args):
                           "avg_launch_us": round(dec_ms * 1e3 / w.decode_steps, 3), "ms_per_step": round(dec_ms, 4),
                           "traffic": None})
     if totals["prefill_retrieval"][1]:
-        fl = fl_r if totals["prefill_streaming"][1] else fl_r + fl_s
+        # one launch per chunk: retrieval heads and (MFMA path: the first tc; fp32 path: all)
+        # streaming-head queries
+        fl = fl_r + fl_s - (fl_s_rest if totals["prefill_streaming"][1] else 0)
         a = fl / (pre_r_ms * 1e-3) / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if w.io_dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
-        rooflines.append({"kernel": "prefill_retrieval_attention", "bound": "mfma", "achieved": round(a, 2),
+        rooflines.append({"kernel": "prefill_attention", "bound": "mfma", "achieved": round(a, 2),
                           "peak": peak, "unit": "TFLOP/s", "frac": round(a / peak, 4),
                           "avg_launch_us": round(pre_r_ms * 1e3 / len(chunks), 2), "ms_per_step": round(pre_r_ms, 4),
                           "traffic": None})
     if totals["prefill_streaming"][1]:
-        a = fl_s / (pre_s_ms * 1e-3) / 1e12
+        a = fl_s_rest / (pre_s_ms * 1e-3) / 1e12
         rooflines.append({"kernel": "prefill_streaming_attention", "bound": "mfma", "achieved": round(a, 2),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
                           "avg_launch_us": round(pre_s_ms * 1e3 / totals["prefill_streaming"][1] * args.steps, 2),
-                          "ms_per_step": round(pre_s_ms, 4),
-                          "traffic": None})
+                          "ms_per_step": round(pre_s_ms, 4), "traffic": None})
     if totals["prefill_stage"][1]:
         a = st_bytes / (stage_ms * 1e-3) / 1e9
         rooflines.append({"kernel": "prefill_chunk_tiles", "bound": "hbm", "achieved": round(a, 1),
@@ -491,8 +494,7 @@ def cpu_baseline(w, total, budget_s):
 # --- rocprofv3 output summaries (host only; no GPU) ---------------------------------
 
 PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
-                    "prefill_retrieval_attention": ["k_prefill_mfma<false>"],
-                    "prefill_streaming_attention": ["k_prefill_mfma<true>"],
+                    "prefill_attention": ["k_prefill_mfma(", "k_prefill_valu"],
                     "prefill_chunk_tiles": ["k_chunk_tiles"]}
 
 

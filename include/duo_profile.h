@@ -24,8 +24,10 @@ extern "C" {
 #endif
 
 #define DUO_KERNEL_APPEND             0  /* fused append / evict (and int4 quantise) */
-#define DUO_KERNEL_PREFILL_RETRIEVAL  1  /* causal prefill attention, retrieval heads */
-#define DUO_KERNEL_PREFILL_STREAMING  2  /* sink + window prefill attention, streaming heads */
+#define DUO_KERNEL_PREFILL_RETRIEVAL  1  /* prefill attention: retrieval heads, and (MFMA path) the
+                                                first 4096 streaming-head queries of a chunk */
+#define DUO_KERNEL_PREFILL_STREAMING  2  /* sink + window prefill attention of further streaming-head
+                                                queries (MFMA path, chunks over 4096 tokens) */
 #define DUO_KERNEL_DECODE             3  /* split-K decode attention with merge, all heads */
 #define DUO_KERNEL_PREFILL_STAGE      4  /* prefill chunk into retrieval caches + streaming staging */
 #define DUO_KERNEL_CLASSES            5

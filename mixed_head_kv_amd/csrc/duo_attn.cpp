@@ -427,20 +427,21 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
       e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, true, 0, nq0, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
-    {
+    {  // retrieval heads and the first staged streaming-head queries, one launch
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
-      e = duo::launch_prefill_mfma(h->geom, lv, q, out, n_tokens, t0, h->partials, h->partial_floats,
+      e = duo::launch_prefill_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,
                                    h->prefill_counters, h->num_cu, st);
     }
-    if (e != hipSuccess) return hip_fail(e, "prefill attention (retrieval)");
-    // streaming heads, at most stage_tokens queries per launch (the staging capacity)
-    for (int q0 = 0; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
+    if (e != hipSuccess) return hip_fail(e, "prefill attention");
+    // further streaming-head queries, at most stage_tokens per launch pair (the staging
+    // capacity)
+    for (int q0 = h->stage_tokens; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
       const int nq = n_tokens - q0 < h->stage_tokens ? n_tokens - q0 : h->stage_tokens;
-      if (q0 > 0) {
+      {
         KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
         e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, false, q0, nq, st);
-        if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
       }
+      if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
       {
         KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
         e = duo::launch_prefill_stream_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, q0, nq, st);

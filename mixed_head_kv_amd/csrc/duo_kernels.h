@@ -41,14 +41,16 @@ hipError_t launch_append(const Geom& g, const LayerView& lv, const void* k, cons
 hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q, const void* k,
                                const void* v, void* out, int T, int64_t t0, hipStream_t st);
 
-// Retrieval-head prefill on bf16 MFMA (D = 128).  Reads keys [0, t0 + T) from the
-// retrieval cache, so the chunk must have been appended to the retrieval caches first.
-// When the grid is small (under two workgroups per CU) each query block's key range is
-// split over two workgroups that merge through `scratch` (fp32 partials, coherent)
-// and `counters` (kPrefillCounters ints, zero between calls).
-hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T,
-                               int64_t t0, float* scratch, int64_t scratch_floats, int* counters, int num_cu,
-                               hipStream_t st);
+// Prefill attention on bf16 MFMA (D = 128), one launch: the retrieval heads (causal,
+// keys [0, t0 + T) read from the retrieval caches, so the chunk must have been appended
+// there first) and the streaming-head queries of chunk rows [0, nq_streaming) over the
+// keys staged by launch_chunk_tiles.  When the retrieval blocks alone are few (under
+// two workgroups per CU) each block's key range is split over two workgroups that merge
+// through `scratch` (fp32 partials, coherent) and `counters` (kPrefillCounters ints,
+// zero between calls).
+hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
+                               int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
+                               int* counters, int num_cu, hipStream_t st);
 
 // Chunk keys into the layouts the MFMA prefill loads directly (bf16, D = 128), one
 // launch: with `retrieval`, rows [t0, t0 + T) of every retrieval cache (the append);
@@ -67,7 +69,8 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
                                       int64_t t0, hipStream_t st);
 
 // Streaming-head (sink + window) prefill on bf16 MFMA (D = 128) of the queries in chunk
-// rows [q0, q0 + nq) (at most kStageTokens), over the keys staged by launch_chunk_tiles.
+// rows [q0, q0 + nq) (at most kStageTokens), over the keys staged by launch_chunk_tiles;
+// for the queries after the first kStageTokens of a chunk.
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);
 

@@ -92,6 +92,16 @@ __device__ inline float max32(const f32x16& a, const f32x16& b) {
   return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
 }
 
+// Workgroups of one head kind in a prefill launch: (sequence, query head, 128-query
+// block, split), longest blocks first.
+struct KindGrid {
+  int n_heads;    // query heads of this kind per sequence
+  int n_qblocks;
+  int nsplit;     // workgroups sharing one query block's key range (1 or 2; retrieval only)
+  int q0, nq;     // queries: chunk rows [q0, q0 + nq)
+  int blocks;     // B * n_heads * n_qblocks * nsplit
+};
+
 struct PrefillArgs {
   Geom g;
   LayerView lv;
@@ -99,12 +109,10 @@ struct PrefillArgs {
   uint16_t* out;        // [B, T, Hq, 128]
   int T;                // tokens of the chunk (row stride of q and out)
   int64_t t0;           // position of chunk row 0
-  int q0, nq;           // this launch's queries: chunk rows [q0, q0 + nq)
-  int n_heads;          // query heads of this kind per sequence
-  int n_qblocks;
-  int nsplit;           // workgroups sharing one query block's key range (1 or 2)
-  float* scratch;       // nsplit > 1: per (block, split) fp32 partial, kSlotFloats each
-  int* counters;        // nsplit > 1: arrival counter per query block
+  KindGrid ret;         // blocks [0, ret.blocks): retrieval heads
+  KindGrid str;         // blocks [ret.blocks, ret.blocks + str.blocks): streaming heads
+  float* scratch;       // split retrieval blocks: per (block, split) fp32 partial, kSlotFloats each
+  int* counters;        // split retrieval blocks: arrival counter per query block
   CacheRegion stage;    // streaming heads: the staged keys, one region per streaming cache
   int stage_sink_rows;  // streaming heads: staged sink rows (before the window rows)
   int64_t stage_p0;     // streaming heads: position held by the first window row
@@ -126,10 +134,9 @@ __device__ inline int o_chunk_offset(int c, int ql) { return (c * kQRows + ql) *
 
 // Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
 // this kind, in KV-head-major order.
-template <bool STREAMING>
-__device__ inline int kind_head(const PrefillArgs& a, int idx, int* kvh) {
+__device__ inline int kind_head(const PrefillArgs& a, bool streaming, int idx, int* kvh) {
   const int G = a.g.G;
-  const int kv = STREAMING ? a.lv.str_kv[idx / G] : a.lv.ret_kv[idx / G];
+  const int kv = streaming ? a.lv.str_kv[idx / G] : a.lv.ret_kv[idx / G];
   *kvh = kv;
   return kv * G + idx % G;
 }
@@ -325,28 +332,33 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   set_priority<0>();
 }
 
-template <bool STREAMING>
+// Retrieval workgroups (long) come first in the grid and streaming ones (short) after,
+// so the streaming work fills the CUs that the retrieval blocks' uneven lengths leave
+// idle towards the end of the launch.
 __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];  // two tile buffers
 
   const Geom& g = a.g;
+  const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
+  const KindGrid& kg = streaming ? a.str : a.ret;
+  const int id = static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0);
   // Longest query blocks first; heads of one block adjacent.
-  const int per_b = a.n_heads * a.n_qblocks * a.nsplit;
-  const int b = blockIdx.x / per_b;
-  const int rem = blockIdx.x % per_b;
-  const int split = rem % a.nsplit;
-  const int hq = rem / a.nsplit;
-  const int qb = a.n_qblocks - 1 - hq / a.n_heads;
-  const int head_idx = hq % a.n_heads;
+  const int per_b = kg.n_heads * kg.n_qblocks * kg.nsplit;
+  const int b = id / per_b;
+  const int rem = id % per_b;
+  const int split = rem % kg.nsplit;
+  const int hq = rem / kg.nsplit;
+  const int qb = kg.n_qblocks - 1 - hq / kg.n_heads;
+  const int head_idx = hq % kg.n_heads;
   int kvh;
-  const int h = kind_head<STREAMING>(a, head_idx, &kvh);
-  const int64_t cache = int64_t(b) * (STREAMING ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
+  const int h = kind_head(a, streaming, head_idx, &kvh);
+  const int64_t cache = int64_t(b) * (streaming ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
-  const int q_first = a.q0 + qb * kQRows;                 // chunk-relative
-  const int q_last = min(q_first + kQRows, a.q0 + a.nq) - 1;
+  const int q_first = kg.q0 + qb * kQRows;                // chunk-relative
+  const int q_last = min(q_first + kQRows, kg.q0 + kg.nq) - 1;
   const int my_q = q_first + 32 * wave + col;             // this lane's query
   const bool q_valid = my_q <= q_last;
   const int64_t i_pos = a.t0 + (q_valid ? my_q : q_last); // absolute position
@@ -374,14 +386,14 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   int koff[4];
   tile_dma_offsets(wave, lane, koff);
 
-  if constexpr (!STREAMING) {
+  if (!streaming) {
     // Retrieval: keys [0, t0 + q_last] of the cache, 64 per tile; a split takes a
     // contiguous share of the tiles (the diagonal ones go to the last split).  The leading
     // tiles hold only keys before the block's first query (visible to every query): they
     // run in a loop with the mask compiled out; the few tiles on the diagonal follow.
     const int64_t all_tiles = (a.t0 + q_last + kTileKeys) / kTileKeys;
-    const int64_t t_begin = all_tiles * split / a.nsplit;
-    const int64_t ntiles = all_tiles * (split + 1) / a.nsplit - t_begin;
+    const int64_t t_begin = all_tiles * split / kg.nsplit;
+    const int64_t ntiles = all_tiles * (split + 1) / kg.nsplit - t_begin;
     const int64_t kb_first = t_begin * kTileKeys;
     const int64_t first_q = a.t0 + q_first;
     int64_t n_inner = first_q >= kb_first + kTileKeys - 1 ? (first_q - (kb_first + kTileKeys - 1)) / kTileKeys + 1 : 0;
@@ -463,14 +475,14 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 
   // normalise and store: lane holds query `col` of its wave, dims 32 jd + 8 j + 4 half + i
   l += __shfl_xor(l, 32);
-  if (a.nsplit > 1) {
+  if (kg.nsplit > 1) {
     // Every split publishes its partial; the last one to arrive merges them all.  A
     // partial is O as float4 chunks [32 dim chunks][128 queries] (a wavefront's lanes
     // cover 512 contiguous bytes per store), then m[128] and l[128], all moved with
     // 16-byte device-coherent buffer accesses.
-    const int pair = (b * a.n_heads + head_idx) * a.n_qblocks + qb;
+    const int pair = (b * kg.n_heads + head_idx) * kg.n_qblocks + qb;
     const int ql = 32 * wave + col;
-    float* mine = a.scratch + (int64_t(pair) * a.nsplit + split) * kSlotFloats;
+    float* mine = a.scratch + (int64_t(pair) * kg.nsplit + split) * kSlotFloats;
     {
       const __amdgpu_buffer_rsrc_t rs = slot_rsrc(mine);
 #pragma unroll
@@ -486,19 +498,19 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, (kQRows * 128 + kQRows + ql) * 4, 0, kCoherent);
       }
     }
-    if (!last_arrival(a.counters + pair, a.nsplit)) return;
+    if (!last_arrival(a.counters + pair, kg.nsplit)) return;
     // Merge in split order whichever split arrived last, so the result is the same bits
     // on every run: L = sum_s w_s l_s, O = sum_s w_s O_s, w_s = 2^(m_s - M), the first
     // term a product and the rest fused multiply-adds.
     float M = m;
-    for (int s2 = 0; s2 < a.nsplit; ++s2) {
+    for (int s2 = 0; s2 < kg.nsplit; ++s2) {
       if (s2 == split) continue;
-      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats);
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
       M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)));
     }
     float L = 0.0f;
     f32x16 acc[4];
-    for (int s2 = 0; s2 < a.nsplit; ++s2) {
+    for (int s2 = 0; s2 < kg.nsplit; ++s2) {
       float ws, ls;  // an empty split has m = -inf: weight 0
       f32x16 os[4];
       if (s2 == split) {
@@ -507,7 +519,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 #pragma unroll
         for (int jd = 0; jd < 4; ++jd) os[jd] = o[jd];
       } else {
-        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * a.nsplit + s2) * kSlotFloats);
+        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
         ws = __builtin_amdgcn_exp2f(
             __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)) - M);
         ls = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + kQRows + ql) * 4, 0, kCoherent));
@@ -699,8 +711,20 @@ __global__ void __launch_bounds__(256) k_chunk_tiles(ChunkTileArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q, void* out, int T, int64_t t0,
-                               float* scratch, int64_t scratch_floats, int* counters, int num_cu, hipStream_t st) {
+// Streaming-head grid of the queries in chunk rows [q0, q0 + nq).
+static KindGrid streaming_grid(const Geom& g, const LayerView& lv, int q0, int nq) {
+  KindGrid k = {};
+  k.n_heads = lv.n_str * g.G;
+  k.n_qblocks = (nq + kQRows - 1) / kQRows;
+  k.nsplit = 1;
+  k.q0 = q0;
+  k.nq = nq;
+  k.blocks = nq > 0 ? g.B * k.n_heads * k.n_qblocks : 0;
+  return k;
+}
+
+static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
+                                void* out, int T, int64_t t0) {
   PrefillArgs a = {};
   a.g = g;
   a.lv = lv;
@@ -708,14 +732,25 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
   a.out = static_cast<uint16_t*>(out);
   a.T = T;
   a.t0 = t0;
-  a.q0 = 0;
-  a.nq = T;
-  a.n_heads = lv.n_ret * g.G;
-  a.n_qblocks = (T + kQRows - 1) / kQRows;
-  // Split a query block's keys over two workgroups when the grid alone would leave
-  // fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own MFMA,
-  // LDS and barrier latencies) and the keys and scratch allow it.
-  const int64_t pairs = int64_t(g.B) * a.n_heads * a.n_qblocks;
+  a.stage = stage;
+  a.stage_sink_rows = stage_sink_rows(g.S);
+  a.ret.nsplit = a.str.nsplit = 1;
+  return a;
+}
+
+hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
+                               int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
+                               int* counters, int num_cu, hipStream_t st) {
+  PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
+  KindGrid& r = a.ret;
+  r.n_heads = lv.n_ret * g.G;
+  r.n_qblocks = (T + kQRows - 1) / kQRows;
+  r.q0 = 0;
+  r.nq = T;
+  // Split a query block's keys over two workgroups when the retrieval blocks alone would
+  // leave fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own
+  // MFMA, LDS and barrier latencies) and the keys and scratch allow it.
+  const int64_t pairs = int64_t(g.B) * r.n_heads * r.n_qblocks;
   int nsplit = 1;
   if (pairs < 2 * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
       pairs * 2 * kSlotFloats <= scratch_floats)
@@ -724,12 +759,15 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const void* q
     const int f = std::atoi(e);
     if (f == 1 || (f == 2 && pairs <= kPrefillCounters && pairs * 2 * kSlotFloats <= scratch_floats)) nsplit = f;
   }
-  a.nsplit = nsplit;
+  r.nsplit = nsplit;
+  r.blocks = static_cast<int>(pairs * nsplit);
   a.scratch = scratch;
   a.counters = counters;
-  const int64_t blocks = pairs * nsplit;
+  a.str = streaming_grid(g, lv, 0, nq_streaming);
+  a.stage_p0 = t0 - stage_window_rows(g.R);
+  const int64_t blocks = int64_t(r.blocks) + a.str.blocks;
   if (blocks == 0) return hipSuccess;
-  launch(k_prefill_mfma<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  launch(k_prefill_mfma, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
   return hipGetLastError();
 }
 
@@ -784,24 +822,11 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
 
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st) {
-  PrefillArgs a = {};
-  a.g = g;
-  a.lv = lv;
-  a.q = static_cast<const uint16_t*>(q);
-  a.out = static_cast<uint16_t*>(out);
-  a.T = T;
-  a.t0 = t0;
-  a.q0 = q0;
-  a.nq = nq;
-  a.n_heads = lv.n_str * g.G;
-  a.n_qblocks = (nq + kQRows - 1) / kQRows;
-  a.nsplit = 1;
-  a.stage = stage;
-  a.stage_sink_rows = stage_sink_rows(g.S);
+  PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
+  a.str = streaming_grid(g, lv, q0, nq);
   a.stage_p0 = t0 + q0 - stage_window_rows(g.R);
-  const int64_t blocks = int64_t(g.B) * a.n_heads * a.n_qblocks;
-  if (blocks == 0) return hipSuccess;
-  launch(k_prefill_mfma<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  if (a.str.blocks == 0) return hipSuccess;
+  launch(k_prefill_mfma, dim3(static_cast<unsigned>(a.str.blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
   return hipGetLastError();
 }
 
