@@ -169,11 +169,17 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
   const uint16_t* k_new = p.k_new ? p.k_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
   const uint16_t* v_new = p.v_new ? p.v_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
+  constexpr int kRing = 2;  // tiles in flight per wavefront
   const bool has_new = new_row >= it.key0 && new_row < it.key1;  // uniform
-  if (has_new) {
-    // The workgroup whose range holds the new row writes it to the cache first and
-    // waits for the stores to land in its XCD's L2 before any of its wavefronts load
-    // the tile: those loads then see the new token like any other row.
+  // The workgroup whose range holds the new row writes it to the cache and waits for the
+  // stores to land in its XCD's L2 before any of its wavefronts loads that row's tile:
+  // the loads then see the new token like any other row.  When the row lies beyond the
+  // tiles of the first ring round (the usual case: it is the last key of the range), the
+  // first round's loads are issued before the write, so the write's latency hides
+  // under theirs instead of delaying this workgroup, which has no slack when the splits
+  // are all full.
+  const bool append_late = has_new && new_row - it.key0 >= int64_t(kStride) * kRing;
+  auto append = [&]() {
     if (threadIdx.x < 128) {
       uint16_t* Kw = reinterpret_cast<uint16_t*>(c.k);
       uint16_t* Vw = reinterpret_cast<uint16_t*>(c.v);
@@ -183,7 +189,8 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+  if (has_new && !append_late) append();
 
   // Q^T operand: column r = query head kvh*G + r (zero beyond G), dims 32g + 8s .. +7.
   u32x4 qop[4];
@@ -204,7 +211,6 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   // Each wavefront takes every kWaves-th 32-key tile of the range and keeps a ring of
   // kRing tiles in flight: the slot just consumed is refilled with the tile kRing
   // rounds ahead (past the range: a bounds-checked load of zeros, no memory traffic).
-  constexpr int kRing = 2;
   const int ntile32 = static_cast<int>((it.key1 - it.key0 + 31) >> 5);
   SplitBuffers sb;
   sb.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K + ((row0 + it.key0) >> 5) * 4096), 0,
@@ -220,6 +226,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   const int n_iter = __builtin_amdgcn_readfirstlane((n_tiles + kRing - 1) / kRing);
 #pragma unroll
   for (int u = 0; u < kRing; ++u) load_tile(ring[u], sb, rel0 + kStride * u, r, grp);
+  if (append_late) append();
   for (int iter = 0; iter < n_iter; ++iter) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
@@ -382,6 +389,45 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
   const int G = g.G;
   const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
 
+  // Fused append of this step's token (retrieval row t or streaming slot new_slot): the
+  // workgroup whose range holds the row quantises K (wavefront 0) and V (wavefront 1)
+  // exactly as the append kernel does and stores codes and (scale, zero) before any of
+  // its wavefronts loads the row's tile (after the first ring round's loads when the row
+  // lies beyond them, as in the bf16 kernel).  V codes share a word with the 7 other rows
+  // of their 8-row block (never split between workgroups: splits are multiples of 64
+  // rows); the token's nibbles go in with device-scope atomics, which bypass the CU's L1,
+  // so the tile loads that follow cannot meet a stale line.
+  constexpr int kRing = 3;  // tiles in flight per wavefront
+  const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
+  const bool has_new = new_row >= it.key0 && new_row < it.key1;  // uniform
+  const bool append_late = has_new && new_row - it.key0 >= int64_t(kStride) * kRing;
+  auto append = [&]() {
+    if (wave < 2) {
+      const uint16_t* src = (wave == 0 ? p.k_new : p.v_new) + (int64_t(it.b) * g.Hkv + it.kvh) * 128 + 2 * lane;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(src);
+      const Q4 qq = quantize_pair(bf16_to_f32(x & 0xffff), bf16_to_f32(x >> 16));
+      const int64_t grow = it.cache * c.rows + new_row;
+      uint16_t* meta = (wave == 0 ? c.k_meta : c.v_meta) + grow * 2;
+      if (wave == 0) {
+        reinterpret_cast<uint8_t*>(c.k)[k_code_byte(grow, lane)] = static_cast<uint8_t>(qq.q0 | (qq.q1 << 4));
+      } else {
+        uint32_t* vw = reinterpret_cast<uint32_t*>(c.v) + (grow & ~int64_t(7)) / 8 * 128 + 2 * lane;
+        const int sh = 4 * static_cast<int>(new_row & 7);
+        __hip_atomic_fetch_and(vw, ~(15u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_and(vw + 1, ~(15u << sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(vw, qq.q0 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(vw + 1, qq.q1 << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) {
+        meta[0] = qq.s_bits;
+        meta[1] = qq.z_bits;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  if (has_new && !append_late) append();
+
   // Q^T operand in the codes' element order; Qsum = sum of the query's 128 values.
   u32x4 qop[4];
   float qsum;
@@ -412,7 +458,6 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
   f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float sl2 = g.scale_log2;
-  constexpr int kRing = 3;
   Tile4 ring[kRing];
   const int64_t first = it.key0 + 32 * wave;
   const int64_t fallback = first < it.key1 ? first : it.key0;  // unconditional loads, as above
@@ -421,6 +466,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
     const int64_t b = first + kStride * u;
     load_tile4(ring[u], c, it.cache, b < it.key1 ? b : fallback, r, grp);
   }
+  if (append_late) append();
   for (int64_t base0 = first; base0 < it.key1; base0 += kStride * kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {

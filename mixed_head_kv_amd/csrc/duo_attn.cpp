@@ -501,8 +501,9 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   const int64_t t = append ? len : len - 1;
   hipError_t e;
   duo::DecodePlan p = make_plan(h, layer, t);
-  if (append && h->use_mfma) {
-    // the MFMA decode appends the token itself (the workgroup covering its row)
+  if (append && h->use_mfma_decode) {
+    // the MFMA decode (bf16 or int4 caches) appends the token itself (the workgroup
+    // covering its row)
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
   } else if (append) {

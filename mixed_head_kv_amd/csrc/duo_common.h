@@ -181,6 +181,46 @@ __host__ __device__ inline int source_token_fast(bool streaming, int64_t row, in
 __host__ __device__ inline int stage_sink_rows(int S) { return (S + kRowAlign - 1) / kRowAlign * kRowAlign; }
 __host__ __device__ inline int stage_window_rows(int R) { return (R - 1 + kRowAlign - 1) / kRowAlign * kRowAlign; }
 
+__device__ inline float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// int4 group-128 quantisation of one vector held two values per lane (d = 2*lane,
+// 2*lane + 1).  Steps and rounding are those of the format: fp32 range, fp32 divide
+// by 15, fp16 round of scale and zero, fp32 (x - z) / s, round half to even, clamp.
+struct Q4 {
+  uint32_t q0, q1;
+  uint16_t s_bits, z_bits;
+};
+__device__ inline Q4 quantize_pair(float x0, float x1) {
+  const float mn = wave_min(fminf(x0, x1));
+  const float mx = wave_max(fmaxf(x0, x1));
+  const float s32 = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+  const __half sh = __float2half_rn(s32);
+  const __half zh = __float2half_rn(mn);
+  const float s = __half2float(sh);
+  const float z = __half2float(zh);
+  Q4 r;
+  r.s_bits = __half_as_ushort(sh);
+  r.z_bits = __half_as_ushort(zh);
+  if (s == 0.0f) {
+    r.q0 = r.q1 = 0;
+  } else {
+    const float a = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x0, z), s)), 0.0f), 15.0f);
+    const float c = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x1, z), s)), 0.0f), 15.0f);
+    r.q0 = static_cast<uint32_t>(a);
+    r.q1 = static_cast<uint32_t>(c);
+  }
+  return r;
+}
+
 // Streaming slot of an absolute position that the constant-length cache holds.
 __host__ __device__ inline int64_t stream_slot(int64_t p, int S, int R) {
   return p < S ? p : S + (p - S) % R;

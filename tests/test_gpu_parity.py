@@ -87,13 +87,17 @@ def test_append_then_read_is_bit_exact(torch_cuda, name, via):
                     assert np.array_equal(got[0], hist[p, g]), (kind, g, p)
 
 
-def test_int4_append_codes_and_dequant_are_bit_exact(torch_cuda):
+@pytest.mark.parametrize("via", ["append", "decode"])
+def test_int4_append_codes_and_dequant_are_bit_exact(torch_cuda, via):
+    """int4 codes, (scale, zero) and dequantised values after kv_append chunks, or after
+    decode steps (which quantise their token inside the decode launch, 8-row V code
+    blocks filled one row per step and the streaming ring wrapped)."""
     w = W("int4", 21, 8, 4, 128, "bf16", 4, 32, 0, 0, 2, fmt="int4")
-    chunks = [3, 50, 8, 1, 100, 9]
-    total = sum(chunks)
-    w = w.scaled(context=total)
-    say(f"int4 append chunks={chunks}")
-    kv, _, _, _ = run_layer(w, chunks, 0, append_only_chunks=True)
+    chunks, steps = ([3, 50, 8, 1, 100, 9], 0) if via == "append" else ([3, 50, 8], 45)
+    total = sum(chunks) + steps
+    w = w.scaled(context=sum(chunks), decode_steps=steps)
+    say(f"int4 {via} chunks={chunks} steps={steps}")
+    kv, _, _, _ = run_layer(w, chunks, steps, append_only_chunks=True)
     mask = w.mask(0)
     for which, kind in ((0, "k"), (1, "v")):
         raw = I.synth(w.seed, 0, kind, 0, total, w.n_kv_heads, 128, "bf16")
