@@ -552,7 +552,7 @@ def summarize_traffic(fetch_dir, write_dir, workload):
             if xs:
                 out[counter][k] = (len(xs), sum(xs) / len(xs))
     try:
-        entries = json.load(open(TRAFFIC_FILE))
+        entries = [e for e in json.load(open(TRAFFIC_FILE)) if e["kernel"] in PROFILED_KERNELS]
     except (OSError, ValueError):
         entries = []
     for k in PROFILED_KERNELS:
