@@ -495,7 +495,7 @@ def cpu_baseline(w, total, budget_s):
 
 PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
                     "prefill_attention": ["k_prefill_mfma(", "k_prefill_valu"],
-                    "prefill_chunk_tiles": ["k_chunk_tiles"]}
+                    "prefill_chunk_tiles": ["k_chunk_tiles<false>"]}
 
 
 def _csvs(d, suffix):

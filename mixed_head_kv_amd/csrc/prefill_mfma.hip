@@ -601,7 +601,6 @@ struct ChunkTileArgs {
   int ret_caches;     // blockIdx.y < ret_caches: retrieval append of cache y
   int64_t ret_tile0;  // first 64-row tile holding a chunk row
   int ret_tiles;
-  int str_mode;       // blockIdx.y >= ret_caches, streaming cache y - ret_caches: 1 staging, 2 update
   int str_tiles;
   int64_t ring_lo;    // update: first chunk position kept in the cache (see source_token_fast)
   int ring_have;      // update: its ring index
@@ -610,13 +609,16 @@ struct ChunkTileArgs {
   int64_t p0;         // staging: position of window row Sp
 };
 
+// UPDATE: the streaming cache update after the attention (its own instantiation, so
+// profiles tell the two uses apart); otherwise the append + staging launch.
+template <bool UPDATE>
 __global__ void __launch_bounds__(256) k_chunk_tiles(ChunkTileArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_k[kStageRows][16];  // chunk c of row r at [r][c ^ (r & 15)]
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kStageRows][128];
   const Geom& g = a.g;
   const bool ret = static_cast<int>(blockIdx.y) < a.ret_caches;
   if (static_cast<int>(blockIdx.x) >= (ret ? a.ret_tiles : a.str_tiles)) return;  // uniform
-  const bool update = !ret && a.str_mode == 2;
+  const bool update = UPDATE && !ret;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cache = ret ? blockIdx.y : blockIdx.y - a.ret_caches;  // b * n_kind + index
@@ -787,13 +789,12 @@ hipError_t launch_chunk_tiles(const Geom& g, const LayerView& lv, const CacheReg
   const int str_caches = nq > 0 ? g.B * lv.n_str : 0;
   a.sink_rows = stage_sink_rows(g.S);
   const int window_rows = stage_window_rows(g.R);
-  a.str_mode = 1;
   a.str_tiles = str_caches ? (a.sink_rows + window_rows) / kStageRows + (nq + kStageRows - 1) / kStageRows : 0;
   a.u_end = t0 + q0 + nq;
   a.p0 = t0 + q0 - window_rows;
   const int tiles = a.ret_caches && a.ret_tiles > a.str_tiles ? a.ret_tiles : a.str_tiles;
   if (a.ret_caches + str_caches == 0 || tiles == 0) return hipSuccess;
-  launch(k_chunk_tiles, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(a.ret_caches + str_caches)),
+  launch(k_chunk_tiles<false>, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(a.ret_caches + str_caches)),
          dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -809,14 +810,13 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
   a.v = static_cast<const uint16_t*>(v);
   a.T = T;
   a.t0 = t0;
-  a.str_mode = 2;
   a.str_tiles = static_cast<int>(lv.str.rows / kStageRows);
   int64_t ring_lo = t0 > g.S ? t0 : g.S;
   if (ring_lo < t0 + T - g.R) ring_lo = t0 + T - g.R;
   a.ring_lo = ring_lo;
   a.ring_have = static_cast<int>((ring_lo - g.S) % g.R);
-  launch(k_chunk_tiles, dim3(static_cast<unsigned>(a.str_tiles), static_cast<unsigned>(caches)), dim3(256), 0, st,
-         a);
+  launch(k_chunk_tiles<true>, dim3(static_cast<unsigned>(a.str_tiles), static_cast<unsigned>(caches)), dim3(256), 0,
+         st, a);
   return hipGetLastError();
 }
 

@@ -402,3 +402,61 @@ def test_streaming_prefill_over_several_staged_launches(torch_cuda, chunks):
             TOL["bf16"])
     ref_d = oracle_rows(w, 0, np.arange(L, total), total)
     compare("decode after staged prefill", to_f64(dec), ref_d, TOL["bf16"])
+
+
+def _batched_run(w, B_, chunks, steps, append_only=False):
+    """Prefill (or append) and decode B_ sequences together; sequence b's data is the
+    workload reseeded with seed + 100 b (the retrieval heads are fixed, so all sequences
+    share one configuration)."""
+    import torch
+    from mixed_head_kv_amd.binding import DuoKV
+    ws = [w.scaled(seed=w.seed + 100 * b) for b in range(B_)]
+    total = sum(chunks) + steps
+    Q = torch.stack([device_synth(x, 0, "q", 0, total) for x in ws])
+    K = torch.stack([device_synth(x, 0, "k", 0, total) for x in ws])
+    V = torch.stack([device_synth(x, 0, "v", 0, total) for x in ws])
+    kv = DuoKV.for_workload(w, batch=B_)
+    pre, t = [], 0
+    for T in chunks:
+        sl = slice(t, t + T)
+        if append_only:
+            kv.append(0, K[:, sl].contiguous(), V[:, sl].contiguous())
+        else:
+            pre.append(kv.prefill(0, Q[:, sl].contiguous(), K[:, sl].contiguous(), V[:, sl].contiguous()))
+        t += T
+    dec = []
+    for _ in range(steps):
+        dec.append(kv.decode(0, Q[:, t].contiguous(), K[:, t].contiguous(), V[:, t].contiguous()))
+        t += 1
+    torch.cuda.synchronize()
+    return ws, kv, (torch.cat(pre, 1) if pre else None), torch.stack(dec, 1), total
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16", "mha_f32_d128", "int4"])
+def test_batched_sequences_match_oracle(torch_cuda, name):
+    """Three sequences in one handle (batch 3): every sequence's prefill and decode
+    outputs and its caches checked against the oracle on that sequence's own data."""
+    if name == "int4":
+        w = W("int4_b", 23, 8, 4, 128, "bf16", 4, 32, 400, 6, 2, fmt="int4", fixed=(0, 3))
+        chunks, append_only = [150, 250], True
+    else:
+        base = SMALL[name]
+        w = base.scaled(fixed_retrieval=tuple(int(g) for g in np.flatnonzero(base.mask(0))))
+        chunks, append_only = CHUNKS[name], False
+    B_ = 3
+    say(f"batched {name} B={B_} chunks={chunks} steps={w.decode_steps}")
+    ws, kv, pre, dec, total = _batched_run(w, B_, chunks, w.decode_steps, append_only)
+    L = sum(chunks)
+    tol = TOL[w.io_dtype]
+    for b, wb in enumerate(ws):
+        ref = oracle_rows(wb, 0, np.arange(0 if pre is not None else L, total), total)
+        if pre is not None:
+            compare(f"batched {name} seq {b} prefill", to_f64(pre[b]), ref[:L], tol)
+            compare(f"batched {name} seq {b} decode", to_f64(dec[b]), ref[L:], tol)
+        else:
+            compare(f"batched {name} seq {b} decode", to_f64(dec[b]), ref, tol)
+        if name != "int4":
+            hist = host_history(wb, 0, "k", total)
+            g = int(np.flatnonzero(wb.mask(0))[0])
+            got = to_f64(kv.read(0, g, 0, 0, total, b=b))
+            assert np.array_equal(got, hist[:, g]), (name, b, "retrieval K cache")
