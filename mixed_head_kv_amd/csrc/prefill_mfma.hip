@@ -190,18 +190,6 @@ __device__ inline u32x4 v_operand(const char* ldsV, int key0, int u, int jd, int
   return *reinterpret_cast<const u32x4*>(ldsV + ((key0 + 16 * u + 8 * half) >> 3) * 2048 + col * 16 + jd * 512);
 }
 
-// Pack 16 probabilities (registers 8u .. 8u+7 form the P^T operand of k-step u) and add
-// them to the row sum (the same bf16 values the product uses).
-__device__ inline void pack_probs(const f32x16& p, u32x4 (&pb)[2], float& l) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    pb[u] = u32x4{pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
-                  pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) l = sum_bf16_pair(pb[u][w], l);
-  }
-}
-
 // Scores of keys a query may not see become -inf, in place.  Register 4j + i of a
 // 32-key block starting at position `base` holds key base + 8 half + c with
 // c = 16(j>>1) + 4(j&1) + i; the query of the lane sits at position i_pos.  Visibility
