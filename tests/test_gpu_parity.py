@@ -432,18 +432,22 @@ def _batched_run(w, B_, chunks, steps, append_only=False):
     return ws, kv, (torch.cat(pre, 1) if pre else None), torch.stack(dec, 1), total
 
 
-@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16", "mha_f32_d128", "int4"])
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16", "mha_f32_d128", "int4", "long_chunk"])
 def test_batched_sequences_match_oracle(torch_cuda, name):
-    """Three sequences in one handle (batch 3): every sequence's prefill and decode
-    outputs and its caches checked against the oracle on that sequence's own data."""
+    """Several sequences in one handle: every sequence's prefill and decode outputs and its
+    caches checked against the oracle on that sequence's own data (long_chunk: two
+    sequences, one chunk of 4600 tokens, so the streaming heads take two staged launches)."""
+    B_ = 3
     if name == "int4":
         w = W("int4_b", 23, 8, 4, 128, "bf16", 4, 32, 400, 6, 2, fmt="int4", fixed=(0, 3))
         chunks, append_only = [150, 250], True
+    elif name == "long_chunk":
+        w = W("long_chunk_b", 42, 8, 4, 128, "bf16", 4, 300, 4600, 2, 1, fixed=(1,))
+        chunks, append_only, B_ = [4600], False, 2
     else:
         base = SMALL[name]
         w = base.scaled(fixed_retrieval=tuple(int(g) for g in np.flatnonzero(base.mask(0))))
         chunks, append_only = CHUNKS[name], False
-    B_ = 3
     say(f"batched {name} B={B_} chunks={chunks} steps={w.decode_steps}")
     ws, kv, pre, dec, total = _batched_run(w, B_, chunks, w.decode_steps, append_only)
     L = sum(chunks)
