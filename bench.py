@@ -135,6 +135,49 @@ def chunk_tile_bytes(w, t0, T):
     return total
 
 
+def workload_for(args):
+    """The named workload, or with --full-attention the same shapes and inputs with every
+    KV head a retrieval head (the full-attention baseline of the same kernels)."""
+    from mixed_head_kv_amd import inputs as I
+    w = I.WORKLOADS[args.workload]
+    if args.full_attention:
+        w = w.scaled(name=w.name + "_full_attention", n_retrieval=w.n_kv_heads, fixed_retrieval=None)
+    return w
+
+
+def capacity(budget_gb):
+    """Largest context (tokens) whose caches fit in `budget_gb` of device memory, per
+    layout, from the library's own workspace arithmetic (duo_kv_bytes; no GPU): the int4
+    32-layer GQA shape with 4 of 8 KV heads retrieval, the same shape in bf16, and both
+    with every head retrieval (full attention)."""
+    import numpy as np
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+    w = I.WORKLOADS["llama3_8b_gqa_32layer_int4_3p3m"]
+    budget = int(budget_gb * 1e9)
+    res = {}
+    for label, fmt, full in (("int4_duo", B.DUO_KV_INT4_G128, False), ("bf16_duo", B.DUO_KV_SAME_AS_IO, False),
+                             ("int4_full", B.DUO_KV_INT4_G128, True), ("bf16_full", B.DUO_KV_SAME_AS_IO, True)):
+        mask = np.ones((w.n_layers, w.n_kv_heads), np.uint8) if full else w.masks().astype(np.uint8)
+
+        def nbytes(ctx):
+            return B.duo_kv_bytes(B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink,
+                                                w.recent, ctx, B.DUO_DTYPE_BF16, fmt, mask))
+        lo, hi = 1, 1 << 40
+        while lo < hi:  # largest ctx with nbytes(ctx) <= budget
+            mid = (lo + hi + 1) // 2
+            if nbytes(mid) <= budget:
+                lo = mid
+            else:
+                hi = mid - 1
+        res[label] = {"max_context": lo, "bytes": nbytes(lo)}
+    res["int4_duo_vs_bf16_full"] = round(res["int4_duo"]["max_context"] / res["bf16_full"]["max_context"], 2)
+    res["bf16_duo_vs_bf16_full"] = round(res["bf16_duo"]["max_context"] / res["bf16_full"]["max_context"], 2)
+    return {"capacity_budget_gb": budget_gb, "layers": w.n_layers, "n_kv_heads": w.n_kv_heads,
+            "retrieval_kv_heads": int(w.mask(0).sum()), "sink": w.sink, "recent": w.recent, **res}
+
+
 def run(args):
     import numpy as np
     import torch
@@ -142,7 +185,7 @@ def run(args):
     from mixed_head_kv_amd import binding as B
     from mixed_head_kv_amd import inputs as I
 
-    w = I.WORKLOADS[args.workload]
+    w = workload_for(args)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     io = B.DUO_DTYPE_F32 if w.io_dtype == "f32" else B.DUO_DTYPE_BF16
@@ -594,7 +637,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--full-attention", action="store_true",
+                    help="every KV head a retrieval head: the full-attention baseline on the same kernels")
+    ap.add_argument("--capacity", type=float, metavar="GB", default=None,
+                    help="print the largest contexts whose caches fit in GB of device memory (no GPU) and exit")
     args = ap.parse_args()
+    if args.capacity is not None:
+        print(json.dumps(capacity(args.capacity)), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)

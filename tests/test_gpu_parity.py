@@ -464,3 +464,27 @@ def test_batched_sequences_match_oracle(torch_cuda, name):
             g = int(np.flatnonzero(wb.mask(0))[0])
             got = to_f64(kv.read(0, g, 0, 0, total, b=b))
             assert np.array_equal(got, hist[:, g]), (name, b, "retrieval K cache")
+
+
+def test_llama2_7b_mha_32k_full_attention_layer(torch_cuda):
+    """The full-attention baseline on the same kernels (all 32 heads retrieval) at the 32K
+    shape: 8 prefill chunks of 4096 and 16 decode steps.  Every decode output is checked;
+    prefill rows are sampled (the first and last 16 rows of every chunk and 16 seeded rows
+    per chunk)."""
+    base = I.WORKLOADS["llama2_7b_mha_32k"]
+    w = base.scaled(name="llama2_7b_mha_32k_full_attention", n_retrieval=base.n_kv_heads, fixed_retrieval=None,
+                    decode_steps=16)
+    assert w.mask(0).all()
+    say("llama2_7b_mha_32k, full attention")
+    chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    rng = np.random.default_rng(2)
+    rows = set()
+    for c in range(len(chunks)):
+        a, b = c * w.prefill_chunk, (c + 1) * w.prefill_chunk
+        rows |= set(range(a, a + 16)) | set(range(b - 16, b)) | set(rng.integers(a, b, 16).tolist())
+    rows = np.array(sorted(rows))
+    ref_dec = oracle_rows(w, 0, np.arange(w.context, total), total)
+    compare("32k full-attention decode", to_f64(dec), ref_dec, TOL["bf16"])
+    ref_pre = oracle_rows(w, 0, rows, total)
+    compare("32k full-attention prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
