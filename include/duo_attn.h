@@ -123,8 +123,10 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
  * sequence; streaming heads to the sinks and the recent window, read from their
  * constant-length cache as it stood before the call plus the chunk itself.  After the
  * call the layer's length is len + T.  int4 caches: DUO_E_UNSUPPORTED (decode-only
- * format in this build).  Errors: DUO_E_INVALID (T <= 0, bad layer, null or
- * misaligned pointer), DUO_E_CAPACITY (len + T > max_context). */
+ * format in this build).  Every sequence of the batch must hold the same length len
+ * (else DUO_E_STATE; duo_prefill_seq fills one sequence).  Errors: DUO_E_INVALID
+ * (T <= 0, bad layer, null or misaligned pointer), DUO_E_CAPACITY
+ * (len + T > max_context). */
 int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v,
                 int32_t n_tokens, void* out, void* hip_stream);
 
@@ -135,19 +137,45 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
 int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, int32_t n_tokens,
                   void* hip_stream);
 
-/* One decoding step of `layer`: appends k_new / v_new (decode layout) at position
- * t = len, then the query q (decode layout) at position t attends to the visible keys
- * (so the new token sees itself), writing out.  If k_new and v_new are both NULL
- * nothing is appended and the query attends at t = len - 1 (its K/V were appended
- * earlier, e.g. by duo_kv_append).  Retrieval heads use split-K flash decoding over
- * the full cache with a log-sum-exp merge; streaming heads read their sink + recent
- * slots.  Errors: DUO_E_INVALID, DUO_E_CAPACITY (append past max_context),
- * DUO_E_STATE (NULL k_new/v_new with an empty layer, or only one of them NULL). */
+/* One decoding step of `layer`: for every sequence b, appends its k_new / v_new row
+ * (decode layout) at position t_b = len_b, the sequence's own length, then its query
+ * (decode layout) at position t_b attends to the visible keys (so the new token sees
+ * itself), writing out.  If k_new and v_new are both NULL nothing is appended and the
+ * queries attend at t_b = len_b - 1 (their K/V were appended earlier, e.g. by
+ * duo_kv_append).  The lengths may differ between sequences (filled with the
+ * per-sequence calls below) when batch <= 32.  Retrieval heads use split-K flash
+ * decoding over the full cache with a log-sum-exp merge; streaming heads read their
+ * sink + recent slots.  Errors: DUO_E_INVALID, DUO_E_CAPACITY (append past
+ * max_context), DUO_E_STATE (NULL k_new/v_new with an empty sequence, or only one of
+ * them NULL), DUO_E_UNSUPPORTED (lengths that differ with batch > 32). */
 int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new,
                void* out, void* hip_stream);
 
-/* Tokens currently held for `layer` (the position of the next appended token). */
+/* Tokens currently held for `layer` (the position of the next appended token) when
+ * every sequence holds the same number; DUO_E_STATE when they differ. */
 int duo_kv_length(const duo_handle* h, int32_t layer, int64_t* out_len);
+
+/* ---- Per-sequence calls ------------------------------------------------------- */
+/* The sequences of a batch are independent requests, each with its own caches and
+ * length; decoding with the dual caches is what lets a GPU hold many long contexts
+ * at once (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with
+ * Retrieval and Streaming Heads", abstract and main results: decoding memory and the
+ * context one GPU serves).  These calls act on sequence `seq` (0 <= seq < batch)
+ * alone, so that the sequences of a batch can hold different lengths; duo_decode then
+ * serves them all in one step.  The pointers are one sequence's tensors: the layouts
+ * above with B = 1.  Errors as the batch calls, and DUO_E_INVALID for seq out of
+ * range.  Calls on one handle are ordered by the caller's stream. */
+
+/* duo_prefill of sequence `seq` alone, at positions len_seq .. len_seq + T - 1. */
+int duo_prefill_seq(duo_handle* h, int32_t layer, int32_t seq, const void* q, const void* k,
+                    const void* v, int32_t n_tokens, void* out, void* hip_stream);
+
+/* duo_kv_append of sequence `seq` alone (int4 caches quantise on the way in). */
+int duo_kv_append_seq(duo_handle* h, int32_t layer, int32_t seq, const void* k, const void* v,
+                      int32_t n_tokens, void* hip_stream);
+
+/* Tokens currently held by sequence `seq` of `layer`. */
+int duo_kv_length_seq(const duo_handle* h, int32_t layer, int32_t seq, int64_t* out_len);
 
 /* Free the host handle (the workspace stays the caller's).  NULL is allowed. */
 void duo_kv_free(duo_handle* h);
@@ -160,8 +188,9 @@ const char* duo_last_error(void);
 /* Copy the stored K (which = 0) or V (which = 1) vectors of one sequence `b`, KV head
  * `kv_head` of `layer`, for absolute positions pos0 .. pos0+n-1, into d_out
  * ([n, head_dim] float32, device), dequantised for int4 caches with the same device
- * code the attention kernels use.  Positions must be held: < len for retrieval heads,
- * visible from position len-1 for streaming heads; otherwise DUO_E_INVALID. */
+ * code the attention kernels use.  Positions must be held by sequence b: < len_b for
+ * retrieval heads, visible from position len_b - 1 for streaming heads; otherwise
+ * DUO_E_INVALID. */
 int duo_kv_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which,
                 int64_t pos0, int32_t n, float* d_out, void* hip_stream);
 

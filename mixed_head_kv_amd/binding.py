@@ -28,7 +28,7 @@ DUO_KV_SAME_AS_IO = 0
 DUO_KV_INT4_G128 = 1
 
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
-           "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
+           "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect"]
 KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage"]
 
@@ -69,6 +69,9 @@ def lib():
         "duo_kv_append": (ctypes.c_int, [vp, i32, vp, vp, i32, vp]),
         "duo_decode": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "duo_kv_length": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64)]),
+        "duo_prefill_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp]),
+        "duo_kv_append_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, i32, vp]),
+        "duo_kv_length_seq": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(i64)]),
         "duo_kv_free": (None, [vp]),
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_kv_read": (ctypes.c_int, [vp, i32, i32, i32, i32, i64, i32, vp, vp]),
@@ -156,6 +159,20 @@ def duo_kv_length(h, layer) -> int:
     return out.value
 
 
+def duo_prefill_seq(h, layer, seq, q, k, v, n_tokens, out, stream=None):
+    _check(lib().duo_prefill_seq(h, layer, seq, _ptr(q), _ptr(k), _ptr(v), n_tokens, _ptr(out), _stream(stream)))
+
+
+def duo_kv_append_seq(h, layer, seq, k, v, n_tokens, stream=None):
+    _check(lib().duo_kv_append_seq(h, layer, seq, _ptr(k), _ptr(v), n_tokens, _stream(stream)))
+
+
+def duo_kv_length_seq(h, layer, seq) -> int:
+    out = ctypes.c_int64()
+    _check(lib().duo_kv_length_seq(h, layer, seq, ctypes.byref(out)))
+    return out.value
+
+
 def duo_kv_free(h):
     lib().duo_kv_free(h)
 
@@ -235,6 +252,20 @@ class DuoKV:
 
     def append(self, layer, k, v):
         duo_kv_append(self.h, layer, k, v, k.shape[-3])
+
+    def length_seq(self, layer, seq):
+        return duo_kv_length_seq(self.h, layer, seq)
+
+    def prefill_seq(self, layer, seq, q, k, v, out=None):
+        """One sequence's chunk: q, k, v of shape [1, T, heads, D] (or [T, heads, D])."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        duo_prefill_seq(self.h, layer, seq, q, k, v, q.shape[-3], out)
+        return out
+
+    def append_seq(self, layer, seq, k, v):
+        duo_kv_append_seq(self.h, layer, seq, k, v, k.shape[-3])
 
     def decode(self, layer, q, k_new=None, v_new=None, out=None):
         import torch

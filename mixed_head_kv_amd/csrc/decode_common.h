@@ -12,7 +12,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 struct DecodeItem {
   int b, kvh, split, nsplit;
   bool retrieval;
-  int64_t cache, key0, key1;  // cache rows [key0, key1) of this split
+  int64_t t;                  // the sequence's query position
+  int64_t cache, key0, key1;  // cache rows [key0, key1) of this split (empty: 0, 0)
 };
 
 // Workgroups are laid out retrieval splits first, then streaming splits, per sequence.
@@ -20,6 +21,14 @@ __device__ inline DecodeItem decode_item(const Geom& g, const LayerView& lv, con
   DecodeItem it;
   const int per_b = lv.n_ret * p.nsplit_r + lv.n_str * p.nsplit_s;
   it.b = item / per_b;
+  it.t = p.t;
+  if (p.varlen) {
+    // constant indices: the plan stays in the kernel-argument segment (an indexed read
+    // of the by-value argument would copy it to scratch memory)
+#pragma unroll
+    for (int s = 0; s < kMaxVarlen; ++s)
+      if (s == it.b) it.t = p.t_seq[s];
+  }
   int r = item % per_b;
   int64_t nkeys;
   int chunk, idx;
@@ -29,7 +38,7 @@ __device__ inline DecodeItem decode_item(const Geom& g, const LayerView& lv, con
     it.split = r % p.nsplit_r;
     it.nsplit = p.nsplit_r;
     chunk = p.chunk_r;
-    nkeys = p.t + 1;
+    nkeys = it.t + 1;
     it.kvh = lv.ret_kv[idx];
     it.cache = int64_t(it.b) * lv.n_ret + idx;
   } else {
@@ -39,12 +48,15 @@ __device__ inline DecodeItem decode_item(const Geom& g, const LayerView& lv, con
     it.split = r % p.nsplit_s;
     it.nsplit = p.nsplit_s;
     chunk = p.chunk_s;
-    nkeys = p.t + 1 < g.S + g.R ? p.t + 1 : g.S + g.R;  // valid slots are [0, nkeys)
+    nkeys = it.t + 1 < g.S + g.R ? it.t + 1 : g.S + g.R;  // valid slots are [0, nkeys)
     it.kvh = lv.str_kv[idx];
     it.cache = int64_t(it.b) * lv.n_str + idx;
   }
   it.key0 = int64_t(it.split) * chunk;
   it.key1 = it.key0 + chunk < nkeys ? it.key0 + chunk : nkeys;
+  // a shorter sequence of a varlen batch leaves its last splits without keys: they
+  // produce the empty partial (m = -inf, l = 0), which the merge weighs with zero
+  if (it.key0 >= nkeys) it.key0 = it.key1 = 0;
   return it;
 }
 

@@ -165,8 +165,9 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
   const uint16_t* K = reinterpret_cast<const uint16_t*>(c.k);
   const uint16_t* V = reinterpret_cast<const uint16_t*>(c.v);
   const int64_t row0 = it.cache * c.rows;
-  // fused append of this step's token: retrieval row t or streaming slot new_slot
-  const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
+  // fused append of this step's token: retrieval row t or its streaming slot
+  const int64_t new_row =
+      p.k_new ? (it.retrieval ? it.t : p.varlen ? stream_slot(it.t, g.S, g.R) : p.new_slot) : -1;
   const uint16_t* k_new = p.k_new ? p.k_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
   const uint16_t* v_new = p.v_new ? p.v_new + (int64_t(it.b) * g.Hkv + it.kvh) * 128 : nullptr;
   constexpr int kRing = 2;  // tiles in flight per wavefront
@@ -389,7 +390,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
   const int G = g.G;
   const CacheRegion& c = it.retrieval ? lv.ret : lv.str;
 
-  // Fused append of this step's token (retrieval row t or streaming slot new_slot): the
+  // Fused append of this step's token (retrieval row t or its streaming slot): the
   // workgroup whose range holds the row quantises K (wavefront 0) and V (wavefront 1)
   // exactly as the append kernel does and stores codes and (scale, zero) before any of
   // its wavefronts loads the row's tile (after the first ring round's loads when the row
@@ -398,7 +399,8 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
   // rows); the token's nibbles go in with device-scope atomics, which bypass the CU's L1,
   // so the tile loads that follow cannot meet a stale line.
   constexpr int kRing = 3;  // tiles in flight per wavefront
-  const int64_t new_row = p.k_new ? (it.retrieval ? p.t : p.new_slot) : -1;
+  const int64_t new_row =
+      p.k_new ? (it.retrieval ? it.t : p.varlen ? stream_slot(it.t, g.S, g.R) : p.new_slot) : -1;
   const bool has_new = new_row >= it.key0 && new_row < it.key1;  // uniform
   const bool append_late = has_new && new_row - it.key0 >= int64_t(kStride) * kRing;
   auto append = [&]() {

@@ -157,7 +157,7 @@ struct duo_handle {
   Layout layout;
   Geom geom;
   std::vector<LayerView> views;
-  std::vector<int64_t> len;
+  std::vector<int64_t> len;  // [layer * batch + sequence]: tokens held
   CacheRegion stage{};   // streaming-head prefill staging (MFMA path)
   int stage_tokens = 0;
   float* partials = nullptr;
@@ -245,6 +245,8 @@ int check_ptr(const void* p, const char* name) {
 duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
   duo::DecodePlan p;
   p.t = t;
+  p.varlen = 0;
+  for (int b = 0; b < duo::kMaxVarlen; ++b) p.t_seq[b] = t;
   p.partials = h->partials;
   p.counters = h->counters;
   p.k_new = nullptr;
@@ -355,7 +357,7 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
       }
     }
   }
-  h->len.assign(cfg->n_layers, 0);
+  h->len.assign(size_t(cfg->n_layers) * cfg->batch, 0);
   h->stage = CacheRegion{h->ws + L.stage_k, h->ws + L.stage_v, nullptr, nullptr, L.stage_rows, 1};
   h->stage_tokens = L.stage_tokens;
   h->partials = reinterpret_cast<float*>(h->ws + L.partials);
@@ -390,18 +392,118 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
 
 void duo_kv_free(duo_handle* h) { delete h; }
 
+static int64_t& seq_len(duo_handle* h, int32_t layer, int32_t seq) { return h->len[size_t(layer) * h->cfg.batch + seq]; }
+static int64_t seq_len(const duo_handle* h, int32_t layer, int32_t seq) {
+  return h->len[size_t(layer) * h->cfg.batch + seq];
+}
+
+// The layer's length when every sequence of the batch holds the same number of tokens.
+static int batch_len(const duo_handle* h, int32_t layer, int64_t* out) {
+  const int64_t l0 = seq_len(h, layer, 0);
+  for (int32_t b = 1; b < h->cfg.batch; ++b)
+    if (seq_len(h, layer, b) != l0)
+      return fail(DUO_E_STATE, "the sequences of the batch hold different lengths (use the per-sequence calls)");
+  *out = l0;
+  return DUO_OK;
+}
+
 int duo_kv_length(const duo_handle* h, int32_t layer, int64_t* out_len) {
   int rc = check_layer(h, layer);
   if (rc) return rc;
   if (!out_len) return fail(DUO_E_INVALID, "out_len is NULL");
-  *out_len = h->len[layer];
+  int64_t l = 0;
+  if ((rc = batch_len(h, layer, &l))) return rc;
+  *out_len = l;
   return ok();
 }
 
-static int check_tokens(const duo_handle* h, int32_t layer, int32_t n_tokens) {
+int duo_kv_length_seq(const duo_handle* h, int32_t layer, int32_t seq, int64_t* out_len) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (seq < 0 || seq >= h->cfg.batch) return fail(DUO_E_INVALID, "sequence index out of range");
+  if (!out_len) return fail(DUO_E_INVALID, "out_len is NULL");
+  *out_len = seq_len(h, layer, seq);
+  return ok();
+}
+
+static int check_tokens(int64_t len, int64_t max_context, int32_t n_tokens) {
   if (n_tokens <= 0) return fail(DUO_E_INVALID, "n_tokens must be > 0");
-  if (h->len[layer] + n_tokens > h->cfg.max_context)
-    return fail(DUO_E_CAPACITY, "length + n_tokens exceeds max_context");
+  if (len + n_tokens > max_context) return fail(DUO_E_CAPACITY, "length + n_tokens exceeds max_context");
+  return DUO_OK;
+}
+
+// The caches of one sequence as a batch of one: every region starts at the sequence's
+// first cache (caches are whole multiples of 64 rows, so tiled and blocked layouts keep
+// their alignment).
+static void one_sequence(const duo_handle* h, int32_t layer, int32_t seq, duo::Geom* g, LayerView* lv) {
+  *g = h->geom;
+  g->B = 1;
+  *lv = h->views[layer];
+  const bool int4 = h->cfg.kv_format == DUO_KV_INT4_G128;
+  const int64_t vec = int4 ? h->cfg.head_dim / 2 : int64_t(h->cfg.head_dim) * (h->cfg.io_dtype == DUO_DTYPE_F32 ? 4 : 2);
+  auto shift = [&](CacheRegion& c, int64_t caches) {
+    const int64_t rows = caches * c.rows;
+    c.k += rows * vec;
+    c.v += rows * vec;
+    if (c.k_meta) c.k_meta += rows * 2;
+    if (c.v_meta) c.v_meta += rows * 2;
+  };
+  shift(lv->ret, int64_t(seq) * lv->n_ret);
+  shift(lv->str, int64_t(seq) * lv->n_str);
+}
+
+// Prefill of n_tokens at positions [t0, t0 + n_tokens) for the batch described by (g, lv).
+static int run_prefill(duo_handle* h, const duo::Geom& g, const LayerView& lv, const void* q, const void* k,
+                       const void* v, int32_t n_tokens, void* out, int64_t t0, hipStream_t st) {
+  hipError_t e;
+  if (h->use_mfma) {
+    // One launch writes the chunk into the retrieval caches (the retrieval kernel reads
+    // its keys there) and stages the keys of the first streaming-head queries; the
+    // streaming caches, read as they stood before the chunk, are updated last.
+    const int nq0 = lv.n_str > 0 ? (n_tokens < h->stage_tokens ? n_tokens : h->stage_tokens) : 0;
+    {
+      KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
+      e = duo::launch_chunk_tiles(g, lv, h->stage, k, v, n_tokens, t0, true, 0, nq0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
+    {  // retrieval heads and the first staged streaming-head queries, one launch
+      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+      e = duo::launch_prefill_mfma(g, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,
+                                   h->prefill_counters, h->num_cu, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention");
+    // further streaming-head queries, at most stage_tokens per launch pair (the staging
+    // capacity)
+    for (int q0 = h->stage_tokens; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
+      const int nq = n_tokens - q0 < h->stage_tokens ? n_tokens - q0 : h->stage_tokens;
+      {
+        KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
+        e = duo::launch_chunk_tiles(g, lv, h->stage, k, v, n_tokens, t0, false, q0, nq, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
+      {
+        KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
+        e = duo::launch_prefill_stream_mfma(g, lv, h->stage, q, out, n_tokens, t0, q0, nq, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
+    }
+    {
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_stream_cache_update(g, lv, k, v, n_tokens, t0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append (streaming)");
+  } else {
+    {
+      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+      e = duo::launch_prefill_valu(g, lv, q, k, v, out, n_tokens, t0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention");
+    {
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_append(g, lv, k, v, n_tokens, t0, 3, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill append");
+  }
   return DUO_OK;
 }
 
@@ -412,60 +514,28 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) || (rc = check_ptr(out, "out")))
     return rc;
   if (h->cfg.kv_format == DUO_KV_INT4_G128) return fail(DUO_E_UNSUPPORTED, "prefill with an int4 cache");
-  if ((rc = check_tokens(h, layer, n_tokens))) return rc;
-  const LayerView& lv = h->views[layer];
-  const int64_t t0 = h->len[layer];
-  hipStream_t st = as_stream(hip_stream);
-  hipError_t e;
-  if (h->use_mfma) {
-    // One launch writes the chunk into the retrieval caches (the retrieval kernel reads
-    // its keys there) and stages the keys of the first streaming-head queries; the
-    // streaming caches, read as they stood before the chunk, are updated last.
-    const int nq0 = lv.n_str > 0 ? (n_tokens < h->stage_tokens ? n_tokens : h->stage_tokens) : 0;
-    {
-      KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
-      e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, true, 0, nq0, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
-    {  // retrieval heads and the first staged streaming-head queries, one launch
-      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
-      e = duo::launch_prefill_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,
-                                   h->prefill_counters, h->num_cu, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "prefill attention");
-    // further streaming-head queries, at most stage_tokens per launch pair (the staging
-    // capacity)
-    for (int q0 = h->stage_tokens; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
-      const int nq = n_tokens - q0 < h->stage_tokens ? n_tokens - q0 : h->stage_tokens;
-      {
-        KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
-        e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, false, q0, nq, st);
-      }
-      if (e != hipSuccess) return hip_fail(e, "prefill staging (streaming)");
-      {
-        KernelMark m(h, DUO_KERNEL_PREFILL_STREAMING, st);
-        e = duo::launch_prefill_stream_mfma(h->geom, lv, h->stage, q, out, n_tokens, t0, q0, nq, st);
-      }
-      if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
-    }
-    {
-      KernelMark m(h, DUO_KERNEL_APPEND, st);
-      e = duo::launch_stream_cache_update(h->geom, lv, k, v, n_tokens, t0, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "prefill append (streaming)");
-  } else {
-    {
-      KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
-      e = duo::launch_prefill_valu(h->geom, lv, q, k, v, out, n_tokens, t0, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "prefill attention");
-    {
-      KernelMark m(h, DUO_KERNEL_APPEND, st);
-      e = duo::launch_append(h->geom, lv, k, v, n_tokens, t0, 3, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "prefill append");
-  }
-  h->len[layer] = t0 + n_tokens;
+  int64_t t0 = 0;
+  if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = run_prefill(h, h->geom, h->views[layer], q, k, v, n_tokens, out, t0, as_stream(hip_stream)))) return rc;
+  for (int32_t b = 0; b < h->cfg.batch; ++b) seq_len(h, layer, b) = t0 + n_tokens;
+  return ok();
+}
+
+int duo_prefill_seq(duo_handle* h, int32_t layer, int32_t seq, const void* q, const void* k, const void* v,
+                    int32_t n_tokens, void* out, void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (seq < 0 || seq >= h->cfg.batch) return fail(DUO_E_INVALID, "sequence index out of range");
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) || (rc = check_ptr(out, "out")))
+    return rc;
+  if (h->cfg.kv_format == DUO_KV_INT4_G128) return fail(DUO_E_UNSUPPORTED, "prefill with an int4 cache");
+  const int64_t t0 = seq_len(h, layer, seq);
+  if ((rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  duo::Geom g;
+  LayerView lv;
+  one_sequence(h, layer, seq, &g, &lv);
+  if ((rc = run_prefill(h, g, lv, q, k, v, n_tokens, out, t0, as_stream(hip_stream)))) return rc;
+  seq_len(h, layer, seq) = t0 + n_tokens;
   return ok();
 }
 
@@ -473,15 +543,36 @@ int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, in
   int rc = check_layer(h, layer);
   if (rc) return rc;
   if ((rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
-  if ((rc = check_tokens(h, layer, n_tokens))) return rc;
-  const int64_t t0 = h->len[layer];
+  int64_t t0 = 0;
+  if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
   hipError_t e;
   {
     KernelMark m(h, DUO_KERNEL_APPEND, as_stream(hip_stream));
     e = duo::launch_append(h->geom, h->views[layer], k, v, n_tokens, t0, 3, as_stream(hip_stream));
   }
   if (e != hipSuccess) return hip_fail(e, "append");
-  h->len[layer] = t0 + n_tokens;
+  for (int32_t b = 0; b < h->cfg.batch; ++b) seq_len(h, layer, b) = t0 + n_tokens;
+  return ok();
+}
+
+int duo_kv_append_seq(duo_handle* h, int32_t layer, int32_t seq, const void* k, const void* v, int32_t n_tokens,
+                      void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (seq < 0 || seq >= h->cfg.batch) return fail(DUO_E_INVALID, "sequence index out of range");
+  if ((rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
+  const int64_t t0 = seq_len(h, layer, seq);
+  if ((rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  duo::Geom g;
+  LayerView lv;
+  one_sequence(h, layer, seq, &g, &lv);
+  hipError_t e;
+  {
+    KernelMark m(h, DUO_KERNEL_APPEND, as_stream(hip_stream));
+    e = duo::launch_append(g, lv, k, v, n_tokens, t0, 3, as_stream(hip_stream));
+  }
+  if (e != hipSuccess) return hip_fail(e, "append");
+  seq_len(h, layer, seq) = t0 + n_tokens;
   return ok();
 }
 
@@ -493,23 +584,48 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(DUO_E_STATE, "k_new and v_new must both be set or both NULL");
   const bool append = k_new != nullptr;
   if (append && ((rc = check_ptr(k_new, "k_new")) || (rc = check_ptr(v_new, "v_new")))) return rc;
-  const int64_t len = h->len[layer];
-  if (append && len + 1 > h->cfg.max_context) return fail(DUO_E_CAPACITY, "decode append exceeds max_context");
-  if (!append && len < 1) return fail(DUO_E_STATE, "decode without new K/V on an empty layer");
+  const int32_t B = h->cfg.batch;
+  int64_t tmax = -1;
+  bool uniform = true;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t len = seq_len(h, layer, b);
+    if (append && len + 1 > h->cfg.max_context) return fail(DUO_E_CAPACITY, "decode append exceeds max_context");
+    if (!append && len < 1) return fail(DUO_E_STATE, "decode without new K/V on an empty sequence");
+    const int64_t t = append ? len : len - 1;
+    if (b > 0 && t != tmax) uniform = false;
+    if (t > tmax) tmax = t;
+  }
+  if (!uniform && B > duo::kMaxVarlen)
+    return fail(DUO_E_UNSUPPORTED, "decode of sequences of different lengths with batch > 32");
   const LayerView& lv = h->views[layer];
   hipStream_t st = as_stream(hip_stream);
-  const int64_t t = append ? len : len - 1;
   hipError_t e;
-  duo::DecodePlan p = make_plan(h, layer, t);
+  duo::DecodePlan p = make_plan(h, layer, tmax);
+  if (!uniform) {
+    p.varlen = 1;
+    for (int32_t b = 0; b < B; ++b) p.t_seq[b] = seq_len(h, layer, b) - (append ? 0 : 1);
+  }
   if (append && h->use_mfma_decode) {
     // the MFMA decode (bf16 or int4 caches) appends the token itself (the workgroup
     // covering its row)
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
-  } else if (append) {
+  } else if (append && uniform) {
     KernelMark m(h, DUO_KERNEL_APPEND, st);
-    e = duo::launch_append(h->geom, lv, k_new, v_new, 1, t, 3, st);
+    e = duo::launch_append(h->geom, lv, k_new, v_new, 1, tmax, 3, st);
     if (e != hipSuccess) return hip_fail(e, "decode append");
+  } else if (append) {
+    // one append per sequence, each at its own position
+    const int64_t row_bytes = int64_t(h->cfg.n_kv_heads) * h->cfg.head_dim * (h->cfg.io_dtype == DUO_DTYPE_F32 ? 4 : 2);
+    for (int32_t b = 0; b < B; ++b) {
+      duo::Geom g1;
+      LayerView lv1;
+      one_sequence(h, layer, b, &g1, &lv1);
+      KernelMark m(h, DUO_KERNEL_APPEND, st);
+      e = duo::launch_append(g1, lv1, static_cast<const char*>(k_new) + b * row_bytes,
+                             static_cast<const char*>(v_new) + b * row_bytes, 1, p.t_seq[b], 3, st);
+      if (e != hipSuccess) return hip_fail(e, "decode append");
+    }
   }
   {
     KernelMark m(h, DUO_KERNEL_DECODE, st);
@@ -517,7 +633,8 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
                            : duo::launch_decode_valu(h->geom, lv, p, q, out, st);
   }
   if (e != hipSuccess) return hip_fail(e, "decode attention");
-  if (append) h->len[layer] = len + 1;
+  if (append)
+    for (int32_t b = 0; b < B; ++b) ++seq_len(h, layer, b);
   return ok();
 }
 
@@ -532,7 +649,7 @@ static int check_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_
   const LayerView& lv = h->views[layer];
   *streaming = lv.kind[kv_head] == duo::kKindStreaming;
   *cache = int64_t(b) * (*streaming ? lv.n_str : lv.n_ret) + lv.slot[kv_head];
-  const int64_t len = h->len[layer];
+  const int64_t len = seq_len(h, layer, b);
   if (pos0 < 0 || pos0 + n > len) return fail(DUO_E_INVALID, "positions not yet appended");
   if (*streaming && n > 0) {
     const int64_t last = len - 1;

@@ -74,8 +74,15 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);
 
+// Most sequences one decode launch takes when their lengths differ.
+constexpr int kMaxVarlen = 32;
+
 struct DecodePlan {
-  int64_t t;          // query position
+  int64_t t;          // query position (the largest one when varlen is set)
+  // varlen != 0: the sequences' query positions differ and sequence b's is t_seq[b]
+  // (batch <= kMaxVarlen); the split sizes are planned for t.
+  int varlen;
+  int64_t t_seq[kMaxVarlen];
   int chunk_r;        // keys per split, retrieval heads
   int nsplit_r;
   int chunk_s;        // keys per split, streaming heads
@@ -84,7 +91,7 @@ struct DecodePlan {
   int* counters;      // [B * Hkv] arrival counters, zero between calls
   // Fused append (MFMA decode): K/V of the token at position t ([B, Hkv, D]), or null
   // when the token is already in the caches.  It lands in retrieval row t and in
-  // streaming slot `new_slot`.
+  // streaming slot `new_slot` (with varlen: row t_seq[b] and that position's slot).
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t new_slot;

@@ -488,3 +488,110 @@ def test_llama2_7b_mha_32k_full_attention_layer(torch_cuda):
     compare("32k full-attention decode", to_f64(dec), ref_dec, TOL["bf16"])
     ref_pre = oracle_rows(w, 0, rows, total)
     compare("32k full-attention prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
+
+
+VARLEN = {
+    # name: (workload, per-sequence lengths before decoding; 0 = the first decode step
+    # is the sequence's first token)
+    "mha_bf16": (W("mha_bf16_var", 31, 8, 8, 128, "bf16", 8, 32, 1801, 6, 3, fixed=(0, 2, 5)),
+                 [0, 1, 40, 1200, 613, 1800]),
+    "gqa_bf16": (W("gqa_bf16_var", 32, 16, 4, 128, "bf16", 4, 64, 2101, 5, 2, fixed=(1, 3)), [700, 2100, 3]),
+    "mha_f32_d128": (W("mha_f32_var", 33, 4, 4, 128, "f32", 2, 16, 501, 5, 2, fixed=(0, 3)), [5, 500, 0, 200]),
+    "int4": (W("int4_var", 34, 8, 4, 128, "bf16", 4, 32, 1501, 5, 2, fmt="int4", fixed=(0, 3)), [90, 1500, 513]),
+}
+
+
+@pytest.mark.parametrize("name", list(VARLEN))
+def test_varlen_batch_decode_matches_oracle(torch_cuda, name):
+    """Sequences of different lengths in one handle: each filled by the per-sequence
+    calls (prefill, or two appends for int4), then decode steps for the whole batch with
+    every sequence's token at its own position, then one decode without new K/V after a
+    per-sequence append.  Every sequence's outputs are checked against the oracle on its
+    own data (sequence b: the workload reseeded with seed + 100 b), and its length and
+    caches too.  The short sequences leave the long ones' later key splits empty."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    w, lens = VARLEN[name]
+    Bn, steps = len(lens), w.decode_steps
+    ws = [w.scaled(seed=w.seed + 100 * b) for b in range(Bn)]
+    say(f"varlen {name} lengths={lens} steps={steps}")
+    kv = B.DuoKV.for_workload(w, batch=Bn)
+    tol = TOL[w.io_dtype]
+    data, pre = [], {}
+    for b, (wb, L) in enumerate(zip(ws, lens)):
+        q, k, v = (device_synth(wb, 0, x, 0, L + steps + 1) for x in "qkv")
+        data.append((q, k, v))
+        if L == 0:
+            continue
+        if w.kv_format == "int4":
+            h = L // 2
+            if h:
+                kv.append_seq(0, b, k[:h].contiguous(), v[:h].contiguous())
+            kv.append_seq(0, b, k[h:L].contiguous(), v[h:L].contiguous())
+        else:
+            pre[b] = kv.prefill_seq(0, b, q[:L].contiguous(), k[:L].contiguous(), v[:L].contiguous())
+    torch.cuda.synchronize()
+    assert [kv.length_seq(0, b) for b in range(Bn)] == lens
+    with pytest.raises(B.DuoError) as e:
+        kv.length(0)
+    assert e.value.code == B.DUO_E_STATE
+    dec = []
+    for s in range(steps):
+        qs, ks, vs = (torch.stack([data[b][i][lens[b] + s] for b in range(Bn)]) for i in range(3))
+        dec.append(kv.decode(0, qs, ks, vs))
+    # one more token per sequence by the per-sequence append, then a decode that reads it
+    for b in range(Bn):
+        t = lens[b] + steps
+        kv.append_seq(0, b, data[b][1][t:t + 1].contiguous(), data[b][2][t:t + 1].contiguous())
+    last = kv.decode(0, torch.stack([data[b][0][lens[b] + steps] for b in range(Bn)]))
+    torch.cuda.synchronize()
+    dec = torch.stack(dec, 1)
+    rng = np.random.default_rng(5)
+    for b, wb in enumerate(ws):
+        L, total = lens[b], lens[b] + steps + 1
+        assert kv.length_seq(0, b) == total
+        ref = oracle_rows(wb, 0, np.arange(L, total), total)
+        compare(f"varlen {name} seq {b} decode", to_f64(dec[b]), ref[:steps], tol)
+        compare(f"varlen {name} seq {b} decode without new K/V", to_f64(last[b])[None], ref[steps:], tol)
+        if b in pre:
+            rows = np.unique(np.concatenate([np.arange(min(L, 8)), np.arange(max(0, L - 8), L),
+                                             rng.integers(0, L, 16)]))
+            compare(f"varlen {name} seq {b} prefill", to_f64(pre[b])[rows], oracle_rows(wb, 0, rows, total), tol)
+        if w.kv_format != "int4":
+            mask = wb.mask(0)
+            g = int(np.flatnonzero(mask)[0])
+            hist = host_history(wb, 0, "k", total)
+            assert np.array_equal(to_f64(kv.read(0, g, 0, 0, total, b=b)), hist[:, g]), (name, b, "retrieval K")
+            gs = int(np.flatnonzero(~mask)[0])
+            n = min(w.recent, total)
+            assert np.array_equal(to_f64(kv.read(0, gs, 0, total - n, n, b=b)), hist[total - n:, gs]), \
+                (name, b, "streaming K window")
+
+
+def test_varlen_batch_limits(torch_cuda):
+    """Differing lengths in one decode launch take at most 32 sequences; a refused call
+    changes nothing, and equal lengths are served at any batch size."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    w = W("varlen_limit", 35, 4, 2, 128, "bf16", 2, 8, 40, 0, 1, fixed=(0,))
+    say("varlen limits, batch 33")
+    kv = B.DuoKV.for_workload(w, batch=33)
+    k, v, q = (device_synth(w, 0, x, 0, 2) for x in "kvq")
+    kv.append_seq(0, 0, k[:1].contiguous(), v[:1].contiguous())
+    # every sequence holds the same data: position 0 appended, position 1 decoded
+    qs, ks, vs = (x[1].expand(33, -1, -1).contiguous() for x in (q, k, v))
+    with pytest.raises(B.DuoError) as e:
+        kv.decode(0, qs, ks, vs)
+    assert e.value.code == B.DUO_E_UNSUPPORTED
+    assert [kv.length_seq(0, b) for b in range(33)] == [1] + [0] * 32
+    for b in range(1, 33):
+        kv.append_seq(0, b, k[:1].contiguous(), v[:1].contiguous())
+    assert kv.length(0) == 1
+    out = kv.decode(0, qs, ks, vs)
+    torch.cuda.synchronize()
+    ref = oracle_rows(w, 0, [1], 2)
+    for b in range(33):
+        compare(f"batch 33 seq {b}", to_f64(out[b])[None], ref, TOL["bf16"])
+    with pytest.raises(B.DuoError) as e:
+        kv.length_seq(0, 33)
+    assert e.value.code == B.DUO_E_INVALID
