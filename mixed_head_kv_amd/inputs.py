@@ -26,7 +26,8 @@ single correctly rounded fp32 operation, so host and device agree bit for bit.  
 mean 0, variance 1 (to 1 part in 2^32) and support [-3.47, 3.47]: a stand-in for the
 workloads' N(0, 1) that costs the attention path exactly the same work.
 
-Streams: stream = layer * 4 + {Q: 0, K: 1, V: 2}.  Counters index the whole sequence by
+Streams: stream = layer * 4 + {Q: 0, K: 1, V: 2, X: 3} (X: a layer's hidden-state input,
+[T, hidden], counter n = pos * hidden + e).  Counters index the whole sequence by
 absolute position: Q at (pos, head, d) uses n = (pos * Hq + head) * D + d and K/V at
 (pos, kv_head, d) use n = (pos * Hkv + kv_head) * D + d, so a prefill chunk
 [pos0, pos0 + T) is the contiguous counter range starting at pos0 * H * D and decode
@@ -46,7 +47,14 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 SCALE_F32 = np.float32(math.sqrt(3.0) / 65536.0)
 CENTER = 131070
-KIND_STREAM = {"q": 0, "k": 1, "v": 2}
+KIND_STREAM = {"q": 0, "k": 1, "v": 2, "x": 3}
+# Synthetic 8-bit weights of the linear layers around the attention: codes of weight
+# `which` of `layer` use stream WEIGHT_BASE + layer * 8 + WEIGHT_STREAM[which] with
+# counter n * K + k for (output channel n, input k); the per-channel scales use that
+# stream + 4 with counter n.
+WEIGHT_BASE = 1 << 16
+WEIGHT_STREAM = {"qkv": 0, "o": 1}
+CODE_MULT = np.float32(32.0)
 
 _CHUNK = 1 << 22  # counters per NumPy pass (bounds host memory)
 
@@ -196,3 +204,32 @@ WORKLOADS = {
                                                 "bf16", "int4", 64, 256, 3300000, 0, 36, 4),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
+
+
+def weight_stream(layer: int, which: str) -> int:
+    return WEIGHT_BASE + layer * 8 + WEIGHT_STREAM[which]
+
+
+def weight_codes(seed: int, layer: int, which: str, n0: int, n: int, K: int) -> np.ndarray:
+    """int8 codes [n, K] of output channels [n0, n0 + n): the generator's fp32 value times
+    32 (exact), rounded to nearest even (|code| <= 111).  The device fill
+    (duo_synth_fill with DUO_SYNTH_INT8) computes the same."""
+    counters = np.uint64(n0) * np.uint64(K) + np.arange(n * K, dtype=np.uint64)
+    x = values_f32(seed, weight_stream(layer, which), counters) * CODE_MULT
+    return np.rint(x).astype(np.int8).reshape(n, K)
+
+
+def weight_codes_rows(seed: int, layer: int, which: str, rows, K: int) -> np.ndarray:
+    """Codes [len(rows), K] of the given output channels (for sampled checks)."""
+    rows = np.asarray(rows, dtype=np.uint64).reshape(-1)
+    counters = rows[:, None] * np.uint64(K) + np.arange(K, dtype=np.uint64)[None, :]
+    x = values_f32(seed, weight_stream(layer, which), counters) * CODE_MULT
+    return np.rint(x).astype(np.int8)
+
+
+def weight_scales(seed: int, layer: int, which: str, N: int, K: int) -> np.ndarray:
+    """fp32 scales [N]: (1 + x / 4) / (32 sqrt(K)) rounded once to fp32, x from the
+    generator, so that a layer fed unit-variance inputs gives outputs of standard
+    deviation 1 + x / 4 (between 0.13 and 1.87)."""
+    x = values_f32(seed, weight_stream(layer, which) + 4, np.arange(N, dtype=np.uint64)).astype(np.float64)
+    return ((1.0 + 0.25 * x) / (32.0 * math.sqrt(K))).astype(np.float32)

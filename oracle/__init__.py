@@ -12,6 +12,8 @@ Contents
                retrieval / streaming visibility rule (plain definition).
 ``int4``       the group-128 asymmetric int4 KV codec with fp16 scale and zero
                (plain definition, fp32 steps as the format fixes them).
+``linear``     the 8-bit-weight linear layers around the attention (fused QKV
+               projection with the rotary encoding, output projection), fp64.
 
 Every function cites the passage of the source pages it follows.  The pages are:
 
@@ -29,4 +31,4 @@ routines, closed forms, brute force and invariants (none of them re-typing the
 oracle's own formula); no function is "parity unpinned".
 """
 
-from . import attention, int4  # noqa: F401
+from . import attention, int4, linear  # noqa: F401
