@@ -26,10 +26,11 @@ DUO_DTYPE_F32 = 0
 DUO_DTYPE_BF16 = 1
 DUO_KV_SAME_AS_IO = 0
 DUO_KV_INT4_G128 = 1
+DUO_SYNTH_INT8 = 2
 
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
            "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
-           "duo_profile_enable", "duo_profile_collect"]
+           "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8"]
 KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage"]
 
 
@@ -79,6 +80,8 @@ def lib():
         "duo_synth_fill": (ctypes.c_int, [vp, i32, u64, ctypes.c_uint32, u64, u64, vp]),
         "duo_profile_enable": (ctypes.c_int, [vp, i32]),
         "duo_profile_collect": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "duo_linear_w8": (ctypes.c_int, [vp, i64, i32, vp, vp, i32, vp, vp]),
+        "duo_qkv_rope_w8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -171,6 +174,38 @@ def duo_kv_length_seq(h, layer, seq) -> int:
     out = ctypes.c_int64()
     _check(lib().duo_kv_length_seq(h, layer, seq, ctypes.byref(out)))
     return out.value
+
+
+def duo_linear_w8(x, M, K, w, scale, N, y, stream=None):
+    _check(lib().duo_linear_w8(_ptr(x), M, K, _ptr(w), _ptr(scale), N, _ptr(y), _stream(stream)))
+
+
+def duo_qkv_rope_w8(x, M, hidden, positions, w, scale, n_q_heads, n_kv_heads, head_dim, rope_base, q, k, v,
+                    stream=None):
+    _check(lib().duo_qkv_rope_w8(_ptr(x), M, hidden, _ptr(positions), _ptr(w), _ptr(scale), n_q_heads, n_kv_heads,
+                                 head_dim, float(rope_base), _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+
+
+def linear_w8(x, w, scale, out=None):
+    """y [M, N] = x [M, K] (bf16) times the int8 weight w [N, K] scaled per row by scale [N]."""
+    import torch
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    duo_linear_w8(x, M, K, w, scale, N, out)
+    return out
+
+
+def qkv_rope_w8(x, positions, w, scale, n_q_heads, n_kv_heads, head_dim, rope_base):
+    """(q [M, Hq, D], k [M, Hkv, D], v [M, Hkv, D]) of tokens x [M, hidden] at positions [M]."""
+    import torch
+    M, hidden = x.shape
+    q = torch.empty((M, n_q_heads, head_dim), dtype=torch.bfloat16, device=x.device)
+    k = torch.empty((M, n_kv_heads, head_dim), dtype=torch.bfloat16, device=x.device)
+    v = torch.empty_like(k)
+    duo_qkv_rope_w8(x, M, hidden, positions, w, scale, n_q_heads, n_kv_heads, head_dim, rope_base, q, k, v)
+    return q, k, v
 
 
 def duo_kv_free(h):

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libduo_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["duo_attn.cpp", "kv_cache.hip", "attention_valu.hip"]
-EXTRA_SOURCES = ["decode_mfma.hip", "prefill_mfma.hip"]
+EXTRA_SOURCES = ["decode_mfma.hip", "prefill_mfma.hip", "linear_w8.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -19,6 +19,7 @@
 #include "../../include/duo_attn.h"
 #include "../../include/duo_profile.h"
 #include "../../include/duo_synth.h"
+#include "../../include/duo_linear.h"
 #include "duo_kernels.h"
 
 using duo::CacheRegion;
@@ -723,10 +724,73 @@ int duo_synth_fill(void* d_out, int32_t dtype, uint64_t seed, uint32_t stream, u
                    void* hip_stream) {
   int rc = check_ptr(d_out, "out");
   if (rc) return rc;
-  if (dtype != DUO_DTYPE_F32 && dtype != DUO_DTYPE_BF16) return fail(DUO_E_INVALID, "unknown dtype");
+  if (dtype != DUO_DTYPE_F32 && dtype != DUO_DTYPE_BF16 && dtype != DUO_SYNTH_INT8)
+    return fail(DUO_E_INVALID, "unknown dtype");
   if (seed >> 32) return fail(DUO_E_INVALID, "seed must fit in 32 bits");
   hipError_t e = duo::launch_synth(d_out, dtype, seed, stream, counter0, n, as_stream(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "synth");
+  return ok();
+}
+
+static int check_w8(const void* x, int64_t M, int32_t K, const int8_t* w, const float* scale, int32_t N) {
+  int rc;
+  if ((rc = check_ptr(x, "x")) || (rc = check_ptr(w, "w")) || (rc = check_ptr(scale, "scale"))) return rc;
+  if (M < 1) return fail(DUO_E_INVALID, "M must be >= 1");
+  if (K < 128 || K % 128 != 0) return fail(DUO_E_UNSUPPORTED, "K must be a positive multiple of 128");
+  if (N < 256 || N % 256 != 0) return fail(DUO_E_UNSUPPORTED, "N must be a positive multiple of 256");
+  if (M > (int64_t(1) << 24) || K > (1 << 20) || N > (1 << 20)) return fail(DUO_E_UNSUPPORTED, "size too large");
+  return DUO_OK;
+}
+
+int duo_linear_w8(const void* x, int64_t M, int32_t K, const int8_t* w, const float* scale, int32_t N, void* y,
+                  void* hip_stream) {
+  int rc = check_w8(x, M, K, w, scale, N);
+  if (rc || (rc = check_ptr(y, "y"))) return rc;
+  duo::W8Args a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = w;
+  a.scale = scale;
+  a.pos = nullptr;
+  a.y0 = a.y1 = a.y2 = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.K = K;
+  a.N = a.n1 = a.n2 = N;
+  a.rope_end = 0;
+  a.log2_base = 0.0;
+  hipError_t e = duo::launch_w8(a, as_stream(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "linear_w8");
+  return ok();
+}
+
+int duo_qkv_rope_w8(const void* x, int64_t M, int32_t hidden, const int64_t* positions, const int8_t* w_qkv,
+                    const float* scale, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float rope_base,
+                    void* q, void* k, void* v, void* hip_stream) {
+  if (head_dim != 128) return fail(DUO_E_UNSUPPORTED, "head_dim must be 128");
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads > 4096 || n_kv_heads > 4096)
+    return fail(DUO_E_INVALID, "head counts out of range");
+  if (!(rope_base > 1.0f) || !std::isfinite(rope_base)) return fail(DUO_E_INVALID, "rope_base must be > 1");
+  const int32_t N = (n_q_heads + 2 * n_kv_heads) * head_dim;
+  int rc = check_w8(x, M, hidden, w_qkv, scale, N);
+  if (rc || (rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
+  if (!positions) return fail(DUO_E_INVALID, "positions is NULL");
+  if (reinterpret_cast<uintptr_t>(positions) % 8) return fail(DUO_E_INVALID, "positions is not 8-byte aligned");
+  duo::W8Args a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = w_qkv;
+  a.scale = scale;
+  a.pos = positions;
+  a.y0 = static_cast<uint16_t*>(q);
+  a.y1 = static_cast<uint16_t*>(k);
+  a.y2 = static_cast<uint16_t*>(v);
+  a.M = M;
+  a.K = hidden;
+  a.N = N;
+  a.n1 = n_q_heads * head_dim;
+  a.n2 = (n_q_heads + n_kv_heads) * head_dim;
+  a.rope_end = a.n2;
+  a.log2_base = std::log2(static_cast<double>(rope_base));
+  hipError_t e = duo::launch_w8(a, as_stream(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "qkv_rope_w8");
   return ok();
 }
 

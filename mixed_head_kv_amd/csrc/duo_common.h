@@ -28,6 +28,7 @@
 #include <stdint.h>
 
 #include "../../include/duo_attn.h"
+#include "../../include/duo_synth.h"
 
 namespace duo {
 
@@ -86,6 +87,7 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f) {
 template <int IO> struct IoType;
 template <> struct IoType<DUO_DTYPE_F32> { using T = float; };
 template <> struct IoType<DUO_DTYPE_BF16> { using T = uint16_t; };
+template <> struct IoType<DUO_SYNTH_INT8> { using T = int8_t; };
 
 template <int IO>
 __device__ inline float io_load(const void* p, int64_t i) {

@@ -106,6 +106,24 @@ hipError_t launch_decode_valu(const Geom& g, const LayerView& lv, const DecodePl
 hipError_t launch_decode_mfma(const Geom& g, const LayerView& lv, const DecodePlan& p, const void* q,
                               void* out, hipStream_t st);
 
+// 8-bit-weight linear layer y = x * (c * s)^T (bf16 x [M, K], int8 c [N, K], fp32 s [N]),
+// output channels [0, n1) to y0, [n1, n2) to y1, [n2, N) to y2 (each row-major with its
+// own row length); channels [0, rope_end) are rotated per 128-channel head with the
+// position pos[m] of row m.  K % 128 == 0, N % 256 == 0, M >= 1.
+struct W8Args {
+  const uint16_t* x;
+  const int8_t* w;
+  const float* scale;
+  const int64_t* pos;  // [M] device, when rope_end > 0
+  uint16_t* y0;
+  uint16_t* y1;
+  uint16_t* y2;
+  int64_t M;
+  int K, N, n1, n2, rope_end;
+  double log2_base;
+};
+hipError_t launch_w8(const W8Args& a, hipStream_t st);
+
 // Inspection: stored vectors of positions [pos0, pos0 + n) of one cache, as fp32
 // (dequantised for int4) or as raw int4 codes + (scale, zero).
 hipError_t launch_read(const Geom& g, const CacheRegion& c, int64_t cache, bool streaming, int64_t pos0,

@@ -280,6 +280,7 @@ __global__ void k_synth(typename IoType<IO>::T* __restrict__ out, uint64_t key, 
     const int s = static_cast<int>((w & 0xffff) + ((w >> 16) & 0xffff) + ((w >> 32) & 0xffff) + (w >> 48));
     const float x = static_cast<float>(s - 131070) * kScale;
     if constexpr (IO == DUO_DTYPE_F32) out[i] = x;
+    else if constexpr (IO == DUO_SYNTH_INT8) out[i] = static_cast<int8_t>(rintf(x * 32.0f));
     else out[i] = f32_to_bf16(x);
   }
 }
@@ -377,6 +378,9 @@ hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, ui
   if (dtype == DUO_DTYPE_F32)
     launch(k_synth<DUO_DTYPE_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        static_cast<float*>(out), key, c0, n);
+  else if (dtype == DUO_SYNTH_INT8)
+    launch(k_synth<DUO_SYNTH_INT8>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<int8_t*>(out), key, c0, n);
   else
     launch(k_synth<DUO_DTYPE_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        static_cast<uint16_t*>(out), key, c0, n);

@@ -33,7 +33,7 @@ def test_headers_declare_the_boundary():
     names = declared_functions()
     for n in ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
               "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error",
-              "duo_synth_fill"]:
+              "duo_synth_fill", "duo_linear_w8", "duo_qkv_rope_w8"]:
         assert n in names
     assert set(names) == set(B.EXPORTS)
 
@@ -154,6 +154,23 @@ def test_null_handle_calls_fail_cleanly():
     assert L.duo_synth_fill(ctypes.c_void_p(4098), 1, 1, 0, 0, 10, None) == B.DUO_E_INVALID
     assert L.duo_synth_fill(p, 5, 1, 0, 0, 10, None) == B.DUO_E_INVALID
     assert L.duo_synth_fill(p, 1, 1 << 40, 0, 0, 10, None) == B.DUO_E_INVALID
+
+
+def test_linear_calls_validate_before_launching():
+    """Shape and pointer checks of the 8-bit-weight layers (no launch happens)."""
+    L = _lib_or_skip()
+    p = ctypes.c_void_p(4096)
+    assert L.duo_linear_w8(p, 4, 100, p, p, 256, p, None) == B.DUO_E_UNSUPPORTED    # K % 128
+    assert L.duo_linear_w8(p, 4, 128, p, p, 300, p, None) == B.DUO_E_UNSUPPORTED    # N % 256
+    assert L.duo_linear_w8(p, 0, 128, p, p, 256, p, None) == B.DUO_E_INVALID        # M
+    assert L.duo_linear_w8(None, 4, 128, p, p, 256, p, None) == B.DUO_E_INVALID
+    assert L.duo_linear_w8(p, 4, 128, p, p, 256, ctypes.c_void_p(4100), None) == B.DUO_E_INVALID
+    f = ctypes.c_float
+    assert L.duo_qkv_rope_w8(p, 4, 256, p, p, p, 4, 2, 64, f(1e4), p, p, p, None) == B.DUO_E_UNSUPPORTED
+    assert L.duo_qkv_rope_w8(p, 4, 256, p, p, p, 4, 2, 128, f(0.5), p, p, p, None) == B.DUO_E_INVALID
+    assert L.duo_qkv_rope_w8(p, 4, 256, None, p, p, 4, 2, 128, f(1e4), p, p, p, None) == B.DUO_E_INVALID
+    assert L.duo_qkv_rope_w8(p, 4, 256, p, p, p, 3, 2, 128, f(1e4), p, p, p, None) == B.DUO_E_UNSUPPORTED  # N % 256
+    assert L.duo_synth_fill(p, B.DUO_SYNTH_INT8, 1 << 40, 0, 0, 10, None) == B.DUO_E_INVALID
 
 
 def test_product_package_has_no_oracle_or_cpu_fallback():
