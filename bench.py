@@ -42,6 +42,10 @@ KERNEL_SOURCES = {
     "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
     "prefill_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "prefill_chunk_tiles": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "qkv_rope_decode": "mixed_head_kv_amd/csrc/linear_w8.hip",
+    "out_proj_decode": "mixed_head_kv_amd/csrc/linear_w8.hip",
+    "qkv_rope_prefill": "mixed_head_kv_amd/csrc/linear_w8.hip",
+    "out_proj_prefill": "mixed_head_kv_amd/csrc/linear_w8.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -133,6 +137,78 @@ def chunk_tile_bytes(w, t0, T):
         read = min(w.sink, u0 + nq) + (u0 + nq - max(w.sink, u0 - win, t0 - w.recent, 0))
         total += ns * vec * (written + read)
     return total
+
+
+def measure_projections(w, chunk, reps_decode=40, reps_prefill=5):
+    """The 8-bit-weight layers around the attention at the workload's model shape (hidden =
+    n_q_heads * head_dim): the fused QKV projection with the rotary encoding and the output
+    projection, for one decoding token (HBM-bound on the codes) and, when chunk > 0, a
+    pre-filling chunk of that many tokens (MFMA-bound).  Synthetic int8 weights; every
+    launch is stamped at its dispatch (duo_profile_thread_*).  Returns roofline entries
+    (algorithmic work: codes + scales + activations in + outputs for the decoding token,
+    2 M N K flops for the chunk)."""
+    import numpy as np
+    import torch
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+
+    D, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
+    hidden = Hq * D
+    Nqkv = (Hq + 2 * Hkv) * D
+    base = 10000.0 if Hq == Hkv else 500000.0  # Llama-2 (MHA) / Llama-3 (GQA)
+    dev = torch.device("cuda", 0)
+
+    def weights(which, N, K):
+        wt = torch.empty((N, K), dtype=torch.int8, device=dev)
+        B.duo_synth_fill(wt, B.DUO_SYNTH_INT8, w.seed, I.weight_stream(0, which), 0, N * K)
+        return wt, torch.from_numpy(I.weight_scales(w.seed, 0, which, N, K)).to(dev)
+
+    wq, sq = weights("qkv", Nqkv, hidden)
+    wo, so = weights("o", hidden, hidden)
+    out = []
+    for M, reps in ((1, reps_decode), (chunk, reps_prefill)):
+        if M <= 0:
+            continue
+        x = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+        B.duo_synth_fill(x, B.DUO_DTYPE_BF16, w.seed, I.KIND_STREAM["x"], 0, M * hidden)
+        pos = torch.arange(w.context - M, w.context, dtype=torch.int64, device=dev).clamp_(min=0)
+        q = torch.empty((M, Hq, D), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((M, Hkv, D), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+        st = B._stream(torch.cuda.current_stream())
+        for _ in range(2):  # warm-up
+            B.duo_qkv_rope_w8(x, M, hidden, pos, wq, sq, Hq, Hkv, D, base, q, k, v, st)
+            B.duo_linear_w8(q, M, hidden, wo, so, hidden, y, st)
+        torch.cuda.synchronize()
+        B.duo_profile_thread_enable(True)
+        for _ in range(reps):
+            B.duo_qkv_rope_w8(x, M, hidden, pos, wq, sq, Hq, Hkv, D, base, q, k, v, st)
+        for _ in range(reps):
+            B.duo_linear_w8(q, M, hidden, wo, so, hidden, y, st)
+        B.duo_profile_thread_enable(False)
+        tot = B.duo_profile_thread_collect()
+        for cls, name, N in (("qkv_rope", "qkv_rope", Nqkv), ("linear", "out_proj", hidden)):
+            ms, n = tot[cls]
+            us = ms * 1e3 / n
+            if M == 1:
+                work = N * hidden + 4 * N + 2 * hidden + 2 * N + (8 if cls == "qkv_rope" else 0)
+                a = work / (us * 1e-6) / 1e9
+                out.append({"kernel": f"{name}_decode", "bound": "hbm", "achieved": round(a, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                            "avg_launch_us": round(us, 3), "tokens": 1, "n_out": N, "k": hidden,
+                            "traffic": None})
+            else:
+                a = 2.0 * M * N * hidden / (us * 1e-6) / 1e12
+                out.append({"kernel": f"{name}_prefill", "bound": "mfma", "achieved": round(a, 2),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(us, 2),
+                            "tokens": M, "n_out": N, "k": hidden, "traffic": None})
+        del x, q, k, v, y
+    for r in out:
+        r["traffic"] = measured_traffic(r["kernel"], w.name)
+    return out
 
 
 def workload_for(args):
@@ -239,7 +315,7 @@ def run(args):
 
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    totals = {c: [0.0, 0] for c in B.KERNEL_CLASSES}
+    totals = {c: [0.0, 0] for c in B.KERNEL_CLASSES[:5]}
     # Timed steps: the whole path with nothing added.
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -265,8 +341,9 @@ def run(args):
     ms_profiled = ev0.elapsed_time(ev1) / args.steps
     for h in handles:
         for c, (ms, n) in B.duo_profile_collect(h).items():
-            totals[c][0] += ms
-            totals[c][1] += n
+            if c in totals:
+                totals[c][0] += ms
+                totals[c][1] += n
         B.duo_kv_free(h)
     handles.clear()
 
@@ -366,6 +443,9 @@ def run(args):
     # decode step including its append (fused into the decode launch on the MFMA path)
     res["components"]["decode_append_plus_attention_us_per_step"] = round(
         (dec_ms / w.decode_steps + per_app * dec_app_launches) * 1e3, 3)
+    if not args.no_projections and w.io_dtype == "bf16" and w.head_dim == 128:
+        # the linear layers around the attention, measured beside the step (not in it)
+        res["roofline_all"] += measure_projections(w, w.prefill_chunk)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, total, args.cpu_seconds)
     return res
@@ -489,6 +569,9 @@ def run_stack(args, w):
         "cpu_baseline": None,
     }
     B.duo_kv_free(h)
+    if not args.no_projections:
+        # per layer, beside the step: the decoding token's QKV / output projections
+        res["roofline_all"] += measure_projections(w, 0)
     return res
 
 
@@ -635,6 +718,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama2_7b_mha_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-projections", action="store_true",
+                    help="skip the timing of the 8-bit-weight QKV / output projections beside the step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--full-attention", action="store_true",

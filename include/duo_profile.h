@@ -30,7 +30,9 @@ extern "C" {
                                                 queries (MFMA path, chunks over 4096 tokens) */
 #define DUO_KERNEL_DECODE             3  /* split-K decode attention with merge, all heads */
 #define DUO_KERNEL_PREFILL_STAGE      4  /* prefill chunk into retrieval caches + streaming staging */
-#define DUO_KERNEL_CLASSES            5
+#define DUO_KERNEL_QKV_ROPE           5  /* duo_qkv_rope_w8 (thread profiler) */
+#define DUO_KERNEL_LINEAR             6  /* duo_linear_w8 (thread profiler) */
+#define DUO_KERNEL_CLASSES            7
 
 /* on != 0 starts recording, on == 0 stops (recorded events stay until collected). */
 int duo_profile_enable(duo_handle* h, int32_t on);
@@ -38,6 +40,13 @@ int duo_profile_enable(duo_handle* h, int32_t on);
 /* total_ms[DUO_KERNEL_CLASSES], launches[DUO_KERNEL_CLASSES]: filled with the sums
  * since the last collect.  Synchronises on the recorded events. */
 int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches);
+
+/* The same for the calls that take no handle (duo_linear.h), per host thread: while on,
+ * their launches from the calling thread are stamped; collect as above (only the
+ * classes of those calls are non-zero).  Errors: DUO_E_INVALID (NULL output array),
+ * DUO_E_HIP. */
+int duo_profile_thread_enable(int32_t on);
+int duo_profile_thread_collect(double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

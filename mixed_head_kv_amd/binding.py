@@ -30,8 +30,10 @@ DUO_SYNTH_INT8 = 2
 
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
            "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
-           "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8"]
-KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage"]
+           "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8",
+           "duo_profile_thread_enable", "duo_profile_thread_collect"]
+KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage", "qkv_rope",
+                  "linear"]
 
 
 class DuoError(RuntimeError):
@@ -81,6 +83,8 @@ def lib():
         "duo_profile_enable": (ctypes.c_int, [vp, i32]),
         "duo_profile_collect": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
         "duo_linear_w8": (ctypes.c_int, [vp, i64, i32, vp, vp, i32, vp, vp]),
+        "duo_profile_thread_enable": (ctypes.c_int, [i32]),
+        "duo_profile_thread_collect": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
         "duo_qkv_rope_w8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -238,6 +242,19 @@ def duo_profile_collect(h) -> dict:
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()
     _check(lib().duo_profile_collect(h, ms, cnt))
+    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def duo_profile_thread_enable(on: bool):
+    _check(lib().duo_profile_thread_enable(1 if on else 0))
+
+
+def duo_profile_thread_collect() -> dict:
+    """{class name: (total_ms, launches)} of this thread's handle-free calls."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().duo_profile_thread_collect(ms, cnt))
     return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
 
 

@@ -150,7 +150,19 @@ bool make_layout(const duo_config* c, Layout* L) {
 
 }  // namespace
 
-struct duo_handle {
+// Kernel timing (duo_profile.h): event pairs stamped at the dispatch of each launch.
+struct Profiler {
+  bool profiling = false;
+  struct Mark { int cls; hipEvent_t start, stop; };
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> event_pool;
+  ~Profiler() {
+    for (Mark& m : marks) { event_pool.push_back(m.start); event_pool.push_back(m.stop); }
+    for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
+  }
+};
+
+struct duo_handle : Profiler {
   duo_config cfg;
   std::vector<uint8_t> mask;
   char* ws = nullptr;
@@ -169,15 +181,6 @@ struct duo_handle {
   int chunk_override = 0;
   bool use_mfma = false;         // bf16 caches: MFMA prefill + decode (append fused into decode)
   bool use_mfma_decode = false;  // MFMA decode (bf16 or int4 caches)
-  // kernel timing (duo_profile.h)
-  bool profiling = false;
-  struct Mark { int cls; hipEvent_t start, stop; };
-  std::vector<Mark> marks;
-  std::vector<hipEvent_t> event_pool;
-  ~duo_handle() {
-    for (Mark& m : marks) { event_pool.push_back(m.start); event_pool.push_back(m.stop); }
-    for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
-  }
 };
 
 namespace duo {
@@ -191,7 +194,7 @@ namespace {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-hipEvent_t take_event(duo_handle* h) {
+hipEvent_t take_event(Profiler* h) {
   if (!h->event_pool.empty()) {
     hipEvent_t e = h->event_pool.back();
     h->event_pool.pop_back();
@@ -205,10 +208,10 @@ hipEvent_t take_event(duo_handle* h) {
 // Times the one kernel launch made inside its scope when the handle is profiling: the
 // launcher stamps the event pair at the dispatch's own begin and end.
 struct KernelMark {
-  duo_handle* h;
+  Profiler* h;
   int cls;
   hipEvent_t start = nullptr, stop = nullptr;
-  KernelMark(duo_handle* h_, int cls_, hipStream_t) : h(h_), cls(cls_) {
+  KernelMark(Profiler* h_, int cls_, hipStream_t) : h(h_), cls(cls_) {
     if (!h->profiling) return;
     start = take_event(h);
     stop = start ? take_event(h) : nullptr;
@@ -222,7 +225,7 @@ struct KernelMark {
   ~KernelMark() {
     if (!start) return;
     if (duo::launch_events().start == nullptr) {  // the launch took the pair
-      h->marks.push_back(duo_handle::Mark{cls, start, stop});
+      h->marks.push_back(Profiler::Mark{cls, start, stop});
     } else {                                       // nothing was launched
       duo::launch_events() = duo::LaunchEvents{};
       h->event_pool.push_back(start);
@@ -698,15 +701,14 @@ int duo_profile_enable(duo_handle* h, int32_t on) {
   return ok();
 }
 
-int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches) {
-  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+static int collect(Profiler* h, double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return fail(DUO_E_INVALID, "output array is NULL");
   for (int c = 0; c < DUO_KERNEL_CLASSES; ++c) {
     total_ms[c] = 0.0;
     launches[c] = 0;
   }
   int rc = DUO_OK;
-  for (duo_handle::Mark& m : h->marks) {
+  for (Profiler::Mark& m : h->marks) {
     float ms = 0.0f;
     hipError_t e = hipEventSynchronize(m.stop);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, m.start, m.stop);
@@ -718,6 +720,27 @@ int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches) {
   }
   h->marks.clear();
   return rc == DUO_OK ? ok() : rc;
+}
+
+int duo_profile_collect(duo_handle* h, double* total_ms, int64_t* launches) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  return collect(h, total_ms, launches);
+}
+
+// The calls that take no handle record on their host thread's profiler (kept for the
+// thread's life; its few events are not released).
+static Profiler& thread_profiler() {
+  thread_local Profiler* p = new Profiler;
+  return *p;
+}
+
+int duo_profile_thread_enable(int32_t on) {
+  thread_profiler().profiling = on != 0;
+  return ok();
+}
+
+int duo_profile_thread_collect(double* total_ms, int64_t* launches) {
+  return collect(&thread_profiler(), total_ms, launches);
 }
 
 int duo_synth_fill(void* d_out, int32_t dtype, uint64_t seed, uint32_t stream, uint64_t counter0, uint64_t n,
@@ -757,7 +780,11 @@ int duo_linear_w8(const void* x, int64_t M, int32_t K, const int8_t* w, const fl
   a.N = a.n1 = a.n2 = N;
   a.rope_end = 0;
   a.log2_base = 0.0;
-  hipError_t e = duo::launch_w8(a, as_stream(hip_stream));
+  hipError_t e;
+  {
+    KernelMark m(&thread_profiler(), DUO_KERNEL_LINEAR, as_stream(hip_stream));
+    e = duo::launch_w8(a, as_stream(hip_stream));
+  }
   if (e != hipSuccess) return hip_fail(e, "linear_w8");
   return ok();
 }
@@ -789,7 +816,11 @@ int duo_qkv_rope_w8(const void* x, int64_t M, int32_t hidden, const int64_t* pos
   a.n2 = (n_q_heads + n_kv_heads) * head_dim;
   a.rope_end = a.n2;
   a.log2_base = std::log2(static_cast<double>(rope_base));
-  hipError_t e = duo::launch_w8(a, as_stream(hip_stream));
+  hipError_t e;
+  {
+    KernelMark m(&thread_profiler(), DUO_KERNEL_QKV_ROPE, as_stream(hip_stream));
+    e = duo::launch_w8(a, as_stream(hip_stream));
+  }
   if (e != hipSuccess) return hip_fail(e, "qkv_rope_w8");
   return ok();
 }
