@@ -130,6 +130,21 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
 int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v,
                 int32_t n_tokens, void* out, void* hip_stream);
 
+/* Pre-filling for head identification: for every query head, both its full causal
+ * attention (out_full) and its streaming attention, the sinks plus the recent window
+ * (out_streaming), over the same keys.  The method labels heads by an optimization
+ * that compares a head's full-attention and streaming-attention behaviour
+ * (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with Retrieval
+ * and Streaming Heads", abstract: optimization-based identification of the retrieval
+ * heads with synthetic data); the pages give neither its objective nor how the two
+ * outputs are mixed, so this call returns the two outputs and nothing more.  The layer
+ * must hold full caches for every head (its retrieval_mask entries all 1; else
+ * DUO_E_STATE) and use bf16 I/O, head_dim 128 and bf16 caches (else
+ * DUO_E_UNSUPPORTED).  Layouts and chunking as duo_prefill; the chunk's K/V are
+ * appended; out_full and out_streaming are [B, T, Hq, D]. */
+int duo_prefill_dual(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v,
+                     int32_t n_tokens, void* out_full, void* out_streaming, void* hip_stream);
+
 /* Append n_tokens K/V rows (prefill layout, no attention) at positions len .. len+T-1:
  * retrieval heads store every row, streaming heads keep the sinks and the last
  * `recent` tokens (evicting older ones); int4 caches quantise on the way in.  Used to

@@ -29,7 +29,7 @@ DUO_KV_INT4_G128 = 1
 DUO_SYNTH_INT8 = 2
 
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
-           "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
+           "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_prefill_dual", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8",
            "duo_profile_thread_enable", "duo_profile_thread_collect"]
 KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage", "qkv_rope",
@@ -73,6 +73,7 @@ def lib():
         "duo_decode": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "duo_kv_length": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64)]),
         "duo_prefill_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp]),
+        "duo_prefill_dual": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp]),
         "duo_kv_append_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, i32, vp]),
         "duo_kv_length_seq": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(i64)]),
         "duo_kv_free": (None, [vp]),
@@ -168,6 +169,11 @@ def duo_kv_length(h, layer) -> int:
 
 def duo_prefill_seq(h, layer, seq, q, k, v, n_tokens, out, stream=None):
     _check(lib().duo_prefill_seq(h, layer, seq, _ptr(q), _ptr(k), _ptr(v), n_tokens, _ptr(out), _stream(stream)))
+
+
+def duo_prefill_dual(h, layer, q, k, v, n_tokens, out_full, out_streaming, stream=None):
+    _check(lib().duo_prefill_dual(h, layer, _ptr(q), _ptr(k), _ptr(v), n_tokens, _ptr(out_full), _ptr(out_streaming),
+                                  _stream(stream)))
 
 
 def duo_kv_append_seq(h, layer, seq, k, v, n_tokens, stream=None):
@@ -315,6 +321,13 @@ class DuoKV:
             out = torch.empty_like(q)
         duo_prefill_seq(self.h, layer, seq, q, k, v, q.shape[-3], out)
         return out
+
+    def prefill_dual(self, layer, q, k, v):
+        """(full output, streaming output) of every head for a chunk (head identification)."""
+        import torch
+        full, stream = torch.empty_like(q), torch.empty_like(q)
+        duo_prefill_dual(self.h, layer, q, k, v, q.shape[-3], full, stream)
+        return full, stream
 
     def append_seq(self, layer, seq, k, v):
         duo_kv_append_seq(self.h, layer, seq, k, v, k.shape[-3])

@@ -543,6 +543,35 @@ int duo_prefill_seq(duo_handle* h, int32_t layer, int32_t seq, const void* q, co
   return ok();
 }
 
+int duo_prefill_dual(duo_handle* h, int32_t layer, const void* q, const void* k, const void* v, int32_t n_tokens,
+                     void* out_full, void* out_streaming, void* hip_stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(out_full, "out_full")) || (rc = check_ptr(out_streaming, "out_streaming")))
+    return rc;
+  if (!h->use_mfma) return fail(DUO_E_UNSUPPORTED, "both outputs need bf16 I/O, head_dim 128 and bf16 caches");
+  const LayerView& lv = h->views[layer];
+  if (lv.n_str != 0) return fail(DUO_E_STATE, "every KV head of the layer must be a retrieval head (full caches)");
+  int64_t t0 = 0;
+  if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  hipStream_t st = as_stream(hip_stream);
+  hipError_t e;
+  {
+    KernelMark m(h, DUO_KERNEL_PREFILL_STAGE, st);
+    e = duo::launch_chunk_tiles(h->geom, lv, h->stage, k, v, n_tokens, t0, true, 0, 0, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill append");
+  {
+    KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
+    e = duo::launch_prefill_mfma(h->geom, lv, h->stage, q, out_full, n_tokens, t0, 0, h->partials,
+                                 h->partial_floats, h->prefill_counters, h->num_cu, st, out_streaming);
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill attention (both outputs)");
+  for (int32_t b = 0; b < h->cfg.batch; ++b) seq_len(h, layer, b) = t0 + n_tokens;
+  return ok();
+}
+
 int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, int32_t n_tokens, void* hip_stream) {
   int rc = check_layer(h, layer);
   if (rc) return rc;

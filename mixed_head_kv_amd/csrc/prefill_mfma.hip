@@ -116,6 +116,10 @@ struct PrefillArgs {
   CacheRegion stage;    // streaming heads: the staged keys, one region per streaming cache
   int stage_sink_rows;  // streaming heads: staged sink rows (before the window rows)
   int64_t stage_p0;     // streaming heads: position held by the first window row
+  // Both outputs of every head (head identification): when set, every KV head is a
+  // retrieval head and the second grid computes every head's sink + window attention
+  // over the retrieval caches, written here ([B, T, Hq, 128]).
+  uint16_t* out_lambda;
 };
 
 // Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
@@ -338,9 +342,13 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   const int hq = rem / kg.nsplit;
   const int qb = kg.n_qblocks - 1 - hq / kg.n_heads;
   const int head_idx = hq % kg.n_heads;
+  // With both outputs requested the second grid reads the retrieval caches directly (row
+  // = position) instead of staged streaming-cache keys.
+  const bool dual = a.out_lambda != nullptr;
+  const bool staged = streaming && !dual;
   int kvh;
-  const int h = kind_head(a, streaming, head_idx, &kvh);
-  const int64_t cache = int64_t(b) * (streaming ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
+  const int h = kind_head(a, staged, head_idx, &kvh);
+  const int64_t cache = int64_t(b) * (staged ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -420,27 +428,32 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     // wavefront computes a tile when some key of it is visible to one of its queries,
     // masked unless every key is visible to all of them.
     const int S = g.S, R = g.R;
+    const CacheRegion& src = dual ? a.lv.ret : a.stage;
+    const int64_t sink_rows = dual ? 0 : a.stage_sink_rows;  // row of position p0 below
+    const int64_t p0 = dual ? 0 : a.stage_p0;
     const int64_t qa = a.t0 + q_first, qz = a.t0 + q_last;
     const int n_sink = static_cast<int>(((S < qz + 1 ? S : qz + 1) + kTileKeys - 1) / kTileKeys);
     const int64_t lo = qa - R + 1 > S ? qa - R + 1 : S;
-    const int64_t w_first = (a.stage_sink_rows + lo - a.stage_p0) / kTileKeys;
-    const int n_win = lo <= qz ? static_cast<int>((a.stage_sink_rows + qz - a.stage_p0) / kTileKeys - w_first + 1) : 0;
+    const int64_t w_first = (sink_rows + lo - p0) / kTileKeys;
+    const int n_win = lo <= qz ? static_cast<int>((sink_rows + qz - p0) / kTileKeys - w_first + 1) : 0;
     const int ntiles = n_sink + n_win;
     auto tile_row = [&](int ti) -> int64_t {
       return ti < n_sink ? int64_t(ti) * kTileKeys : (w_first + (ti - n_sink)) * kTileKeys;
     };
     const bool live = q_first + 32 * wave <= q_last;  // the wavefront has queries
-    if (ntiles > 0) tile_dma(a.stage, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
+    if (ntiles > 0) tile_dma(src, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
     __syncthreads();
     for (int ti = 0; ti < ntiles; ++ti) {
       const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
       if (ti + 1 < ntiles) {  // the next tile is in flight during the compute
         char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-        tile_dma(a.stage, cache, tile_row(ti + 1), nK, nK + kKBytes, wave, lane, koff);
+        tile_dma(src, cache, tile_row(ti + 1), nK, nK + kKBytes, wave, lane, koff);
       }
+      // (a window tile may cover sink rows too when S is not a multiple of 64: its mask
+      // keeps keys >= S only, the sink tile's keys < S, so no key counts twice)
       const bool sink = ti < n_sink;
       const int64_t row = tile_row(ti);
-      const int64_t p = sink ? row : a.stage_p0 + (row - a.stage_sink_rows);  // position of the first key
+      const int64_t p = sink ? row : p0 + (row - sink_rows);  // position of the first key
       const int64_t p_last = p + kTileKeys - 1;
       bool any, full;
       if (sink) {
@@ -538,7 +551,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   }
   if (q_valid) {
     const float inv = 1.0f / l;
-    uint16_t* orow = a.out + ((int64_t(b) * a.T + my_q) * g.Hq + h) * 128;
+    uint16_t* orow = (streaming && dual ? a.out_lambda : a.out) + ((int64_t(b) * a.T + my_q) * g.Hq + h) * 128;
 #pragma unroll
     for (int jd = 0; jd < 4; ++jd)
 #pragma unroll
@@ -730,8 +743,9 @@ static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheR
 
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
                                int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
-                               int* counters, int num_cu, hipStream_t st) {
+                               int* counters, int num_cu, hipStream_t st, void* out_lambda) {
   PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
+  a.out_lambda = static_cast<uint16_t*>(out_lambda);
   KindGrid& r = a.ret;
   r.n_heads = lv.n_ret * g.G;
   r.n_qblocks = (T + kQRows - 1) / kQRows;
@@ -753,7 +767,17 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
   r.blocks = static_cast<int>(pairs * nsplit);
   a.scratch = scratch;
   a.counters = counters;
-  a.str = streaming_grid(g, lv, 0, nq_streaming);
+  if (out_lambda) {  // every head, every query of the chunk, over the retrieval caches
+    KindGrid& k = a.str;
+    k.n_heads = r.n_heads;
+    k.n_qblocks = r.n_qblocks;
+    k.nsplit = 1;
+    k.q0 = 0;
+    k.nq = T;
+    k.blocks = T > 0 ? g.B * k.n_heads * k.n_qblocks : 0;
+  } else {
+    a.str = streaming_grid(g, lv, 0, nq_streaming);
+  }
   a.stage_p0 = t0 - stage_window_rows(g.R);
   const int64_t blocks = int64_t(r.blocks) + a.str.blocks;
   if (blocks == 0) return hipSuccess;

@@ -32,7 +32,8 @@ def declared_functions():
 def test_headers_declare_the_boundary():
     names = declared_functions()
     for n in ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
-              "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_kv_free", "duo_last_error",
+              "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_prefill_dual", "duo_kv_free",
+              "duo_last_error",
               "duo_synth_fill", "duo_linear_w8", "duo_qkv_rope_w8"]:
         assert n in names
     assert set(names) == set(B.EXPORTS)
@@ -148,6 +149,7 @@ def test_null_handle_calls_fail_cleanly():
     assert L.duo_prefill_seq(None, 0, 0, p, p, p, 4, p, None) == B.DUO_E_INVALID
     assert L.duo_kv_append_seq(None, 0, 0, p, p, 4, None) == B.DUO_E_INVALID
     assert L.duo_kv_length_seq(None, 0, 0, ctypes.byref(n)) == B.DUO_E_INVALID
+    assert L.duo_prefill_dual(None, 0, p, p, p, 4, p, p, None) == B.DUO_E_INVALID
     assert L.duo_kv_read(None, 0, 0, 0, 0, 0, 1, p, None) == B.DUO_E_INVALID
     L.duo_kv_free(None)
     assert L.duo_synth_fill(None, 1, 1, 0, 0, 10, None) == B.DUO_E_INVALID
