@@ -211,6 +211,60 @@ def measure_projections(w, chunk, reps_decode=40, reps_prefill=5):
     return out
 
 
+def measure_identification(w, chunks):
+    """Head-identification pre-filling (duo_prefill_dual) over the workload's chunks with
+    every KV head holding a full cache: every head's full causal output and its
+    sinks + window output.  Algorithmic flops: the causal pairs of every head plus its
+    sink + window pairs (4 D flops each).  One pass after a warm-up pass."""
+    import numpy as np
+    import torch
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+
+    wa = w.scaled(n_retrieval=w.n_kv_heads, fixed_retrieval=None)
+    dev = torch.device("cuda", 0)
+    L = sum(chunks)
+    cfg = B.make_config(1, 1, wa.n_q_heads, wa.n_kv_heads, wa.head_dim, wa.sink, wa.recent, L,
+                        B.DUO_DTYPE_BF16, B.DUO_KV_SAME_AS_IO, np.ones(wa.n_kv_heads, dtype=np.uint8))
+    ws = torch.empty(B.duo_kv_bytes(cfg), dtype=torch.uint8, device=dev)
+
+    def synth(kind, H):
+        t = torch.empty((L, H, wa.head_dim), dtype=torch.bfloat16, device=dev)
+        B.duo_synth_fill(t, B.DUO_DTYPE_BF16, wa.seed, I.KIND_STREAM[kind], 0, t.numel())
+        return t
+
+    Q, K, V = synth("q", wa.n_q_heads), synth("k", wa.n_kv_heads), synth("v", wa.n_kv_heads)
+    of = torch.empty((max(chunks), wa.n_q_heads, wa.head_dim), dtype=torch.bfloat16, device=dev)
+    os_ = torch.empty_like(of)
+    st = B._stream(torch.cuda.current_stream())
+    ms = 0.0
+    for rep in range(2):
+        h = B.duo_kv_init(cfg, ws, st)
+        if rep:
+            B.duo_profile_enable(h, True)
+        t = 0
+        for T in chunks:
+            B.duo_prefill_dual(h, 0, Q[t:t + T], K[t:t + T], V[t:t + T], T, of, os_, st)
+            t += T
+        if rep:
+            ms = B.duo_profile_collect(h)["prefill_retrieval"][0]
+        B.duo_kv_free(h)
+    torch.cuda.synchronize()
+    full = stream = 0
+    t = 0
+    for T in chunks:
+        full += prefill_flops(wa, t, T, True)
+        ws_ = wa.scaled(n_retrieval=0, fixed_retrieval=None)
+        stream += prefill_flops(ws_, t, T, False)
+        t += T
+    a = (full + stream) / (ms * 1e-3) / 1e12
+    return {"kernel": "prefill_dual_attention", "bound": "mfma", "achieved": round(a, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(ms * 1e3 / len(chunks), 2), "ms_per_pass": round(ms, 4),
+            "tokens": L, "traffic": None}
+
+
 def workload_for(args):
     """The named workload, or with --full-attention the same shapes and inputs with every
     KV head a retrieval head (the full-attention baseline of the same kernels)."""
@@ -446,6 +500,8 @@ def run(args):
     if not args.no_projections and w.io_dtype == "bf16" and w.head_dim == 128:
         # the linear layers around the attention, measured beside the step (not in it)
         res["roofline_all"] += measure_projections(w, w.prefill_chunk)
+    if not args.no_identification and w.io_dtype == "bf16" and w.head_dim == 128 and w.kv_format == "same":
+        res["roofline_all"].append(measure_identification(w, chunks))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, total, args.cpu_seconds)
     return res
@@ -718,6 +774,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama2_7b_mha_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-identification", action="store_true",
+                    help="skip the timing of the head-identification pre-filling beside the step")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the timing of the 8-bit-weight QKV / output projections beside the step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
