@@ -808,7 +808,6 @@ int duo_linear_w8(const void* x, int64_t M, int32_t K, const int8_t* w, const fl
   a.K = K;
   a.N = a.n1 = a.n2 = N;
   a.rope_end = 0;
-  a.log2_base = 0.0;
   hipError_t e;
   {
     KernelMark m(&thread_profiler(), DUO_KERNEL_LINEAR, as_stream(hip_stream));
@@ -844,7 +843,7 @@ int duo_qkv_rope_w8(const void* x, int64_t M, int32_t hidden, const int64_t* pos
   a.n1 = n_q_heads * head_dim;
   a.n2 = (n_q_heads + n_kv_heads) * head_dim;
   a.rope_end = a.n2;
-  a.log2_base = std::log2(static_cast<double>(rope_base));
+  for (int j = 0; j < 6; ++j) a.theta_pow[j] = std::pow(static_cast<double>(rope_base), -double(1 << j) / 64.0);
   hipError_t e;
   {
     KernelMark m(&thread_profiler(), DUO_KERNEL_QKV_ROPE, as_stream(hip_stream));

@@ -123,7 +123,7 @@ struct W8Args {
   uint16_t* y2;
   int64_t M;
   int K, N, n1, n2, rope_end;
-  double log2_base;
+  double theta_pow[6];  // base^(-2^j / 64), j = 0..5: theta_d is the product over d's bits
 };
 hipError_t launch_w8(const W8Args& a, hipStream_t st);
 
