@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "out_proj_decode": "mixed_head_kv_amd/csrc/linear_w8.hip",
     "qkv_rope_prefill": "mixed_head_kv_amd/csrc/linear_w8.hip",
     "out_proj_prefill": "mixed_head_kv_amd/csrc/linear_w8.hip",
+    "prefill_dual_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -263,6 +264,22 @@ def measure_identification(w, chunks):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(ms * 1e3 / len(chunks), 2), "ms_per_pass": round(ms, 4),
             "tokens": L, "traffic": None}
+
+
+def run_extras(args):
+    """The projections and the identification pre-filling of the workload, alone."""
+    import torch
+    w = workload_for(args)
+    torch.cuda.set_device(0)
+    chunks = []
+    if w.prefill_chunk:
+        chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
+        if sum(chunks) < w.context:
+            chunks.append(w.context - sum(chunks))
+    roof = measure_projections(w, w.prefill_chunk)
+    if chunks and w.kv_format == "same":
+        roof.append(measure_identification(w, chunks))
+    return {"metric": METRIC, "config": {"workload": w.name}, "roofline_all": roof}
 
 
 def workload_for(args):
@@ -680,6 +697,23 @@ PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4("
                     "prefill_chunk_tiles": ["k_chunk_tiles<false>"]}
 
 
+def extra_kernels(workload):
+    """Kernels of `bench.py --extras-only` (the projections and the identification
+    pre-filling): label -> (name pattern, grid size in threads or None).  The projections'
+    two layers run the same kernel and are told apart by their grids."""
+    import math
+    from mixed_head_kv_amd import inputs as I
+    w = I.WORKLOADS[workload]
+    hidden, nqkv = w.n_q_heads * w.head_dim, (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim
+    out = {"qkv_rope_decode": ("k_w8_gemv<1>", nqkv // 16 * 512), "out_proj_decode": ("k_w8_gemv<1>", hidden // 16 * 512)}
+    if w.prefill_chunk:
+        tm = math.ceil(w.prefill_chunk / 256)
+        out["qkv_rope_prefill"] = ("k_w8_gemm<", tm * nqkv // 256 * 512)
+        out["out_proj_prefill"] = ("k_w8_gemm<", tm * hidden // 256 * 512)
+        out["prefill_dual_attention"] = ("k_prefill_mfma(", None)
+    return out
+
+
 def _csvs(d, suffix):
     import glob
     return sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
@@ -690,9 +724,10 @@ def _short(name):
     return name.split("(")[0]
 
 
-def summarize_stats(d):
+def summarize_stats(d, extras_workload=None):
     """Text table of a `rocprofv3 --kernel-trace --stats` run: calls, mean and total time
-    per kernel, as the profiler reports them."""
+    per kernel, as the profiler reports them.  With extras_workload, also the launches of
+    the extras' kernels split by grid (from the kernel trace)."""
     import csv
     rows = []
     for f in _csvs(d, "kernel_stats.csv"):
@@ -702,10 +737,22 @@ def summarize_stats(d):
     for r in rows:
         lines.append(f"{_short(r['Name'])[:58]:<58} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>10.3f} "
                      f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+    if extras_workload:
+        trace = []
+        for f in _csvs(d, "kernel_trace.csv"):
+            trace += list(csv.DictReader(open(f)))
+        lines.append("")
+        lines.append(f"{'launches by grid':<40} {'grid':>9} {'calls':>7} {'avg_us':>10}")
+        for label, (pat, grid) in extra_kernels(extras_workload).items():
+            ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                  if pat in r["Kernel_Name"] and (grid is None or int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+                                                   * int(r["Grid_Size_Z"]) == grid)]
+            if ds:
+                lines.append(f"{label:<40} {str(grid or 'any'):>9} {len(ds):>7} {sum(ds) / len(ds):>10.3f}")
     return "\n".join(lines)
 
 
-def summarize_traffic(fetch_dir, write_dir, workload):
+def summarize_traffic(fetch_dir, write_dir, workload, extras=False):
     """Per-launch HBM bytes of the path's kernels from two `rocprofv3 --pmc` runs of
     `bench.py --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled
     by what the same counter reads for the probe's 1 GiB device copy.  Updates the
@@ -718,26 +765,33 @@ def summarize_traffic(fetch_dir, write_dir, workload):
         for f in _csvs(d, "counter_collection.csv"):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
-                    per[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+                    per[(r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))] += float(r["Counter_Value"])
         return per
+
+    kmap = ({k: (pat, grid) for k, (pat, grid) in extra_kernels(workload).items()} if extras else
+            {k: (pats, None) for k, pats in PROFILED_KERNELS.items()})
+
+    def match(name, grid, pat, want):
+        pats = pat if isinstance(pat, list) else [pat]
+        return any(p in name for p in pats) and (want is None or grid == want)
 
     out, lines = {}, []
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = load(d, counter)
-        copies = [v for (_, n), v in vals.items() if "copy" in n.lower() or "elementwise" in n.lower()]
+        copies = [v for (_, n, _g), v in vals.items() if "copy" in n.lower() or "elementwise" in n.lower()]
         ref = max(copies)
         factor = (1 << 30) / 1024.0 / ref
         lines.append(f"{counter}: the 1 GiB copy reads {ref:.0f} KiB -> scale factor {factor:.4f}")
         out[counter] = {"factor": factor}
-        for k, pats in PROFILED_KERNELS.items():
-            xs = [v for (_, n), v in vals.items() if any(p in n for p in pats)]
+        for k, (pat, grid) in kmap.items():
+            xs = [v for (_, n, g), v in vals.items() if match(n, g, pat, grid)]
             if xs:
                 out[counter][k] = (len(xs), sum(xs) / len(xs))
     try:
-        entries = [e for e in json.load(open(TRAFFIC_FILE)) if e["kernel"] in PROFILED_KERNELS]
+        entries = [e for e in json.load(open(TRAFFIC_FILE)) if e["kernel"] in KERNEL_SOURCES]
     except (OSError, ValueError):
         entries = []
-    for k in PROFILED_KERNELS:
+    for k in kmap:
         if k not in out["FETCH_SIZE"] or k not in out["WRITE_SIZE"]:
             continue
         n, fk = out["FETCH_SIZE"][k]
@@ -762,11 +816,12 @@ def main():
         sp = argparse.ArgumentParser()
         sp.add_argument("dirs", nargs="+")
         sp.add_argument("--workload", default="llama2_7b_mha_32k")
+        sp.add_argument("--extras", action="store_true", help="the run was `bench.py --extras-only`")
         a = sp.parse_args(sys.argv[2:])
         if sys.argv[1] == "--summarize-stats":
-            print(summarize_stats(a.dirs[0]))
+            print(summarize_stats(a.dirs[0], a.workload if a.extras else None))
         else:
-            print(summarize_traffic(a.dirs[0], a.dirs[1], a.workload))
+            print(summarize_traffic(a.dirs[0], a.dirs[1], a.workload, a.extras))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -778,6 +833,8 @@ def main():
                     help="skip the timing of the head-identification pre-filling beside the step")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the timing of the 8-bit-weight QKV / output projections beside the step")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="run only the projections and the identification pre-filling (for profiling them alone)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--full-attention", action="store_true",
@@ -791,7 +848,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    res = run(args)
+    if args.extras_only:
+        res = run_extras(args)
+    else:
+        res = run(args)
     if args.copy_probe:
         copy_probe()
     print(json.dumps(res), flush=True)
