@@ -16,7 +16,8 @@
 //   k_w8_gemm  (M > 64, pre-filling): 256 x 256 output tiles, 8 wavefronts of 128 x 64,
 //     v_mfma_f32_32x32x16_bf16.  x and code tiles of 64 inputs go HBM -> LDS with direct
 //     loads, three stages deep; each wavefront converts the codes it needs to bf16 in
-//     registers (one sign-extending byte convert per code, exact).
+//     registers (one sign-extending byte convert per code, exact).  Its waits are L2
+//     misses: each XCD's first touch of a 64-input slice of the x and code tiles.
 //   k_w8_gemv  (M <= 64, decoding): HBM-bound on the codes.  A workgroup owns 16 output
 //     channels; its 8 wavefronts split the inputs, each streaming 128-input slices of
 //     the 16 rows with v_mfma_f32_16x16x32_bf16 (channels x tokens), then the partial
@@ -414,13 +415,11 @@ hipError_t launch_gemm(void (*kernel)(W8Args, int, int), const W8Args& a, hipStr
   constexpr int lds = STAGES * Sh::kStageBytes;
   const int tiles_m = static_cast<int>((a.M + Sh::kBM - 1) / Sh::kBM);
   const int tiles_n = a.N / kBN;
-  static bool lds_set = false;  // the attribute allows more than 64 KB of LDS
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    lds_set = true;
-  }
+  // More than 64 KB of dynamic LDS needs the attribute; set once per process (a
+  // thread-safe static), on the device current at the first call.
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
   launch(kernel, dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(Sh::kThreads), lds, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
