@@ -263,7 +263,7 @@ def measure_identification(w, chunks):
     return {"kernel": "prefill_dual_attention", "bound": "mfma", "achieved": round(a, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(ms * 1e3 / len(chunks), 2), "ms_per_pass": round(ms, 4),
-            "tokens": L, "traffic": None}
+            "tokens": L, "traffic": measured_traffic("prefill_dual_attention", w.name)}
 
 
 def run_extras(args):
