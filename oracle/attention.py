@@ -158,3 +158,36 @@ def layer_attention(Q: np.ndarray, positions, K: np.ndarray, V: np.ndarray,
         out[:, h] = head_attention(Q[:, h], positions, K[:, g], V[:, g],
                                    bool(retrieval_kv[g]), sink, recent, scale)
     return out
+
+
+def head_attention_periodic(q: np.ndarray, t: int, K_period: np.ndarray, V_period: np.ndarray,
+                            retrieval: bool, sink: int, recent: int, scale: float | None = None) -> np.ndarray:
+    """Attention of ONE query row at position ``t`` over a history that repeats with
+    period P: the key and value at position j are K_period[j mod P], V_period[j mod P].
+
+    The visible set is the one ``visible`` defines (same passages as ``head_attention``).
+    For a retrieval head it is every position 0..t: position class c (= j mod P) occurs
+    n + [c < r] times, with t + 1 = n P + r, so the softmax over the set equals the
+    softmax over one period with each class's weight multiplied by its count (a sum of
+    equal terms, grouped).  For a streaming head the sink and window positions are listed
+    explicitly.  This lets the oracle check contexts far longer than a history it could
+    hold.  q: [D]; K_period, V_period: [P, D] float64.  Returns [D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    P, D = K_period.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if retrieval:
+        n, r = divmod(int(t) + 1, P)
+        count = np.full(P, float(n))
+        count[:r] += 1.0
+        s = scale * (K_period @ q)
+        s = np.where(count > 0, s, -np.inf)
+        m = s.max()
+        w = count * np.exp(s - m)
+        return (w @ V_period) / w.sum()
+    cand, valid = _candidates(np.array([t]), False, sink, recent)
+    keys = cand[0][valid[0]]
+    kc = K_period[keys % P]
+    s = scale * (kc @ q)
+    e = np.exp(s - s.max())
+    return (e @ V_period[keys % P]) / e.sum()

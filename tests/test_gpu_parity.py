@@ -653,3 +653,34 @@ def test_prefill_dual_needs_full_caches(torch_cuda):
     with pytest.raises(B.DuoError) as e:
         kv.prefill_dual(0, q, k, k)
     assert e.value.code == B.DUO_E_STATE and kv.length(0) == 0
+
+
+def test_int4_decode_at_32m_context_periodic_history(torch_cuda):
+    """One Llama-3-8B-shaped layer (32 query heads, 8 KV heads, 4 of them retrieval, sink
+    64 + recent 256) holding an int4 cache of 2^25 tokens, ten times the pages' longest
+    context: the history repeats one 65536-token block (appended 512 times), so the
+    oracle checks every head exactly through the periodic form of the softmax; then two
+    decode steps whose tokens continue the period."""
+    import torch
+    from mixed_head_kv_amd.binding import DuoKV
+    P, ctx = 1 << 16, 1 << 25
+    w = W("int4_32m", 51, 32, 8, 128, "bf16", 64, 256, ctx, 2, 4, fmt="int4", fixed=(0, 2, 5, 7))
+    say("int4 decode at 2^25 tokens (periodic history)")
+    kv = DuoKV.for_workload(w)
+    K, V = device_synth(w, 0, "k", 0, P), device_synth(w, 0, "v", 0, P)
+    for _ in range(ctx // P):
+        kv.append(0, K, V)
+    torch.cuda.synchronize()
+    assert kv.length(0) == ctx
+    outs = []
+    for t in (ctx, ctx + 1):
+        q = device_synth(w, 0, "q", t, 1)[0]
+        outs.append(kv.decode(0, q, K[t % P], V[t % P]))
+    torch.cuda.synchronize()
+    Kp, Vp = host_history(w, 0, "k", P), host_history(w, 0, "v", P)
+    mask, G = w.mask(0), w.group
+    for t, o in zip((ctx, ctx + 1), outs):
+        qh = OA.upcast(q_rows(w, 0, [t]), w.io_dtype)[0]
+        ref = np.stack([OA.head_attention_periodic(qh[h], t, Kp[:, h // G], Vp[:, h // G], bool(mask[h // G]),
+                                                   w.sink, w.recent) for h in range(w.n_q_heads)])
+        compare(f"int4 2^25 decode t={t}", to_f64(o), ref, TOL["bf16"])

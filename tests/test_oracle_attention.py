@@ -286,3 +286,36 @@ def test_planted_gqa_mapping_mistake_is_caught(monkeypatch):
     wrong = np.stack([A.head_attention(Q[:, h], np.arange(L), K[:, h % Hkv], V[:, h % Hkv],
                                        bool(mask[h % Hkv]), 2, 5) for h in range(Hkv * G)], axis=1)
     assert np.max(np.abs(wrong - mha)) > 1e-3
+
+
+
+@pytest.mark.parametrize("retrieval", [True, False])
+@pytest.mark.parametrize("t", [0, 5, 6, 7, 30, 34, 60])
+def test_periodic_history_equals_the_explicit_history(retrieval, t):
+    """head_attention_periodic against head_attention over the repeated history written
+    out (period 7), below, at and past period boundaries, for both head kinds."""
+    rng = np.random.default_rng(11)
+    P, D = 7, 16
+    Kp, Vp = rng.standard_normal((P, D)), rng.standard_normal((P, D))
+    L = t + 1
+    K = Kp[np.arange(L) % P]
+    V = Vp[np.arange(L) % P]
+    q = rng.standard_normal(D)
+    ref = A.head_attention(q[None], [t], K, V, retrieval, 3, 4)[0]
+    got = A.head_attention_periodic(q, t, Kp, Vp, retrieval, 3, 4)
+    assert np.allclose(got, ref, atol=1e-12, rtol=1e-12)
+
+
+def test_periodic_history_counts_classes_by_multiplicity():
+    """A planted mistake (every class counted once, i.e. the history truncated to one
+    period) fails the comparison."""
+    rng = np.random.default_rng(12)
+    P, D, t = 5, 8, 12
+    Kp, Vp = rng.standard_normal((P, D)) * 3, rng.standard_normal((P, D))
+    q = rng.standard_normal(D)
+    K = Kp[np.arange(t + 1) % P]
+    V = Vp[np.arange(t + 1) % P]
+    ref = A.head_attention(q[None], [t], K, V, True, 0, 1)[0]
+    once = A.head_attention(q[None], [P - 1], Kp, Vp, True, 0, 1)[0]
+    assert not np.allclose(once, ref, atol=1e-6)
+    assert np.allclose(A.head_attention_periodic(q, t, Kp, Vp, True, 0, 1), ref, atol=1e-12)
