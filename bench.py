@@ -325,6 +325,94 @@ def capacity(budget_gb):
             "retrieval_kv_heads": int(w.mask(0).sum()), "sink": w.sink, "recent": w.recent, **res}
 
 
+def capacity_run(args):
+    """Measured capacity: the Llama-3-8B-shaped 32-layer stack with an int4 cache (4 of 8
+    KV heads retrieval, sink 64 + recent 256) at the largest context, in whole 65536-token
+    blocks, whose workspace fits the GPU's free memory less a 4 GB margin.  Every layer's
+    history repeats one synthetic 65536-token block (appended block by block; the cost of
+    the path does not depend on the values, and the parity tests check a periodic history
+    of 2^25 tokens exactly), then `--steps` decode tokens run through all 32 layers.
+    Reports the context, the workspace, the fill rate and the decode time per token with
+    its HBM rate (algorithmic bytes: every cached vector read once per KV head)."""
+    import numpy as np
+    import torch
+
+    from mixed_head_kv_amd import binding as B
+    from mixed_head_kv_amd import inputs as I
+
+    w = I.WORKLOADS["llama3_8b_gqa_32layer_int4_3p3m"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    P = 1 << 16
+    free, _ = torch.cuda.mem_get_info()
+    budget = free - (4 << 30)
+    masks = w.masks().astype(np.uint8)
+
+    def cfg_for(ctx):
+        return B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent,
+                             ctx + args.steps + args.warmup, B.DUO_DTYPE_BF16, B.DUO_KV_INT4_G128, masks)
+    blocks = 1
+    while B.duo_kv_bytes(cfg_for((blocks + 1) * P)) <= budget:
+        blocks += 1
+    ctx = blocks * P
+    cfg = cfg_for(ctx)
+    ws = torch.empty(B.duo_kv_bytes(cfg), dtype=torch.uint8, device=dev)
+    st = B._stream(torch.cuda.current_stream())
+    h = B.duo_kv_init(cfg, ws, st)
+    kb = torch.empty((P, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vb = torch.empty_like(kb)
+    q = torch.empty((w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    n = P * w.n_kv_heads * w.head_dim
+    torch.cuda.synchronize()
+    t_fill = time.perf_counter()
+    for layer in range(w.n_layers):
+        B.duo_synth_fill(kb, B.DUO_DTYPE_BF16, w.seed, layer * 4 + 1, 0, n)
+        B.duo_synth_fill(vb, B.DUO_DTYPE_BF16, w.seed, layer * 4 + 2, 0, n)
+        for _ in range(blocks):
+            B.duo_kv_append(h, layer, kb, vb, P, st)
+        log(f"capacity: layer {layer} filled ({ctx} tokens)")
+    torch.cuda.synchronize()
+    fill_s = time.perf_counter() - t_fill
+    # decode tokens continue the period: position t holds block row t mod P
+    row = kb[0].numel() * kb.element_size()
+
+    def token(t):
+        for layer in range(w.n_layers):
+            B.duo_synth_fill(q, B.DUO_DTYPE_BF16, w.seed, layer * 4, t * q.numel(), q.numel())
+            r = t % P
+            B.duo_decode(h, layer, q, kb.data_ptr() + r * row, vb.data_ptr() + r * row, out, st)
+
+    t = ctx
+    for _ in range(args.warmup):
+        token(t)
+        t += 1
+    torch.cuda.synchronize()
+    B.duo_profile_enable(h, True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        token(t)
+        t += 1
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_token = ev0.elapsed_time(ev1) / args.steps
+    prof = B.duo_profile_collect(h)
+    dec_ms = prof["decode"][0] / args.steps
+    bytes_token = sum(decode_bytes(w, tt, layer) for tt in range(ctx + args.warmup, ctx + args.warmup + args.steps)
+                      for layer in range(w.n_layers)) / args.steps
+    B.duo_kv_free(h)
+    a = bytes_token / (dec_ms * 1e-3) / 1e9
+    return {"metric": "measured capacity: longest int4 context decoded on one GPU", "context_tokens": ctx,
+            "workspace_gb": round(ws.numel() / 1e9, 2), "free_gb_before": round(free / 1e9, 2),
+            "layers": w.n_layers, "fill_s": round(fill_s, 2),
+            "fill_tok_s_per_layer": round(ctx * w.n_layers / fill_s, 1),
+            "decode_ms_per_token": round(ms_token, 3), "decode_kernel_ms_per_token": round(dec_ms, 3),
+            "roofline": {"kernel": "decode_attention", "bound": "hbm", "achieved": round(a, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4)},
+            "vs_pages_context": round(ctx / 3.3e6, 2), "steps": args.steps, "data": "synthetic, periodic (65536)"}
+
+
 def run(args):
     import numpy as np
     import torch
@@ -833,6 +921,8 @@ def main():
                     help="skip the timing of the head-identification pre-filling beside the step")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the timing of the 8-bit-weight QKV / output projections beside the step")
+    ap.add_argument("--capacity-run", action="store_true",
+                    help="decode the int4 32-layer stack at the largest context the GPU's memory holds")
     ap.add_argument("--extras-only", action="store_true",
                     help="run only the projections and the identification pre-filling (for profiling them alone)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -848,7 +938,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    if args.extras_only:
+    if args.capacity_run:
+        res = capacity_run(args)
+    elif args.extras_only:
         res = run_extras(args)
     else:
         res = run(args)
