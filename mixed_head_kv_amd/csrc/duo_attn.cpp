@@ -470,10 +470,14 @@ static int run_prefill(duo_handle* h, const duo::Geom& g, const LayerView& lv, c
       e = duo::launch_chunk_tiles(g, lv, h->stage, k, v, n_tokens, t0, true, 0, nq0, st);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
+    // When every streaming-head query was staged above, the streaming caches' update
+    // (nothing later reads them as they stood) joins the attention launch.
+    const bool fuse_update = n_tokens <= h->stage_tokens;
     {  // retrieval heads and the first staged streaming-head queries, one launch
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
       e = duo::launch_prefill_mfma(g, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,
-                                   h->prefill_counters, h->num_cu, st);
+                                   h->prefill_counters, h->num_cu, st, nullptr, fuse_update ? k : nullptr,
+                                   fuse_update ? v : nullptr);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill attention");
     // further streaming-head queries, at most stage_tokens per launch pair (the staging
@@ -491,7 +495,7 @@ static int run_prefill(duo_handle* h, const duo::Geom& g, const LayerView& lv, c
       }
       if (e != hipSuccess) return hip_fail(e, "prefill attention (streaming)");
     }
-    {
+    if (!fuse_update) {
       KernelMark m(h, DUO_KERNEL_APPEND, st);
       e = duo::launch_stream_cache_update(g, lv, k, v, n_tokens, t0, st);
     }

@@ -48,12 +48,15 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
 // two workgroups per CU) each block's key range is split over two workgroups that merge
 // through `scratch` (fp32 partials, coherent) and `counters` (kPrefillCounters ints,
 // zero between calls).
+// upd_k / upd_v != null: the streaming caches' update with the chunk (K/V inputs) runs
+// in the same launch (valid when no later staging reads the caches as they stood).
 // out_lambda != null (every KV head a retrieval head): the second grid computes every
 // head's sink + window attention over the retrieval caches for all T queries and writes
 // it there, beside the full causal output in `out`.
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
                                int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
-                               int* counters, int num_cu, hipStream_t st, void* out_lambda = nullptr);
+                               int* counters, int num_cu, hipStream_t st, void* out_lambda = nullptr,
+                               const void* upd_k = nullptr, const void* upd_v = nullptr);
 
 // Chunk keys into the layouts the MFMA prefill loads directly (bf16, D = 128), one
 // launch: with `retrieval`, rows [t0, t0 + T) of every retrieval cache (the append);

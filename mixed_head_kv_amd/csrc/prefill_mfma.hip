@@ -37,6 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTileKeys = 64;
 constexpr int kKBytes = kTileKeys * 256;           // K rows, 16-byte chunks XOR-swizzled by row
 constexpr int kVBytes = kTileKeys * 128 * 2;       // 16384
+constexpr int kStageRows = 64;
 constexpr int kQRows = 128;                        // queries per workgroup
 
 __device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -102,6 +103,27 @@ struct KindGrid {
   int blocks;     // B * n_heads * n_qblocks * nsplit
 };
 
+// The per-launch scalars of a chunk-tile pass (k_chunk_tiles below).
+struct ChunkScalars {
+  const uint16_t* k;  // chunk inputs [B, T, Hkv, 128]
+  const uint16_t* v;
+  int T;
+  int64_t t0;
+  int ret_caches;     // blockIdx.y < ret_caches: retrieval append of cache y
+  int64_t ret_tile0;  // first 64-row tile holding a chunk row
+  int ret_tiles;
+  int str_tiles;
+  int64_t ring_lo;    // update: first chunk position kept in the cache (see source_token_fast)
+  int ring_have;      // update: its ring index
+  int64_t u_end;      // staging: end of the launch's query positions
+  int sink_rows;      // staging: Sp
+  int64_t p0;         // staging: position of window row Sp
+};
+
+template <bool UPDATE>
+__device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const CacheRegion& stage, const ChunkScalars& a,
+                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128]);
+
 struct PrefillArgs {
   Geom g;
   LayerView lv;
@@ -120,6 +142,11 @@ struct PrefillArgs {
   // retrieval head and the second grid computes every head's sink + window attention
   // over the retrieval caches, written here ([B, T, Hq, 128]).
   uint16_t* out_lambda;
+  // Blocks [ret.blocks + str.blocks, + upd_blocks): the streaming caches' update with the
+  // chunk (the k_chunk_tiles<true> pass), run in the same launch when every streaming
+  // query of the chunk was staged before it (nothing later reads the cache as it stood).
+  ChunkScalars upd;
+  int upd_blocks;
 };
 
 // Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
@@ -331,6 +358,14 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];  // two tile buffers
 
   const Geom& g = a.g;
+  const int upd0 = a.ret.blocks + a.str.blocks;
+  if (static_cast<int>(blockIdx.x) >= upd0) {  // uniform: a streaming cache update block
+    const int id = static_cast<int>(blockIdx.x) - upd0;
+    chunk_tiles_body<true>(g, a.lv, a.stage, a.upd, id % a.upd.str_tiles, id / a.upd.str_tiles,
+                           reinterpret_cast<uint4(*)[16]>(lds),
+                           reinterpret_cast<uint16_t(*)[128]>(lds + kStageRows * 16 * 16));
+    return;
+  }
   const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
   const KindGrid& kg = streaming ? a.str : a.ret;
   const int id = static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0);
@@ -589,25 +624,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 // contiguous KB of the cache layout (a 1 KB block of a K tile, or 64 dims x 8 keys of a V
 // block).  Storing straight from registers (16 bytes per lane to 64 different lines per
 // instruction) ran at under half the bandwidth.
-constexpr int kStageRows = 64;
 
 struct ChunkTileArgs {
   Geom g;
   LayerView lv;
   CacheRegion stage;
-  const uint16_t* k;  // chunk inputs [B, T, Hkv, 128]
-  const uint16_t* v;
-  int T;
-  int64_t t0;
-  int ret_caches;     // blockIdx.y < ret_caches: retrieval append of cache y
-  int64_t ret_tile0;  // first 64-row tile holding a chunk row
-  int ret_tiles;
-  int str_tiles;
-  int64_t ring_lo;    // update: first chunk position kept in the cache (see source_token_fast)
-  int ring_have;      // update: its ring index
-  int64_t u_end;      // staging: end of the launch's query positions
-  int sink_rows;      // staging: Sp
-  int64_t p0;         // staging: position of window row Sp
+  ChunkScalars s;
 };
 
 // UPDATE: the streaming cache update after the attention (its own instantiation, so
@@ -616,19 +638,27 @@ template <bool UPDATE>
 __global__ void __launch_bounds__(256) k_chunk_tiles(ChunkTileArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_k[kStageRows][16];  // chunk c of row r at [r][c ^ (r & 15)]
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kStageRows][128];
-  const Geom& g = a.g;
-  const bool ret = static_cast<int>(blockIdx.y) < a.ret_caches;
-  if (static_cast<int>(blockIdx.x) >= (ret ? a.ret_tiles : a.str_tiles)) return;  // uniform
+  chunk_tiles_body<UPDATE>(a.g, a.lv, a.stage, a.s, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), s_k,
+                           s_v);
+}
+
+// One 64-row tile (bx) of one cache (by) of a chunk-tile pass; s_k, s_v: this workgroup's
+// LDS (s_k: chunk c of row r at [r][c ^ (r & 15)]).
+template <bool UPDATE>
+__device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const CacheRegion& stage, const ChunkScalars& a,
+                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128]) {
+  const bool ret = by < a.ret_caches;
+  if (bx >= (ret ? a.ret_tiles : a.str_tiles)) return;  // uniform
   const bool update = UPDATE && !ret;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cache = ret ? blockIdx.y : blockIdx.y - a.ret_caches;  // b * n_kind + index
-  const int n_kind = ret ? a.lv.n_ret : a.lv.n_str;
+  const int cache = ret ? by : by - a.ret_caches;  // b * n_kind + index
+  const int n_kind = ret ? lv.n_ret : lv.n_str;
   const int b = cache / n_kind;
-  const int kvh = ret ? a.lv.ret_kv[cache % n_kind] : a.lv.str_kv[cache % n_kind];
-  const int64_t row0 = (ret ? a.ret_tile0 + blockIdx.x : int64_t(blockIdx.x)) * kStageRows;
-  const CacheRegion& held = ret ? a.lv.ret : a.lv.str;  // rows read back from a cache
-  const CacheRegion& dst = ret ? a.lv.ret : (update ? a.lv.str : a.stage);
+  const int kvh = ret ? lv.ret_kv[cache % n_kind] : lv.str_kv[cache % n_kind];
+  const int64_t row0 = (ret ? a.ret_tile0 + bx : int64_t(bx)) * kStageRows;
+  const CacheRegion& held = ret ? lv.ret : lv.str;  // rows read back from a cache
+  const CacheRegion& dst = ret ? lv.ret : (update ? lv.str : stage);
   const uint16_t* hk = reinterpret_cast<const uint16_t*>(held.k);
   const uint16_t* hv = reinterpret_cast<const uint16_t*>(held.v);
   const int ch = tid & 15;
@@ -741,11 +771,33 @@ static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheR
   return a;
 }
 
+// Scalars of the streaming caches' update with chunk rows [t0, t0 + T) (every cache:
+// str_tiles tiles each).
+static ChunkScalars update_scalars(const Geom& g, const LayerView& lv, const void* k, const void* v, int T,
+                                   int64_t t0) {
+  ChunkScalars u = {};
+  u.k = static_cast<const uint16_t*>(k);
+  u.v = static_cast<const uint16_t*>(v);
+  u.T = T;
+  u.t0 = t0;
+  u.str_tiles = static_cast<int>(lv.str.rows / kStageRows);
+  int64_t ring_lo = t0 > g.S ? t0 : g.S;
+  if (ring_lo < t0 + T - g.R) ring_lo = t0 + T - g.R;
+  u.ring_lo = ring_lo;
+  u.ring_have = static_cast<int>((ring_lo - g.S) % g.R);
+  return u;
+}
+
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
                                int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
-                               int* counters, int num_cu, hipStream_t st, void* out_lambda) {
+                               int* counters, int num_cu, hipStream_t st, void* out_lambda, const void* upd_k,
+                               const void* upd_v) {
   PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
   a.out_lambda = static_cast<uint16_t*>(out_lambda);
+  if (upd_k && g.B * lv.n_str > 0) {  // the streaming caches' update joins the launch
+    a.upd = update_scalars(g, lv, upd_k, upd_v, T, t0);
+    a.upd_blocks = a.upd.str_tiles * g.B * lv.n_str;
+  }
   KindGrid& r = a.ret;
   r.n_heads = lv.n_ret * g.G;
   r.n_qblocks = (T + kQRows - 1) / kQRows;
@@ -779,7 +831,7 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
     a.str = streaming_grid(g, lv, 0, nq_streaming);
   }
   a.stage_p0 = t0 - stage_window_rows(g.R);
-  const int64_t blocks = int64_t(r.blocks) + a.str.blocks;
+  const int64_t blocks = int64_t(r.blocks) + a.str.blocks + a.upd_blocks;
   if (blocks == 0) return hipSuccess;
   launch(k_prefill_mfma, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
   return hipGetLastError();
@@ -791,22 +843,22 @@ hipError_t launch_chunk_tiles(const Geom& g, const LayerView& lv, const CacheReg
   a.g = g;
   a.lv = lv;
   a.stage = stage;
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.T = T;
-  a.t0 = t0;
-  a.ret_caches = retrieval && T > 0 ? g.B * lv.n_ret : 0;
-  a.ret_tile0 = t0 / kStageRows;
-  a.ret_tiles = static_cast<int>((t0 + T + kStageRows - 1) / kStageRows - a.ret_tile0);
+  a.s.k = static_cast<const uint16_t*>(k);
+  a.s.v = static_cast<const uint16_t*>(v);
+  a.s.T = T;
+  a.s.t0 = t0;
+  a.s.ret_caches = retrieval && T > 0 ? g.B * lv.n_ret : 0;
+  a.s.ret_tile0 = t0 / kStageRows;
+  a.s.ret_tiles = static_cast<int>((t0 + T + kStageRows - 1) / kStageRows - a.s.ret_tile0);
   const int str_caches = nq > 0 ? g.B * lv.n_str : 0;
-  a.sink_rows = stage_sink_rows(g.S);
+  a.s.sink_rows = stage_sink_rows(g.S);
   const int window_rows = stage_window_rows(g.R);
-  a.str_tiles = str_caches ? (a.sink_rows + window_rows) / kStageRows + (nq + kStageRows - 1) / kStageRows : 0;
-  a.u_end = t0 + q0 + nq;
-  a.p0 = t0 + q0 - window_rows;
-  const int tiles = a.ret_caches && a.ret_tiles > a.str_tiles ? a.ret_tiles : a.str_tiles;
-  if (a.ret_caches + str_caches == 0 || tiles == 0) return hipSuccess;
-  launch(k_chunk_tiles<false>, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(a.ret_caches + str_caches)),
+  a.s.str_tiles = str_caches ? (a.s.sink_rows + window_rows) / kStageRows + (nq + kStageRows - 1) / kStageRows : 0;
+  a.s.u_end = t0 + q0 + nq;
+  a.s.p0 = t0 + q0 - window_rows;
+  const int tiles = a.s.ret_caches && a.s.ret_tiles > a.s.str_tiles ? a.s.ret_tiles : a.s.str_tiles;
+  if (a.s.ret_caches + str_caches == 0 || tiles == 0) return hipSuccess;
+  launch(k_chunk_tiles<false>, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(a.s.ret_caches + str_caches)),
          dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -818,16 +870,8 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
   ChunkTileArgs a = {};
   a.g = g;
   a.lv = lv;
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.T = T;
-  a.t0 = t0;
-  a.str_tiles = static_cast<int>(lv.str.rows / kStageRows);
-  int64_t ring_lo = t0 > g.S ? t0 : g.S;
-  if (ring_lo < t0 + T - g.R) ring_lo = t0 + T - g.R;
-  a.ring_lo = ring_lo;
-  a.ring_have = static_cast<int>((ring_lo - g.S) % g.R);
-  launch(k_chunk_tiles<true>, dim3(static_cast<unsigned>(a.str_tiles), static_cast<unsigned>(caches)), dim3(256), 0,
+  a.s = update_scalars(g, lv, k, v, T, t0);
+  launch(k_chunk_tiles<true>, dim3(static_cast<unsigned>(a.s.str_tiles), static_cast<unsigned>(caches)), dim3(256), 0,
          st, a);
   return hipGetLastError();
 }
