@@ -936,7 +936,7 @@ def main():
         print(json.dumps(capacity(args.capacity)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.capacity_run:
         res = capacity_run(args)

@@ -59,7 +59,7 @@ extern "C" {
 /* Return codes. */
 #define DUO_OK             0
 #define DUO_E_INVALID     -1  /* null / misaligned pointer, value out of range        */
-#define DUO_E_UNSUPPORTED -2  /* valid request this build does not implement          */
+#define DUO_E_UNSUPPORTED -2  /* valid request the library does not implement         */
 #define DUO_E_CAPACITY    -3  /* length + tokens > max_context, or workspace too small */
 #define DUO_E_STATE       -4  /* call not allowed in the handle's current state        */
 #define DUO_E_HIP         -5  /* a HIP runtime call or kernel launch failed            */
@@ -78,7 +78,7 @@ extern "C" {
                                 fp32(q*s + z).  The pages only name a 4-bit KV cache
                                 (hotpaper.ai page, abstract and main results). */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define DUO_MAX_KV_HEADS 64
 #define DUO_MAX_GROUP    16   /* n_q_heads / n_kv_heads */
 
@@ -123,7 +123,7 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
  * sequence; streaming heads to the sinks and the recent window, read from their
  * constant-length cache as it stood before the call plus the chunk itself.  After the
  * call the layer's length is len + T.  int4 caches: DUO_E_UNSUPPORTED (decode-only
- * format in this build).  Every sequence of the batch must hold the same length len
+ * format of the library).  Every sequence of the batch must hold the same length len
  * (else DUO_E_STATE; duo_prefill_seq fills one sequence).  Errors: DUO_E_INVALID
  * (T <= 0, bad layer, null or misaligned pointer), DUO_E_CAPACITY
  * (len + T > max_context). */

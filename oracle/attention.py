@@ -26,7 +26,7 @@ absolute position ``i`` (0-based):
 * scores ``s_ij = c * <q_i, k_j>`` with ``c = 1/sqrt(D)`` unless given, softmax over
   the visible set, output ``o_i = sum_j p_ij v_j``.
 
-Readings where the pages are silent (each listed in the design doc): sinks are the first
+Readings where the pages are silent: sinks are the first
 ``sink`` positions; the recent window counts the current token (``i - j < recent``);
 sink and window overlap is a set union; labels are per KV head and a query head takes
 its KV head's label (MHA and GQA, hotpaper.ai technical-approach section); prefill is

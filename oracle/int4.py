@@ -8,8 +8,7 @@ Heads": abstract, which pairs the method with quantization for 3.3M-token decodi
 Llama-3-8B on one A100; and its key-contributions and main-results sections, which
 name 8-bit weights with a 4-bit KV cache).  The format itself (one group per 128-value
 vector, asymmetric, scale and zero stored as fp16) is the workload's stated format.
-Where neither fixes a step, this module takes the plainest reading, recorded in
-DESIGN.md:
+Where neither fixes a step, this module takes the plainest reading:
 
 For each stored vector x (one token, one KV head, K or V; 128 bfloat16 values):
 

@@ -11,7 +11,7 @@ Retrieval and Streaming Heads" (abstract; the Korean sections on the technical a
 and the main results) states that the method combines with 8-bit weight quantization
 and a 4-bit KV cache, and that Llama-3-8B then decodes 3.3M tokens on one A100.  The
 pages give no weight format and say nothing of position encoding, so this module takes
-the plainest readings (each listed in the design doc):
+the plainest readings:
 
 * 8-bit weights: a linear layer's weight W [N, K] (output channel n, input feature k)
   is held as int8 codes c[n, k] in [-127, 127] and one fp32 scale s[n] per output
