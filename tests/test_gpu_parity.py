@@ -602,6 +602,7 @@ DUAL = {
     "gqa_sink4": (W("dual_gqa", 41, 16, 4, 128, "bf16", 4, 64, 1024, 3, 4), [257, 255, 512]),
     "mha_sink64": (W("dual_mha", 42, 8, 8, 128, "bf16", 64, 256, 1700, 3, 8), [700, 1000]),
     "nosink": (W("dual_nosink", 43, 4, 2, 128, "bf16", 0, 8, 300, 2, 2), [37, 263]),
+    "long_chunk": (W("dual_long", 44, 4, 2, 128, "bf16", 16, 128, 4700, 2, 2), [4600, 100]),
 }
 
 
@@ -684,3 +685,37 @@ def test_int4_decode_at_32m_context_periodic_history(torch_cuda):
         ref = np.stack([OA.head_attention_periodic(qh[h], t, Kp[:, h // G], Vp[:, h // G], bool(mask[h // G]),
                                                    w.sink, w.recent) for h in range(w.n_q_heads)])
         compare(f"int4 2^25 decode t={t}", to_f64(o), ref, TOL["bf16"])
+
+
+
+def test_per_sequence_prefill_with_a_chunk_over_one_staging_pass(torch_cuda):
+    """A batch of two where one sequence takes a 4600-token chunk by itself (its streaming
+    heads need two staged launches, and the streaming caches are updated in a launch of
+    their own) and the other a short one; then decode steps for both at their own
+    positions."""
+    import torch
+    from mixed_head_kv_amd.binding import DuoKV
+    w = W("seq_long", 45, 8, 4, 128, "bf16", 4, 300, 4600, 3, 1, fixed=(2,))
+    lens = [4600, 120]
+    ws = [w.scaled(seed=w.seed + 100 * b) for b in range(2)]
+    say(f"per-sequence prefill lengths={lens}")
+    kv = DuoKV.for_workload(w, batch=2)
+    data, pre = [], []
+    for b, (wb, L) in enumerate(zip(ws, lens)):
+        q, k, v = (device_synth(wb, 0, x, 0, L + w.decode_steps) for x in "qkv")
+        data.append((q, k, v))
+        pre.append(kv.prefill_seq(0, b, q[:L].contiguous(), k[:L].contiguous(), v[:L].contiguous()))
+    dec = []
+    for s in range(w.decode_steps):
+        qs, ks, vs = (torch.stack([data[b][i][lens[b] + s] for b in range(2)]) for i in range(3))
+        dec.append(kv.decode(0, qs, ks, vs))
+    torch.cuda.synchronize()
+    dec = torch.stack(dec, 1)
+    rng = np.random.default_rng(3)
+    for b, wb in enumerate(ws):
+        L, total = lens[b], lens[b] + w.decode_steps
+        rows = np.unique(np.concatenate([np.arange(min(L, 16)), np.arange(max(0, L - 16), L),
+                                         rng.integers(0, L, 48), np.arange(4090, 4110) if L > 4110 else []]))
+        rows = rows.astype(np.int64)
+        compare(f"seq {b} prefill", to_f64(pre[b])[rows], oracle_rows(wb, 0, rows, total), TOL["bf16"])
+        compare(f"seq {b} decode", to_f64(dec[b]), oracle_rows(wb, 0, np.arange(L, total), total), TOL["bf16"])
