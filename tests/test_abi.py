@@ -182,3 +182,22 @@ def test_product_package_has_no_oracle_or_cpu_fallback():
         if fn.endswith((".py", ".hip", ".cpp", ".h")):
             text = open(fn).read()
             assert "import oracle" not in text and "from oracle" not in text, fn
+
+
+def test_capacity_arithmetic_orders_the_layouts():
+    """bench.py --capacity (workspace arithmetic only, no GPU): int4 Duo holds the longest
+    context, then int4 full attention (int4 saves 3.76x, the head split 2x), bf16 Duo,
+    bf16 full attention; the int4 Duo context fits its budget and one more token does
+    not."""
+    _lib_or_skip()
+    import bench
+    from mixed_head_kv_amd import inputs as I
+    import numpy as np
+    r = bench.capacity(288)
+    c = {k: r[k]["max_context"] for k in ("int4_duo", "bf16_duo", "int4_full", "bf16_full")}
+    assert c["int4_duo"] > c["int4_full"] > c["bf16_duo"] > c["bf16_full"] > 1_000_000
+    assert abs(r["int4_duo_vs_bf16_full"] - c["int4_duo"] / c["bf16_full"]) < 0.01
+    w = I.WORKLOADS["llama3_8b_gqa_32layer_int4_3p3m"]
+    cfg = B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent,
+                        c["int4_duo"] + 1, B.DUO_DTYPE_BF16, B.DUO_KV_INT4_G128, w.masks().astype(np.uint8))
+    assert r["int4_duo"]["bytes"] <= 288e9 < B.duo_kv_bytes(cfg)
