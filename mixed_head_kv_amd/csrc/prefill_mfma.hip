@@ -3,7 +3,7 @@
 //   retrieval heads: causal attention of the chunk's queries over every key [0, i],
 //     read from the retrieval cache (the chunk is appended to it first);
 //   streaming heads: the Lambda-shaped mask of sinks [0, S) plus the recent window
-//     (i - R, i], over keys staged (k_stage_streaming) into the same cache layout: the
+//     (i - R, i], over keys staged (k_chunk_tiles) into the same cache layout: the
 //     sink rows, then the window rows of the launch's queries, taken from the chunk
 //     inputs and from the constant-length cache as it stood before the chunk.
 // Source: hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with
