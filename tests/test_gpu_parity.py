@@ -719,3 +719,23 @@ def test_per_sequence_prefill_with_a_chunk_over_one_staging_pass(torch_cuda):
         rows = rows.astype(np.int64)
         compare(f"seq {b} prefill", to_f64(pre[b])[rows], oracle_rows(wb, 0, rows, total), TOL["bf16"])
         compare(f"seq {b} decode", to_f64(dec[b]), oracle_rows(wb, 0, np.arange(L, total), total), TOL["bf16"])
+
+
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_wide_query_groups_match_oracle(torch_cuda, G):
+    """GQA groups of 8 and 16 query heads per KV head (16 fills every column of the decode
+    products): prefill over two chunks, then decode steps, bf16 and int4 caches."""
+    for fmt in ("same", "int4"):
+        hkv = 2
+        w = W(f"group{G}_{fmt}", 60 + G, hkv * G, hkv, 128, "bf16", 4, 48, 600, 4, 1, fmt=fmt, fixed=(1,))
+        say(f"group {G} {fmt}")
+        chunks = [333, 267]
+        kv, pre, dec, total = run_layer(w, chunks, w.decode_steps, append_only_chunks=fmt == "int4")
+        L = sum(chunks)
+        ref = oracle_rows(w, 0, np.arange(0 if pre is not None else L, total), total)
+        if pre is not None:
+            compare(f"G={G} {fmt} prefill", to_f64(pre), ref[:L], TOL["bf16"])
+            compare(f"G={G} {fmt} decode", to_f64(dec), ref[L:], TOL["bf16"])
+        else:
+            compare(f"G={G} {fmt} decode", to_f64(dec), ref, TOL["bf16"])
