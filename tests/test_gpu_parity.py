@@ -739,3 +739,21 @@ def test_wide_query_groups_match_oracle(torch_cuda, G):
             compare(f"G={G} {fmt} decode", to_f64(dec), ref[L:], TOL["bf16"])
         else:
             compare(f"G={G} {fmt} decode", to_f64(dec), ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("name", ["mha64_bf16", "gqa64x2_f32_d64"])
+def test_most_kv_heads_match_oracle(torch_cuda, name):
+    """The largest head count the library accepts (64 KV heads): a bf16 MHA layer whose
+    retrieval heads' decode runs in three splits (1100 keys), and an fp32 head_dim 64 layer
+    with two query heads per KV head (128 query heads; vector-ALU kernels)."""
+    w = {
+        "mha64_bf16": W("mha64_bf16", 70, 64, 64, 128, "bf16", 8, 96, 1100, 3, 16),
+        "gqa64x2_f32_d64": W("gqa64x2_f32_d64", 71, 128, 64, 64, "f32", 4, 40, 300, 2, 20),
+    }[name]
+    chunks = {"mha64_bf16": [700, 400], "gqa64x2_f32_d64": [300]}[name]
+    say(f"64 KV heads: {name}")
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    L = sum(chunks)
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare(f"{name} prefill", to_f64(pre), ref[:L], TOL[w.io_dtype])
+    compare(f"{name} decode", to_f64(dec), ref[L:], TOL[w.io_dtype])
