@@ -227,6 +227,13 @@ def test_failed_calls_leave_state_unchanged(torch_cuda):
     with pytest.raises(B.DuoError) as e:
         B.duo_prefill(kv.h, 1, q, k, v, 4, q)
     assert e.value.code == B.DUO_E_INVALID
+    for n in (0, -3):  # empty and negative token counts: rejected, nothing changes
+        with pytest.raises(B.DuoError) as e:
+            B.duo_prefill(kv.h, 0, q, k, v, n, q)
+        assert e.value.code == B.DUO_E_INVALID and kv.length(0) == 60
+        with pytest.raises(B.DuoError) as e:
+            B.duo_kv_append(kv.h, 0, k, v, n)
+        assert e.value.code == B.DUO_E_INVALID and kv.length(0) == 60
     with pytest.raises(B.DuoError) as e:
         kv.read(0, int(np.nonzero(~w.mask(0))[0][0]), 0, 20, 1)  # evicted from a streaming cache
     assert e.value.code == B.DUO_E_INVALID
