@@ -81,6 +81,7 @@ extern "C" {
 /* Limits of the library. */
 #define DUO_MAX_KV_HEADS 64
 #define DUO_MAX_GROUP    16   /* n_q_heads / n_kv_heads */
+#define DUO_MAX_WINDOW   (1 << 28)  /* largest sink, and largest recent */
 
 typedef struct duo_config {
   int32_t n_layers;     /* >= 1 */
@@ -88,8 +89,9 @@ typedef struct duo_config {
   int32_t n_q_heads;    /* multiple of n_kv_heads */
   int32_t n_kv_heads;   /* 1..DUO_MAX_KV_HEADS */
   int32_t head_dim;     /* 64 or 128 */
-  int32_t sink;         /* attention-sink tokens, >= 0 */
-  int32_t recent;       /* recent-window tokens including the current one, >= 1 */
+  int32_t sink;         /* attention-sink tokens, 0..DUO_MAX_WINDOW */
+  int32_t recent;       /* recent-window tokens including the current one,
+                           1..DUO_MAX_WINDOW (larger: DUO_E_UNSUPPORTED) */
   int32_t io_dtype;     /* DUO_DTYPE_* */
   int32_t kv_format;    /* DUO_KV_* */
   int32_t reserved;     /* must be 0 */
@@ -108,17 +110,27 @@ typedef struct duo_handle duo_handle;
 int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes);
 
 /* Create a handle over a caller-allocated device workspace of `bytes` bytes
- * (>= duo_kv_bytes, 256-byte aligned).  Lays out one retrieval cache per retrieval KV
- * head and one constant-length (sink + recent slots) cache per streaming KV head, per
- * layer and sequence, and clears the scratch counters (one small kernel on `stream`).
- * Every layer starts with length 0.  The workspace must not be used by anything else
- * while the handle lives. */
+ * (>= duo_kv_bytes, 256-byte aligned).  Regroups each layer's KV heads by their label
+ * into a dense list of retrieval heads and a dense list of streaming heads, and lays
+ * out one full cache per retrieval KV head and one constant-length (sink + recent
+ * slots) cache per streaming KV head, per layer and sequence: the two kinds of KV cache
+ * each layer keeps (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM
+ * Inference with Retrieval and Streaming Heads", abstract and technical-approach
+ * section; cn.bg3.co article, DuoAttention 的创新设计).  Clears the workspace (one fill
+ * kernel on `stream`).  Every layer starts with length 0.  The workspace must not be
+ * used by anything else while the handle lives.  Errors: DUO_E_INVALID (bad config,
+ * null or misaligned workspace), DUO_E_UNSUPPORTED, DUO_E_CAPACITY (bytes too small),
+ * DUO_E_HIP (the fill kernel failed to launch; no handle is returned). */
 int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream,
                 duo_handle** out);
 
 /* Causal attention of n_tokens new tokens of `layer` (positions len .. len+T-1) and
  * append of their K/V (pre-filling; a prompt may be split into chunks, one call each,
- * and the result equals one unchunked call).  q, k, v, out: device pointers in the
+ * and the result equals one unchunked call).  The method pre-fills retrieval heads
+ * with full attention and streaming heads over the sinks and recent tokens only
+ * (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM Inference with Retrieval
+ * and Streaming Heads", abstract: lower pre-filling latency; cn.bg3.co article,
+ * 研究背景: full-attention pre-filling cost grows quadratically with the context).  q, k, v, out: device pointers in the
  * prefill layouts above.  Retrieval heads attend to every earlier token of the
  * sequence; streaming heads to the sinks and the recent window, read from their
  * constant-length cache as it stood before the call plus the chunk itself.  After the
@@ -147,7 +159,11 @@ int duo_prefill_dual(duo_handle* h, int32_t layer, const void* q, const void* k,
 
 /* Append n_tokens K/V rows (prefill layout, no attention) at positions len .. len+T-1:
  * retrieval heads store every row, streaming heads keep the sinks and the last
- * `recent` tokens (evicting older ones); int4 caches quantise on the way in.  Used to
+ * `recent` tokens (evicting older ones); int4 caches quantise on the way in.  The two
+ * caches are the method's full cache for retrieval heads and its constant-length cache
+ * of sinks and recent tokens for streaming heads (hotpaper.ai page, abstract and
+ * technical-approach section); the 4-bit format is the one DUO_KV_INT4_G128 states
+ * (same page, abstract and main results: combined with a 4-bit KV cache).  Used to
  * fill long contexts.  Errors as duo_prefill. */
 int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, int32_t n_tokens,
                   void* hip_stream);
@@ -155,7 +171,11 @@ int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, in
 /* One decoding step of `layer`: for every sequence b, appends its k_new / v_new row
  * (decode layout) at position t_b = len_b, the sequence's own length, then its query
  * (decode layout) at position t_b attends to the visible keys (so the new token sees
- * itself), writing out.  If k_new and v_new are both NULL nothing is appended and the
+ * itself), writing out.  Retrieval heads attend over the full cache and streaming
+ * heads over their constant-length cache of sinks and recent tokens (hotpaper.ai page
+ * "DuoAttention: Efficient Long-Context LLM Inference with Retrieval and Streaming
+ * Heads", abstract: decoding speed-up; cn.bg3.co article, 研究背景: decoding cost of
+ * full attention grows linearly with the context).  If k_new and v_new are both NULL nothing is appended and the
  * queries attend at t_b = len_b - 1 (their K/V were appended earlier, e.g. by
  * duo_kv_append).  The lengths may differ between sequences (filled with the
  * per-sequence calls below) when batch <= 32.  Retrieval heads use split-K flash
@@ -202,8 +222,12 @@ const char* duo_last_error(void);
 
 /* Copy the stored K (which = 0) or V (which = 1) vectors of one sequence `b`, KV head
  * `kv_head` of `layer`, for absolute positions pos0 .. pos0+n-1, into d_out
- * ([n, head_dim] float32, device), dequantised for int4 caches with the same device
- * code the attention kernels use.  Positions must be held by sequence b: < len_b for
+ * ([n, head_dim] float32, device).  int4 caches are dequantised to fp32(q*s + z), the
+ * format's value (bit-exact).  The int4 decode kernel does not form these values: it
+ * feeds the codes to the matrix cores and applies s and z algebraically (per key, the
+ * score is s * (sum over d of q_d * code_d) + z * sum over d of q_d, and likewise for
+ * the value side), which equals attention over the dequantised values up to rounding
+ * (held to the bf16 tolerance against the oracle over fp32(q*s + z)).  Positions must be held by sequence b: < len_b for
  * retrieval heads, visible from position len_b - 1 for streaming heads; otherwise
  * DUO_E_INVALID. */
 int duo_kv_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which,

@@ -189,16 +189,16 @@ __global__ void __launch_bounds__(256) k_decode_valu(Geom g, LayerView lv, Decod
 hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q, const void* k, const void* v,
                                void* out, int T, int64_t t0, hipStream_t st) {
   dim3 grid((T + 63) / 64, g.Hq, g.B);
+  // (bf16 with head_dim 128 runs on the MFMA kernels only)
   if (g.io == DUO_DTYPE_F32) {
     if (g.D == 64)
       launch(k_prefill_valu<DUO_DTYPE_F32, 64>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
     else
       launch(k_prefill_valu<DUO_DTYPE_F32, 128>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+  } else if (g.D == 64) {
+    launch(k_prefill_valu<DUO_DTYPE_BF16, 64>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
   } else {
-    if (g.D == 64)
-      launch(k_prefill_valu<DUO_DTYPE_BF16, 64>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
-    else
-      launch(k_prefill_valu<DUO_DTYPE_BF16, 128>, grid, dim3(64), 0, st, g, lv, q, k, v, out, T, t0);
+    return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
@@ -210,14 +210,15 @@ hipError_t launch_decode_valu(const Geom& g, const LayerView& lv, const DecodePl
   dim3 grid(items);
 #define DUO_DECODE_VALU(IO, KVF, D) \
   launch(k_decode_valu<IO, KVF, D>, grid, dim3(256), 0, st, g, lv, p, q, out)
-  if (g.kvfmt == DUO_KV_INT4_G128) {
-    DUO_DECODE_VALU(DUO_DTYPE_BF16, DUO_KV_INT4_G128, 128);
-  } else if (g.io == DUO_DTYPE_F32) {
+  // (int4 caches and bf16 with head_dim 128 run on the MFMA kernels only)
+  if (g.kvfmt == DUO_KV_INT4_G128) return hipErrorNotSupported;
+  if (g.io == DUO_DTYPE_F32) {
     if (g.D == 64) DUO_DECODE_VALU(DUO_DTYPE_F32, DUO_KV_SAME_AS_IO, 64);
     else DUO_DECODE_VALU(DUO_DTYPE_F32, DUO_KV_SAME_AS_IO, 128);
+  } else if (g.D == 64) {
+    DUO_DECODE_VALU(DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO, 64);
   } else {
-    if (g.D == 64) DUO_DECODE_VALU(DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO, 64);
-    else DUO_DECODE_VALU(DUO_DTYPE_BF16, DUO_KV_SAME_AS_IO, 128);
+    return hipErrorNotSupported;
   }
 #undef DUO_DECODE_VALU
   return hipGetLastError();

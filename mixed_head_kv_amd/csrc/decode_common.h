@@ -61,7 +61,7 @@ __device__ inline DecodeItem decode_item(const Geom& g, const LayerView& lv, con
 }
 
 __device__ inline float* partial_ptr(const Geom& g, const DecodePlan& p, int b, int h, int split) {
-  return p.partials + ((int64_t(b) * g.Hq + h) * kMaxSplits + split) * (g.D + 2);
+  return p.partials + ((int64_t(b) * g.Hq + h) * p.max_splits + split) * (g.D + 2);
 }
 
 // Split partials cross workgroups (and XCDs, each with its own L2) inside one launch.

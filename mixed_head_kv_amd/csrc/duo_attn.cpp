@@ -80,6 +80,10 @@ int validate_config(const duo_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DUO_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->sink < 0) return fail(DUO_E_INVALID, "sink must be >= 0");
   if (c->recent < 1) return fail(DUO_E_INVALID, "recent must be >= 1");
+  // Bounded so that every sum of sink, recent and a tile's rows stays within int32
+  // (kernels index the constant-length caches with 32-bit slot counts).
+  if (c->sink > DUO_MAX_WINDOW || c->recent > DUO_MAX_WINDOW)
+    return fail(DUO_E_UNSUPPORTED, "sink and recent above 2^28 tokens each are not supported");
   if (c->max_context < 1 || c->max_context > (int64_t(1) << 40)) return fail(DUO_E_INVALID, "max_context out of range");
   if (c->io_dtype != DUO_DTYPE_F32 && c->io_dtype != DUO_DTYPE_BF16) return fail(DUO_E_INVALID, "unknown io_dtype");
   if (c->kv_format != DUO_KV_SAME_AS_IO && c->kv_format != DUO_KV_INT4_G128)
@@ -178,7 +182,6 @@ struct duo_handle : Profiler {
   int* counters = nullptr;
   int* prefill_counters = nullptr;
   int num_cu = 256;
-  int chunk_override = 0;
   bool use_mfma = false;         // bf16 caches: MFMA prefill + decode (append fused into decode)
   bool use_mfma_decode = false;  // MFMA decode (bf16 or int4 caches)
 };
@@ -246,27 +249,38 @@ int check_ptr(const void* p, const char* name) {
   return DUO_OK;
 }
 
-duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
-  duo::DecodePlan p;
+// Decode plan of `layer` at query position t with split partials in `partials`
+// (max_splits slots per query head) and arrival counters in `counters`.  Returns false
+// (with the error set) when the key range cannot be split within max_splits.
+bool make_plan(const duo_handle* h, int32_t layer, int64_t t, float* partials, int* counters, int max_splits,
+               duo::DecodePlan* out) {
+  duo::DecodePlan& p = *out;
   p.t = t;
   p.varlen = 0;
   for (int b = 0; b < duo::kMaxVarlen; ++b) p.t_seq[b] = t;
-  p.partials = h->partials;
-  p.counters = h->counters;
+  p.partials = partials;
+  p.max_splits = max_splits;
+  p.counters = counters;
   p.k_new = nullptr;
   p.v_new = nullptr;
   p.new_slot = duo::stream_slot(t, h->cfg.sink, h->cfg.recent);
   const int64_t nkeys = t + 1;
   const int64_t batch = h->cfg.batch;
-  // Streaming heads: one split each (no merge) unless the window is long.
-  const int64_t nslots = nkeys < h->cfg.sink + h->cfg.recent ? nkeys : int64_t(h->cfg.sink) + h->cfg.recent;
-  p.chunk_s = int(align_up(uint64_t(nslots < 2048 ? nslots : 2048), 64));
-  p.nsplit_s = int((nslots + p.chunk_s - 1) / p.chunk_s);
+  // Streaming heads: one split each (no merge) up to 2048 slots; a longer window is
+  // split in pieces of at least 2048 slots, and of at least 1/max_splits of the window
+  // so that the split count stays within the partial buffer.
+  const int64_t window = int64_t(h->cfg.sink) + int64_t(h->cfg.recent);
+  const int64_t nslots = nkeys < window ? nkeys : window;
+  int64_t chunk_s = nslots < 2048 ? nslots : 2048;
+  const int64_t min_chunk_s = (nslots + max_splits - 1) / max_splits;
+  if (chunk_s < min_chunk_s) chunk_s = min_chunk_s;
+  chunk_s = int64_t(align_up(uint64_t(chunk_s), 64));
   // Retrieval heads: the decode workgroup fills a CU, so the splits share what the
   // streaming workgroups leave of one workgroup per CU (at least 512 keys per split, a
   // multiple of 64, within the partial buffer).
   const int64_t heads = batch * h->views[layer].n_ret;
-  const int64_t str_wgs = batch * h->views[layer].n_str * p.nsplit_s;
+  const int64_t nsplit_s = (nslots + chunk_s - 1) / chunk_s;
+  const int64_t str_wgs = batch * h->views[layer].n_str * nsplit_s;
   int64_t chunk = 512;
   if (heads > 0) {
     int64_t slots = h->num_cu - str_wgs;
@@ -275,16 +289,22 @@ duo::DecodePlan make_plan(const duo_handle* h, int32_t layer, int64_t t) {
     const int64_t want = (nkeys + per_head - 1) / per_head;
     if (want > chunk) chunk = want;
   }
-  const int64_t max_splits = duo::kMaxSplits;
   const int64_t min_chunk = (nkeys + max_splits - 1) / max_splits;
   if (chunk < min_chunk) chunk = min_chunk;
-  if (h->chunk_override > 0 && h->chunk_override >= min_chunk) chunk = h->chunk_override;
   // a split's K and V are addressed with 32-bit byte offsets (256 bytes per key)
-  if (chunk > (int64_t(1) << 22)) chunk = int64_t(1) << 22;
+  constexpr int64_t kMaxChunk = int64_t(1) << 22;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   chunk = int64_t(align_up(uint64_t(chunk), 64));
+  if (chunk_s > kMaxChunk) chunk_s = kMaxChunk;
   p.chunk_r = int(chunk);
   p.nsplit_r = int((nkeys + chunk - 1) / chunk);
-  return p;
+  p.chunk_s = int(chunk_s);
+  p.nsplit_s = int((nslots + chunk_s - 1) / chunk_s);
+  if (p.nsplit_r > max_splits || p.nsplit_s > max_splits) {
+    fail(DUO_E_UNSUPPORTED, "decode key range needs more splits than the partial buffer holds");
+    return false;
+  }
+  return true;
 }
 
 }  // namespace
@@ -373,13 +393,10 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) h->num_cu = n;
   }
-  if (const char* e = std::getenv("DUO_DECODE_CHUNK")) h->chunk_override = std::atoi(e);
-  // bf16 with head_dim 128 runs on the MFMA kernels; DUO_FORCE_VALU=1 keeps the
-  // vector-ALU kernels (used to compare the two paths).
-  const char* force_valu = std::getenv("DUO_FORCE_VALU");
-  const bool valu = force_valu && force_valu[0] == '1';
-  h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && cfg->kv_format == DUO_KV_SAME_AS_IO && !valu;
-  h->use_mfma_decode = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && !valu;
+  // bf16 with head_dim 128 runs on the MFMA kernels (int4 caches: decode only); fp32
+  // I/O and head_dim 64 on the vector-ALU kernels.
+  h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && cfg->kv_format == DUO_KV_SAME_AS_IO;
+  h->use_mfma_decode = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128;
   // Clear every cache and the counters.  The MFMA kernels read whole 32/64-row tiles
   // and weight rows past the valid length by exactly zero, which needs those rows
   // finite; cleared memory guarantees it.
@@ -613,8 +630,10 @@ int duo_kv_append_seq(duo_handle* h, int32_t layer, int32_t seq, const void* k, 
   return ok();
 }
 
-int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
-               void* hip_stream) {
+// One decoding step (duo_decode) with its split partials and arrival counters in the
+// given scratch (the workspace's, or the library's static array).
+static int run_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
+                      void* hip_stream, float* partials, int* counters, int max_splits) {
   int rc = check_layer(h, layer);
   if (rc) return rc;
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(out, "out"))) return rc;
@@ -637,7 +656,8 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   const LayerView& lv = h->views[layer];
   hipStream_t st = as_stream(hip_stream);
   hipError_t e;
-  duo::DecodePlan p = make_plan(h, layer, tmax);
+  duo::DecodePlan p;
+  if (!make_plan(h, layer, tmax, partials, counters, max_splits, &p)) return DUO_E_UNSUPPORTED;
   if (!uniform) {
     p.varlen = 1;
     for (int32_t b = 0; b < B; ++b) p.t_seq[b] = seq_len(h, layer, b) - (append ? 0 : 1);
@@ -673,6 +693,12 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
   if (append)
     for (int32_t b = 0; b < B; ++b) ++seq_len(h, layer, b);
   return ok();
+}
+
+int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
+               void* hip_stream) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  return run_decode(h, layer, q, k_new, v_new, out, hip_stream, h->partials, h->counters, duo::kMaxSplits);
 }
 
 static int check_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,

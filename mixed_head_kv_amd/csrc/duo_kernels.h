@@ -93,7 +93,8 @@ struct DecodePlan {
   int nsplit_r;
   int chunk_s;        // keys per split, streaming heads
   int nsplit_s;
-  float* partials;    // [B * Hq * kMaxSplits * (D + 2)]
+  float* partials;    // [B * Hq * max_splits * (D + 2)]
+  int max_splits;     // partial slots per query head (at least nsplit_r and nsplit_s)
   int* counters;      // [B * Hkv] arrival counters, zero between calls
   // Fused append (MFMA decode): K/V of the token at position t ([B, Hkv, D]), or null
   // when the token is already in the caches.  It lands in retrieval row t and in

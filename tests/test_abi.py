@@ -88,6 +88,7 @@ def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask
     dict(io_dtype=B.DUO_DTYPE_F32, head_dim=64, max_context=513),
     dict(kv_format=B.DUO_KV_INT4_G128, max_context=3_300_000),
     dict(batch=3, sink=0, recent=1),
+    dict(sink=1 << 28, recent=1 << 28, max_context=64),   # the largest window
 ])
 def test_kv_bytes_matches_layout_arithmetic(kw):
     _lib_or_skip()
@@ -108,6 +109,8 @@ def test_kv_bytes_matches_layout_arithmetic(kw):
     (dict(head_dim=96), B.DUO_E_UNSUPPORTED),
     (dict(sink=-1), B.DUO_E_INVALID),
     (dict(recent=0), B.DUO_E_INVALID),
+    (dict(sink=(1 << 28) + 1), B.DUO_E_UNSUPPORTED),   # windows are bounded so slot sums fit int32
+    (dict(recent=(1 << 28) + 1), B.DUO_E_UNSUPPORTED),
     (dict(max_context=0), B.DUO_E_INVALID),
     (dict(io_dtype=7), B.DUO_E_INVALID),
     (dict(kv_format=3), B.DUO_E_INVALID),

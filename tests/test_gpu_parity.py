@@ -28,6 +28,9 @@ SMALL = {
     "all_streaming_bf16": W("all_streaming_bf16", 16, 4, 2, 128, "bf16", 16, 48, 400, 6, 0),
     "all_retrieval_bf16": W("all_retrieval_bf16", 17, 4, 2, 128, "bf16", 16, 48, 400, 6, 2),
     "nosink_r1_bf16": W("nosink_r1_bf16", 18, 8, 4, 128, "bf16", 0, 1, 300, 5, 1),
+    # a window longer than one decode split (2048 slots): streaming decode in two splits
+    # with a merge, staged prefill over a 2304-row window, the ring wrapped
+    "long_window_bf16": W("long_window_bf16", 19, 8, 4, 128, "bf16", 4, 2300, 3000, 12, 2),
 }
 CHUNKS = {
     "mha_bf16": [100, 156, 1, 300],
@@ -38,6 +41,7 @@ CHUNKS = {
     "all_streaming_bf16": [40, 360],
     "all_retrieval_bf16": [400],
     "nosink_r1_bf16": [37, 263],
+    "long_window_bf16": [1000, 1900, 100],
 }
 
 
