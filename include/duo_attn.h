@@ -186,6 +186,26 @@ int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, in
 int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new,
                void* out, void* hip_stream);
 
+/* ---- Decoding without any allocation -------------------------------------------- */
+/* For callers that cannot allocate device memory at all (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): duo_decode with its split-K
+ * partials and arrival counters in a static device array that the library holds,
+ * DUO_STATIC_SCRATCH_BYTES per GPU (each GPU the library runs on keeps its copy until
+ * the process ends), instead of the handle's workspace.  Same arguments, semantics and
+ * results as duo_decode; it calls no hipMalloc, hipFree or allocating routine.  The
+ * array's address is set up at the first duo_kv_init on each device (with that device
+ * current); the handle uses its init device's array.  Every call on one GPU, from any
+ * handle, shares that array: calls that overlap on one GPU (different streams not
+ * ordered by the caller) race and give wrong results.  The kernels leave the arrival
+ * counters at zero after every call.  Errors: those of duo_decode; DUO_E_CAPACITY when
+ * the batch's arrival counters (batch * n_kv_heads above 16384) or one split of every
+ * query head (batch * n_q_heads * (head_dim + 2) * 4 bytes) do not fit; DUO_E_UNSUPPORTED
+ * when the context needs more splits than fit (the split count shrinks as
+ * batch * n_q_heads grows); DUO_E_HIP when the array's set-up failed. */
+#define DUO_STATIC_SCRATCH_BYTES (16u << 20)
+int duo_decode_static(duo_handle* h, int32_t layer, const void* q, const void* k_new,
+                      const void* v_new, void* out, void* hip_stream);
+
 /* Tokens currently held for `layer` (the position of the next appended token) when
  * every sequence holds the same number; DUO_E_STATE when they differ. */
 int duo_kv_length(const duo_handle* h, int32_t layer, int64_t* out_len);

@@ -27,8 +27,10 @@ DUO_DTYPE_BF16 = 1
 DUO_KV_SAME_AS_IO = 0
 DUO_KV_INT4_G128 = 1
 DUO_SYNTH_INT8 = 2
+DUO_STATIC_SCRATCH_BYTES = 16 << 20
 
-EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_kv_length",
+EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_decode_static",
+           "duo_kv_length",
            "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_prefill_dual", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8",
            "duo_profile_thread_enable", "duo_profile_thread_collect"]
@@ -71,6 +73,7 @@ def lib():
         "duo_prefill": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp]),
         "duo_kv_append": (ctypes.c_int, [vp, i32, vp, vp, i32, vp]),
         "duo_decode": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
+        "duo_decode_static": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "duo_kv_length": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64)]),
         "duo_prefill_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp]),
         "duo_prefill_dual": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp]),
@@ -159,6 +162,10 @@ def duo_kv_append(h, layer, k, v, n_tokens, stream=None):
 
 def duo_decode(h, layer, q, k_new, v_new, out, stream=None):
     _check(lib().duo_decode(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _stream(stream)))
+
+
+def duo_decode_static(h, layer, q, k_new, v_new, out, stream=None):
+    _check(lib().duo_decode_static(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _stream(stream)))
 
 
 def duo_kv_length(h, layer) -> int:

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -25,6 +26,9 @@
 using duo::CacheRegion;
 using duo::Geom;
 using duo::LayerView;
+
+// The static scratch of duo_decode_static (one copy per GPU; see setup_static_scratch).
+static __device__ __align__(256) char scratch[DUO_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -182,6 +186,7 @@ struct duo_handle : Profiler {
   int* counters = nullptr;
   int* prefill_counters = nullptr;
   int num_cu = 256;
+  int device = 0;                // the device current at init (its static scratch serves duo_decode_static)
   bool use_mfma = false;         // bf16 caches: MFMA prefill + decode (append fused into decode)
   bool use_mfma_decode = false;  // MFMA decode (bf16 or int4 caches)
 };
@@ -307,6 +312,77 @@ bool make_plan(const duo_handle* h, int32_t layer, int64_t t, float* partials, i
   return true;
 }
 
+// ---- Static scratch of duo_decode_static ------------------------------------------
+// Device memory that the library holds for callers that cannot allocate: one array per
+// GPU (each device holds its own copy of a __device__ array until the process ends).
+// Its device address is taken once per device with hipGetSymbolAddress, with that
+// device current, at the first duo_kv_init on it; host code uses that address only (the
+// array's name is a host-side stand-in, not a device address).  Layout: arrival
+// counters first (kStaticCounterBytes), then split partials.
+constexpr uint64_t kStaticCounterBytes = 64 << 10;
+static_assert(DUO_STATIC_SCRATCH_BYTES > kStaticCounterBytes, "static scratch too small");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once set up
+int g_scratch_state[kMaxDevices];   // 0: not set up, 1: ready, -1: set-up failed
+std::string g_scratch_err[kMaxDevices];
+
+// Set-up on the current device `dev` (once): the array's device address, and its
+// counters cleared by a fill kernel (the kernels leave every counter at zero after
+// each call, so one clear serves every later call).  The clear is waited for here, so
+// calls on any stream afterwards see zeroed counters.
+void setup_static_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_state[dev] != 0) return;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && ptr == nullptr) e = hipErrorInvalidSymbol;
+  if (e == hipSuccess) e = duo::launch_zero_bytes(ptr, kStaticCounterBytes, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    g_scratch_state[dev] = -1;
+    g_scratch_err[dev] = std::string("static scratch set-up: ") + hipGetErrorString(e);
+    return;
+  }
+  g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  g_scratch_state[dev] = 1;
+}
+
+struct StaticScratch {
+  float* partials;
+  int* counters;
+  int max_splits;
+};
+
+// The static scratch of the handle's device, sized for its decode.
+int static_scratch(const duo_handle* h, StaticScratch* out) {
+  const int dev = h->device;
+  if (dev < 0 || dev >= kMaxDevices) return fail(DUO_E_UNSUPPORTED, "static scratch: device index above 63");
+  char* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_state[dev] != 1)
+      return fail(DUO_E_HIP, g_scratch_state[dev] == 0 ? std::string("static scratch was not set up")
+                                                        : g_scratch_err[dev]);
+    base = g_scratch_ptr[dev];
+  }
+  const uint64_t counters = uint64_t(h->cfg.batch) * h->cfg.n_kv_heads * 4;
+  if (counters > kStaticCounterBytes)
+    return fail(DUO_E_CAPACITY, "static scratch: batch * n_kv_heads above 16384 arrival counters");
+  const uint64_t per_split = uint64_t(h->cfg.batch) * h->cfg.n_q_heads * (h->cfg.head_dim + 2) * 4;
+  uint64_t splits = (DUO_STATIC_SCRATCH_BYTES - kStaticCounterBytes) / per_split;
+  if (splits > uint64_t(duo::kMaxSplits)) splits = duo::kMaxSplits;
+  if (splits < 1)
+    return fail(DUO_E_CAPACITY, "static scratch: one split of every query head needs " + std::to_string(per_split) +
+                                    " bytes, above the library's " + std::to_string(DUO_STATIC_SCRATCH_BYTES - kStaticCounterBytes));
+  out->counters = reinterpret_cast<int*>(base);
+  out->partials = reinterpret_cast<float*>(base + kStaticCounterBytes);
+  out->max_splits = int(splits);
+  return DUO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +468,8 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   if (hipGetDevice(&dev) == hipSuccess) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) h->num_cu = n;
+    h->device = dev;
+    setup_static_scratch(dev);
   }
   // bf16 with head_dim 128 runs on the MFMA kernels (int4 caches: decode only); fp32
   // I/O and head_dim 64 on the vector-ALU kernels.
@@ -699,6 +777,15 @@ int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, c
                void* hip_stream) {
   if (!h) return fail(DUO_E_INVALID, "handle is NULL");
   return run_decode(h, layer, q, k_new, v_new, out, hip_stream, h->partials, h->counters, duo::kMaxSplits);
+}
+
+int duo_decode_static(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
+                      void* hip_stream) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  StaticScratch sc;
+  int rc = static_scratch(h, &sc);
+  if (rc) return rc;
+  return run_decode(h, layer, q, k_new, v_new, out, hip_stream, sc.partials, sc.counters, sc.max_splits);
 }
 
 static int check_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,

@@ -147,6 +147,7 @@ def test_null_handle_calls_fail_cleanly():
     assert L.duo_prefill(None, 0, p, p, p, 4, p, None) == B.DUO_E_INVALID
     assert L.duo_kv_append(None, 0, p, p, 4, None) == B.DUO_E_INVALID
     assert L.duo_decode(None, 0, p, p, p, p, None) == B.DUO_E_INVALID
+    assert L.duo_decode_static(None, 0, p, p, p, p, None) == B.DUO_E_INVALID
     n = ctypes.c_int64()
     assert L.duo_kv_length(None, 0, ctypes.byref(n)) == B.DUO_E_INVALID
     assert L.duo_prefill_seq(None, 0, 0, p, p, p, 4, p, None) == B.DUO_E_INVALID
