@@ -35,6 +35,16 @@ def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _scale_fp16(s32: np.ndarray) -> np.ndarray:
+    """The stored scale: the fp32 quotient rounded to nearest fp16."""
+    return np.asarray(s32, dtype=np.float32).astype(np.float16)
+
+
+def _zero_fp16(mn: np.ndarray) -> np.ndarray:
+    """The stored zero: the vector's minimum rounded to nearest fp16."""
+    return np.asarray(mn, dtype=np.float32).astype(np.float16)
+
+
 def quantize(x_bf16_bits: np.ndarray):
     """Quantise bf16 vectors (uint16 bit patterns, last axis 128).
 
@@ -46,8 +56,8 @@ def quantize(x_bf16_bits: np.ndarray):
     mx = x.max(axis=-1)
     rng = (mx - mn).astype(np.float32)                       # fp32 subtract
     s32 = (rng / np.float32(15.0)).astype(np.float32)        # fp32 divide
-    s16 = s32.astype(np.float16)                             # RN to fp16
-    z16 = mn.astype(np.float16)                              # RN to fp16
+    s16 = _scale_fp16(s32)                                   # RN to fp16
+    z16 = _zero_fp16(mn)                                     # RN to fp16
     s = s16.astype(np.float32)[..., None]
     z = z16.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):

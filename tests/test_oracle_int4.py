@@ -1,9 +1,12 @@
 """Pins for the int4 KV codec oracle (CPU only).
 
-Checked against: hand-derived worked examples (tests/golden), a brute-force nearest
-code search, exact rational arithmetic for the dequantised value, the error bound the
-format implies, and degenerate inputs.  Planted mistakes (wrong nibble order, round
-half away from zero, zero not rounded to fp16) are shown to fail a pin.
+Checked against: hand-derived worked examples (tests/golden: a 0.25 grid, half-even
+ties, a range whose fifteenth is not an fp32 number so the scale's fp32-then-fp16
+rounding decides a code, and a minimum that rounds to an fp16 zero of -0), a
+brute-force nearest code search, exact rational arithmetic for the dequantised value,
+the error bound the format implies, and degenerate inputs.  Planted mistakes (wrong
+nibble order, round half away from zero, scale left in fp32, zero not rounded to
+fp16) are shown to fail a pin.
 """
 
 import json
@@ -151,3 +154,25 @@ def test_planted_nibble_swap_is_caught():
     swapped = ((codes >> 4) | (codes << 4)).astype(np.uint8)
     assert swapped.tolist() != c["codes"]
     assert not np.array_equal(Q.dequantize(swapped, s, z), np.asarray(c["x"], np.float32))
+
+
+def _golden(name):
+    return next(c for c in json.load(open(GOLDEN))["cases"] if c["name"] == name)
+
+
+def test_planted_scale_left_in_fp32_is_caught(monkeypatch):
+    """A quantiser that divides by the fp32 quotient instead of its fp16 rounding puts
+    x = 0 of the inexact-range example in code 7 instead of 8."""
+    c = _golden("inexact_range_over_15")
+    monkeypatch.setattr(Q, "_scale_fp16", lambda s32: np.asarray(s32, dtype=np.float32))
+    codes, _, _ = Q.quantize(_bf16(c["x"]))
+    assert codes.tolist() != c["codes"]
+
+
+def test_planted_zero_not_rounded_to_fp16_is_caught(monkeypatch):
+    """A quantiser that subtracts the unrounded minimum moves every code of the
+    subnormal-grid example up by one."""
+    c = _golden("zero_rounds_to_fp16_subnormal_grid")
+    monkeypatch.setattr(Q, "_zero_fp16", lambda mn: np.asarray(mn, dtype=np.float32))
+    codes, _, _ = Q.quantize(_bf16(c["x"]))
+    assert codes.tolist() != c["codes"]
