@@ -2,6 +2,9 @@
 
     python -m mixed_head_kv_amd.build          # compile every source, link the library
 
+It also builds libduo_inputs.so, the host (C, OpenMP) twin of the seeded input
+generator that the tests and the bench's CPU baseline use for long histories.
+
 Every HIP source compiles with packed-fp32 instructions disabled and with correctly
 rounded fp32 division (the int4 quantiser's divisions must round like the format's
 definition).  Objects go to mixed_head_kv_amd/_build/, the library next to this file.
@@ -59,8 +62,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+INPUTS_SRC = os.path.join(HERE, "inputs_host.c")
+INPUTS_LIB = os.path.join(HERE, "libduo_inputs.so")
+
+
+def build_inputs(verbose: bool = False) -> str:
+    """The host twin of the seeded input generator (plain C, gcc with OpenMP)."""
+    tmp = INPUTS_LIB + ".tmp"
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", INPUTS_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed for inputs_host.c:\n" + r.stdout + r.stderr)
+    os.replace(tmp, INPUTS_LIB)
+    return INPUTS_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    build_inputs(verbose)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))

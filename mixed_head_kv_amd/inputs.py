@@ -8,8 +8,9 @@ oracle.  It defines:
   context lengths, chunking);
 * the per-layer retrieval masks (a seeded choice of KV heads);
 * a counter-based generator for Q, K and V, so that any slice of a multi-gigabyte
-  input can be produced independently on the host (this module, NumPy) or on the
-  device (a HIP fill kernel implementing the same published definition), bit for bit.
+  input can be produced independently on the host (this module, NumPy, or its C twin
+  inputs_host.c when built) or on the device (a HIP fill kernel implementing the same
+  published definition), bit for bit.
 
 Generator definition (SplitMix64, Steele, Lea and Flood, "Fast Splittable
 Pseudorandom Number Generators", OOPSLA 2014): with GAMMA = 0x9E3779B97F4A7C15 and the
@@ -57,6 +58,27 @@ WEIGHT_STREAM = {"qkv": 0, "o": 1}
 CODE_MULT = np.float32(32.0)
 
 _CHUNK = 1 << 22  # counters per NumPy pass (bounds host memory)
+
+# The same generator in C (inputs_host.c, OpenMP), used when built: identical values,
+# far faster for the multi-gigabyte histories of the long-context workloads.
+_HOST_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libduo_inputs.so")
+_host = None
+
+
+def _host_lib():
+    global _host
+    if _host is None:
+        _host = False
+        if os.path.exists(_HOST_LIB):
+            import ctypes
+            L = ctypes.CDLL(_HOST_LIB)
+            vp = ctypes.c_void_p
+            L.duo_inputs_head_rows.argtypes = [ctypes.c_uint64, ctypes.c_uint32, vp, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_float, vp, vp]
+            L.duo_inputs_range.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                                           ctypes.c_float, vp, vp]
+            _host = L
+    return _host or None
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -124,19 +146,36 @@ def _cast(x32: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def synth(seed: int, layer: int, kind: str, pos0: int, T: int, H: int, D: int, dtype: str) -> np.ndarray:
+def synth(seed: int, layer: int, kind: str, pos0: int, T: int, H: int, D: int, dtype: str,
+          use_host_lib: bool = True) -> np.ndarray:
     """Tensor [T, H, D] for positions [pos0, pos0 + T) of one layer.
 
     dtype "f32" -> float32; "bf16" -> uint16 bf16 bit patterns."""
     stream = layer * 4 + KIND_STREAM[kind]
+    L = _host_lib() if use_host_lib else None
+    if L is not None and dtype in ("f32", "bf16"):
+        out = np.empty((T, H, D), dtype=np.float32 if dtype == "f32" else np.uint16)
+        ptr = out.ctypes.data
+        L.duo_inputs_range(seed, stream, pos0 * H * D, T * H * D, float(SCALE_F32),
+                           ptr if dtype == "f32" else None, ptr if dtype == "bf16" else None)
+        return out
     c0 = np.uint64(pos0) * np.uint64(H * D)
     counters = c0 + np.arange(T * H * D, dtype=np.uint64)
     return _cast(values_f32(seed, stream, counters), dtype).reshape(T, H, D)
 
 
-def synth_head(seed: int, layer: int, kind: str, positions, head: int, H: int, D: int, dtype: str) -> np.ndarray:
+def synth_head(seed: int, layer: int, kind: str, positions, head: int, H: int, D: int, dtype: str,
+               use_host_lib: bool = True) -> np.ndarray:
     """Rows [n, D] of one head at the given absolute positions (strided counters)."""
     stream = layer * 4 + KIND_STREAM[kind]
+    L = _host_lib() if use_host_lib else None
+    if L is not None and dtype in ("f32", "bf16"):
+        pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(-1))
+        out = np.empty((len(pos), D), dtype=np.float32 if dtype == "f32" else np.uint16)
+        ptr = out.ctypes.data
+        L.duo_inputs_head_rows(seed, stream, pos.ctypes.data, len(pos), head, H, D, float(SCALE_F32),
+                               ptr if dtype == "f32" else None, ptr if dtype == "bf16" else None)
+        return out
     pos = np.asarray(positions, dtype=np.uint64).reshape(-1)
     counters = (pos[:, None] * np.uint64(H) + np.uint64(head)) * np.uint64(D) + np.arange(D, dtype=np.uint64)[None, :]
     return _cast(values_f32(seed, stream, counters), dtype)

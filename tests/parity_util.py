@@ -3,6 +3,8 @@ C-ABI binding) and through the oracle on the same seeded inputs, and compare."""
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 import time
 
@@ -48,42 +50,86 @@ def host_history(w: I.Workload, layer: int, kind: str, L: int) -> np.ndarray:
     return OA.upcast(raw, w.io_dtype)
 
 
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
 def head_history(w: I.Workload, layer: int, kind: str, g: int, positions) -> np.ndarray:
     """K or V rows [n, D] (float64) of KV head g at the given positions, as the cache
-    holds them (int4: the oracle codec's dequantised values).  Processed in slices so a
-    3.3M-token head fits in host memory."""
+    holds them (int4: the oracle codec's dequantised values).  Processed in slices, in
+    parallel threads (each vector is quantised on its own), so a 3.3M-token head is
+    prepared in seconds and fits in host memory."""
     positions = np.asarray(positions, dtype=np.int64)
     out = np.empty((len(positions), w.head_dim), dtype=np.float64)
-    step = 1 << 18
-    for a in range(0, len(positions), step):
+    step = 1 << 16
+
+    def fill(a):
         raw = I.synth_head(w.seed, layer, kind, positions[a:a + step], g, w.n_kv_heads, w.head_dim, w.io_dtype)
         if w.kv_format == "int4":
             codes, s, z = OQ.quantize(raw)
             out[a:a + step] = OQ.dequantize(codes, s, z)
         else:
             out[a:a + step] = OA.upcast(raw, w.io_dtype)
+
+    starts = list(range(0, len(positions), step))
+    if len(starts) <= 1:
+        for a in starts:
+            fill(a)
+    else:
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            list(ex.map(fill, starts))
     return out
 
 
-def oracle_decode_rows(w: I.Workload, layer: int, t: int, kv_heads, q) -> dict:
-    """Oracle decode output at position t for the query heads of the given KV heads.
-    q: [Hq, D] stored query values (upcast here).  Returns {query head: [D]}."""
+def oracle_decode_steps(w: I.Workload, layer: int, t0: int, n_steps: int, kv_heads, q) -> dict:
+    """Oracle decode outputs at positions t0 .. t0 + n_steps - 1 (one token per step, the
+    history through each step's own position) for the query heads of the given KV heads.
+    q: [n_steps, Hq, D] stored query values.  Returns {query head: [n_steps, D]}.  Each
+    KV head's history is prepared once; KV heads run in parallel threads."""
     qf = OA.upcast(q, w.io_dtype)
     mask = w.mask(layer)
-    out = {}
-    for g in kv_heads:
+    t_last = t0 + n_steps - 1
+    pos_q = np.arange(t0, t0 + n_steps)
+
+    def one(g):
         if mask[g]:
-            pos = np.arange(t + 1)
-        else:
-            pos = np.array([j for j in range(min(w.sink, t + 1))] +
-                           [j for j in range(max(w.sink, t - w.recent + 1), t + 1)])
-        K = np.zeros((t + 1, w.head_dim))
-        V = np.zeros((t + 1, w.head_dim))
-        K[pos] = head_history(w, layer, "k", g, pos)
-        V[pos] = head_history(w, layer, "v", g, pos)
-        for i in range(w.group):
-            h = g * w.group + i
-            out[h] = OA.head_attention(qf[h][None], [t], K, V, bool(mask[g]), w.sink, w.recent)[0]
+            pos = np.arange(t_last + 1)
+            K = head_history(w, layer, "k", g, pos)
+            V = head_history(w, layer, "v", g, pos)
+        else:  # the sinks and every step's window (other rows are never visible)
+            pos = np.unique(np.concatenate([np.arange(min(w.sink, t_last + 1)),
+                                            np.arange(max(0, t0 - w.recent + 1), t_last + 1)]))
+            K = np.zeros((t_last + 1, w.head_dim))
+            V = np.zeros((t_last + 1, w.head_dim))
+            K[pos] = head_history(w, layer, "k", g, pos)
+            V[pos] = head_history(w, layer, "v", g, pos)
+        return {g * w.group + i: OA.head_attention(qf[:, g * w.group + i], pos_q, K, V, bool(mask[g]), w.sink,
+                                                   w.recent)
+                for i in range(w.group)}
+
+    out = {}
+    with cf.ThreadPoolExecutor(min(len(kv_heads), 4)) as ex:  # (each history is gigabytes)
+        for d in ex.map(one, kv_heads):
+            out.update(d)
+    return out
+
+
+def oracle_rows_threaded(w: I.Workload, layer: int, rows, total: int, heads=None) -> np.ndarray:
+    """Oracle outputs [len(rows), Hq, D] at absolute positions `rows`, like oracle_rows,
+    with the query heads computed in parallel threads (NumPy releases the interpreter
+    lock inside its array operations)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Kh = host_history(w, layer, "k", total)
+    Vh = host_history(w, layer, "v", total)
+    Qh = OA.upcast(q_rows(w, layer, rows), w.io_dtype)
+    mask = w.mask(layer)
+    out = np.full((len(rows), w.n_q_heads, w.head_dim), np.nan)
+
+    def one(h):
+        g = h // w.group
+        out[:, h] = OA.head_attention(Qh[:, h], rows, Kh[:, g], Vh[:, g], bool(mask[g]), w.sink, w.recent)
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(one, range(w.n_q_heads) if heads is None else heads))
     return out
 
 

@@ -9,8 +9,8 @@ from mixed_head_kv_amd import inputs as I
 from oracle import attention as OA
 from oracle import int4 as OQ
 
-from parity_util import (TOL, compare, device_synth, fill_stack, host_history, oracle_decode_rows, oracle_rows,
-                         q_rows, run_layer, say, to_f64)
+from parity_util import (TOL, compare, device_synth, fill_stack, host_history, oracle_decode_steps, oracle_rows,
+                         oracle_rows_threaded, q_rows, run_layer, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -247,60 +247,55 @@ def test_failed_calls_leave_state_unchanged(torch_cuda):
 
 def test_llama2_7b_mha_32k_layer(torch_cuda):
     """32 heads (8 retrieval), head_dim 128, bf16, 8 prefill chunks of 4096 and 128 decode
-    steps.  Every decode output is checked; prefill rows are sampled: the first 64 and last
-    64 rows of every chunk, +-R rows around every chunk boundary, 128 seeded rows per chunk."""
+    steps.  Every prefill and every decode output of every head is checked."""
     w = I.WORKLOADS["llama2_7b_mha_32k"]
     say("llama2_7b_mha_32k")
     chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
     kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
-    rng = np.random.default_rng(0)
-    rows = set()
-    for c in range(len(chunks)):
-        a = c * w.prefill_chunk
-        b = a + w.prefill_chunk
-        rows |= set(range(a, a + 64)) | set(range(b - 64, b))
-        rows |= set(range(max(0, a - w.recent - 2), min(w.context, a + w.recent + 2)))
-        rows |= set(rng.integers(a, b, 128).tolist())
-    rows = np.array(sorted(rows))
-    ref_dec = oracle_rows(w, 0, np.arange(w.context, total), total)
-    compare("32k decode", to_f64(dec), ref_dec, TOL["bf16"])
-    ref_pre = oracle_rows(w, 0, rows, total)
-    compare("32k prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
+    got = np.concatenate([to_f64(pre), to_f64(dec)], 0)
+    say("  oracle: every row of every head")
+    ref = oracle_rows_threaded(w, 0, np.arange(total), total)
+    compare("32k prefill (every row)", got[:w.context], ref[:w.context], TOL["bf16"])
+    compare("32k decode (every step)", got[w.context:], ref[w.context:], TOL["bf16"])
 
 
 def test_llama3_8b_gqa_128k_layer(torch_cuda):
     """32 query / 8 KV heads (4 retrieval), head_dim 128, bf16, 16 prefill chunks of 8192
-    and 256 decode steps.  Checked: every decode output of the first and last 8 steps
-    (all heads); prefill rows: first and last 16 rows of every chunk, +-4 rows around
-    every chunk boundary and window edge, 24 seeded rows per chunk (all heads)."""
+    and 256 decode steps.  Checked, all heads: every decode step; prefill rows: the whole
+    first chunk, the last 256 rows of the last chunk, +-R rows around every chunk
+    boundary, and 256 seeded rows per chunk."""
     w = I.WORKLOADS["llama3_8b_gqa_128k"]
     say("llama3_8b_gqa_128k")
     chunks = [w.prefill_chunk] * (w.context // w.prefill_chunk)
     kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
     rng = np.random.default_rng(1)
-    rows = set()
+    rows = set(range(w.prefill_chunk)) | set(range(w.context - 256, w.context))
     for c in range(len(chunks)):
         a, b = c * w.prefill_chunk, (c + 1) * w.prefill_chunk
-        rows |= set(range(a, a + 16)) | set(range(b - 16, b))
-        for e in (a, a + w.recent - 1, a + w.recent):
-            rows |= set(range(max(0, e - 4), min(w.context, e + 4)))
-        rows |= set(rng.integers(a, b, 24).tolist())
+        rows |= set(range(max(0, a - w.recent), min(w.context, a + w.recent)))
+        rows |= set(rng.integers(a, b, 256).tolist())
     rows = np.array(sorted(rows))
-    steps = list(range(8)) + list(range(w.decode_steps - 8, w.decode_steps))
-    ref_dec = oracle_rows(w, 0, np.array([w.context + s for s in steps]), total)
-    compare("128k decode (first/last 8 steps)", to_f64(dec[steps]), ref_dec, TOL["bf16"])
-    ref_pre = oracle_rows(w, 0, rows, total)
-    compare("128k prefill (sampled rows)", to_f64(pre[rows]), ref_pre, TOL["bf16"])
+    say(f"  oracle: {len(rows)} prefill rows and {w.decode_steps} decode steps, all heads")
+    ref = oracle_rows_threaded(w, 0, np.concatenate([rows, np.arange(w.context, total)]), total)
+    compare("128k decode (every step)", to_f64(dec), ref[len(rows):], TOL["bf16"])
+    compare("128k prefill (sampled rows)", to_f64(pre[rows]), ref[:len(rows)], TOL["bf16"])
     assert np.isfinite(to_f64(dec)).all() and np.isfinite(to_f64(pre)).all()
 
 
-def _stack_decode_check(torch_cuda, name, steps, check_heads):
+STACK_LAYERS = (0, 15, 31)
+
+
+def _stack_decode_check(torch_cuda, name, steps):
+    """Fill every layer to the workload's context with kv_append, decode `steps` tokens
+    through all 32 layers; layers 0, 15 and 31 are checked on every KV head (all query
+    heads) at every step, every other layer finite at every step."""
     from mixed_head_kv_amd.binding import DuoKV
     w = I.WORKLOADS[name].scaled(decode_steps=steps)
     say(f"{name}: fill {w.n_layers} layers x {w.context} tokens")
     kv = DuoKV.for_workload(w)
     fill_stack(w, kv)
-    outs = {}
+    outs = {l: [] for l in STACK_LAYERS}
+    qs = {l: [] for l in STACK_LAYERS}
     for s in range(steps):
         t = w.context + s
         for layer in range(w.n_layers):
@@ -308,39 +303,30 @@ def _stack_decode_check(torch_cuda, name, steps, check_heads):
             k = device_synth(w, layer, "k", t, 1)[0]
             v = device_synth(w, layer, "v", t, 1)[0]
             o = kv.decode(layer, q, k, v)
-            if layer in check_heads and s == steps - 1:
-                outs[layer] = (to_f64(o), q.cpu())
-            elif s == steps - 1:
-                assert torch_cuda.isfinite(o.float()).all()
-    for layer, heads in check_heads.items():
-        got, q = outs[layer]
-        qb = q.view(torch_cuda.int16).numpy().view(np.uint16)
-        say(f"  oracle: layer {layer} KV heads {heads}")
-        ref = oracle_decode_rows(w, layer, w.context + steps - 1, heads, qb)
-        hs = sorted(ref)
-        compare(f"{name} layer {layer} decode", got[hs], np.stack([ref[h] for h in hs]), TOL["bf16"])
+            if layer in outs:
+                outs[layer].append(to_f64(o))
+                qs[layer].append(q.cpu().view(torch_cuda.int16).numpy().view(np.uint16))
+            else:
+                assert torch_cuda.isfinite(o.float()).all(), (layer, s)
     kv.close()
+    for layer in STACK_LAYERS:
+        say(f"  oracle: layer {layer}, all 8 KV heads, {steps} steps")
+        ref = oracle_decode_steps(w, layer, w.context, steps, list(range(w.n_kv_heads)), np.stack(qs[layer]))
+        got = np.stack(outs[layer])  # [steps, Hq, D]
+        refa = np.stack([ref[h] for h in range(w.n_q_heads)], 1)
+        compare(f"{name} layer {layer} decode ({steps} steps)", got, refa, TOL["bf16"])
 
 
 def test_llama3_8b_gqa_32layer_1m_stack(torch_cuda):
-    """32-layer GQA stack, 1,048,576-token bf16 caches filled by kv_append, 2 decode steps
-    through all layers; the last step checked on layer 0 (all 8 KV heads) and layer 31
-    (one retrieval and one streaming KV head), every other layer checked finite."""
-    w = I.WORKLOADS["llama3_8b_gqa_32layer_1m"]
-    m31 = w.mask(31)
-    heads31 = [int(np.nonzero(m31)[0][0]), int(np.nonzero(~m31)[0][0])]
-    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_1m", 2, {0: list(range(8)), 31: heads31})
+    """32-layer GQA stack, 1,048,576-token bf16 caches filled by kv_append, 8 decode
+    steps through all layers."""
+    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_1m", 8)
 
 
 def test_llama3_8b_gqa_32layer_int4_3p3m_stack(torch_cuda):
-    """32-layer GQA stack, 3,300,000-token int4 caches (quantised by kv_append), 2 decode
-    steps through all layers; the last step checked on layer 0 (two retrieval and two
-    streaming KV heads) and layer 31 (one of each); every other layer checked finite."""
-    w = I.WORKLOADS["llama3_8b_gqa_32layer_int4_3p3m"]
-    m0, m31 = w.mask(0), w.mask(31)
-    h0 = [int(x) for x in np.nonzero(m0)[0][:2]] + [int(x) for x in np.nonzero(~m0)[0][:2]]
-    h31 = [int(np.nonzero(m31)[0][0]), int(np.nonzero(~m31)[0][0])]
-    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_int4_3p3m", 2, {0: h0, 31: h31})
+    """32-layer GQA stack, 3,300,000-token int4 caches (quantised by kv_append), 8 decode
+    steps through all layers."""
+    _stack_decode_check(torch_cuda, "llama3_8b_gqa_32layer_int4_3p3m", 8)
 
 
 def _ramped_inputs(w, total, growth):

@@ -51,3 +51,22 @@ def test_masks():
     assert t.mask(0).tolist() == [True, False, True, False]
     s = I.WORKLOADS["llama3_8b_gqa_32layer_1m"].masks()
     assert s.shape == (32, 8) and (s.sum(axis=1) == 4).all()
+
+
+def test_host_c_twin_matches_numpy_definition():
+    """The C twin of the generator (libduo_inputs.so) gives the NumPy definition's
+    values bit for bit: contiguous ranges and strided head rows, fp32 and bf16."""
+    if I._host_lib() is None:
+        import pytest
+        pytest.skip("libduo_inputs.so not built")
+    rng = np.random.default_rng(5)
+    for dtype in ("f32", "bf16"):
+        for seed, layer, kind, pos0, T, H, D in [(3, 0, "k", 0, 37, 8, 128), (5, 31, "v", 3_299_990, 9, 8, 128),
+                                                 (1, 2, "q", 123, 5, 32, 64)]:
+            a = I.synth(seed, layer, kind, pos0, T, H, D, dtype)
+            b = I.synth(seed, layer, kind, pos0, T, H, D, dtype, use_host_lib=False)
+            assert a.dtype == b.dtype and np.array_equal(a, b)
+        pos = rng.integers(0, 3_300_000, 300)
+        a = I.synth_head(4, 17, "k", pos, 5, 8, 128, dtype)
+        b = I.synth_head(4, 17, "k", pos, 5, 8, 128, dtype, use_host_lib=False)
+        assert a.dtype == b.dtype and np.array_equal(a, b)
