@@ -6,9 +6,12 @@ attention, streaming sink + window attention) and every decode step (append/evic
 split-K retrieval decode + streaming decode + merge).  Inputs (Q, K, V for every
 position) are generated on the device before timing and stay resident in HBM.
 
-Default workload: Llama-2-7B-shaped MHA layer (32 heads, head_dim 128, bf16, 8 of 32
-heads retrieval, sink 64 + recent 256), 32768-token prefill in 4096-token chunks, then
-128 decode steps.  Prints one JSON line.
+Default workload: Llama-3-8B-shaped GQA layer (32 query / 8 KV heads, head_dim 128, bf16,
+4 of 8 KV heads retrieval, sink 64 + recent 256), 131072-token prefill in 8192-token
+chunks, then 256 decode steps: the largest single-layer configuration, which carries
+both halves of the metric (decode us/step and prefill tok/s).  Prints one JSON line;
+`value` is the step's whole-job throughput, (prefill + decode tokens) / step time, and
+`components` carries the metric's two numbers.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
 
 METRIC = "DuoAttn layer decode µs/step & prefill tok/s at context L; % HBM/MFMA roofline"
+DEFAULT_WORKLOAD = "llama3_8b_gqa_128k"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, vendor figure
@@ -587,6 +591,8 @@ def run(args):
                    "head_dim": w.head_dim, "retrieval_kv_heads": int(w.mask(0).sum()), "sink": w.sink,
                    "recent": w.recent, "kv_format": w.kv_format, "parallelism": "single_gpu"},
         "components": {
+            "value_is": (f"(prefill {w.context} + decode {w.decode_steps} tokens) / step time; the metric's two "
+                         "numbers are decode_us_per_step and prefill_tok_s"),
             "decode_us_per_step": round(dec_ms * 1e3 / w.decode_steps, 3),
             "decode_append_plus_attention_us_per_step": None,
             "prefill_tok_s": round(w.context / (prefill_ms * 1e-3), 1) if prefill_ms > 0 else None,
@@ -672,15 +678,16 @@ def run_stack(args, w):
         step(s)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    for s in range(args.warmup, args.warmup + args.steps):  # timed: nothing added
+    evs[0].record(stream)
+    for i, s in enumerate(range(args.warmup, args.warmup + args.steps)):  # timed: nothing added
         step(s)
-    ev1.record(stream)
+        evs[i + 1].record(stream)  # (a marker between steps: per-step times for the median and p90)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     # the next tokens with each launch's dispatch-stamped events: kernel durations
     B.duo_profile_collect(h)
     B.duo_profile_enable(h, True)
@@ -720,7 +727,10 @@ def run_stack(args, w):
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "retrieval_kv_heads_per_layer": int(w.mask(0).sum()), "sink": w.sink, "recent": w.recent,
                    "kv_format": w.kv_format, "parallelism": "single_gpu"},
-        "components": {"decode_us_per_step": round(ms_per_step * 1e3, 2),
+        "components": {"value_is": "decoded tokens per second through all 32 layers (1 / step time)",
+                       "decode_us_per_step": round(ms_per_step * 1e3, 2),
+                       "decode_us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+                       "decode_us_per_step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
                        "decode_attention_us_per_step": round(dec_ms * 1e3, 2),
                        "append_us_per_step": round(app_ms * 1e3, 2),
                        "workspace_gb": round(ws.numel() / 1e9, 2),
@@ -730,10 +740,85 @@ def run_stack(args, w):
         "cpu_baseline": None,
     }
     B.duo_kv_free(h)
+    del ws
+    torch.cuda.empty_cache()
     if not args.no_projections:
         # per layer, beside the step: the decoding token's QKV / output projections
         res["roofline_all"] += measure_projections(w, 0)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_stack(w, w.context + args.warmup)
     return res
+
+
+STACK_SAMPLE_LAYERS = (0, 15, 31)
+
+
+def stored_history(w, layer, kind, g, pos):
+    """K or V rows of KV head g at positions `pos` as the caches store them: bf16 bit
+    patterns, or for int4 caches the codec's dequantised fp32 values.  Input
+    preparation for the oracle (not timed): slices in parallel threads."""
+    import concurrent.futures as cf
+    import numpy as np
+
+    from mixed_head_kv_amd import inputs as I
+    from oracle import int4 as OQ
+
+    def part(a):
+        raw = I.synth_head(w.seed, layer, kind, pos[a:a + (1 << 16)], g, w.n_kv_heads, w.head_dim, "bf16")
+        if w.kv_format == "int4":
+            codes, sc, z = OQ.quantize(raw)
+            return OQ.dequantize(codes, sc, z)
+        return raw
+
+    with cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        return np.concatenate(list(ex.map(part, range(0, len(pos), 1 << 16))))
+
+
+def cpu_baseline_stack(w, t):
+    """The oracle's decode of one token at position t on layers 0, 15 and 31 (every KV
+    head's history as the caches hold it, upcast to fp64: every earlier token for
+    retrieval heads, the sinks and the recent window for streaming heads; one query head
+    per KV head timed and counted for the group), timed on the host cores and scaled to
+    32 layers.  History generation (and int4 quantisation) is excluded from the timing;
+    the fp64 upcast is included."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixed_head_kv_amd import inputs as I
+    from oracle import attention as OA
+
+    elapsed = 0.0
+    for layer in STACK_SAMPLE_LAYERS:
+        mask = w.mask(layer)
+        q = I.synth(w.seed, layer, "q", t, 1, w.n_q_heads, w.head_dim, "bf16")[0]
+        for g in range(w.n_kv_heads):
+            pos = (np.arange(t + 1) if mask[g] else
+                   np.unique(np.concatenate([np.arange(min(w.sink, t + 1)), np.arange(max(0, t - w.recent + 1), t + 1)])))
+            hist = {kind: stored_history(w, layer, kind, g, pos) for kind in ("k", "v")}
+            t0 = time.perf_counter()
+            K = np.zeros((t + 1, w.head_dim))
+            V = np.zeros((t + 1, w.head_dim))
+            up = (lambda a: a.astype(np.float64)) if w.kv_format == "int4" else (lambda a: OA.upcast(a, "bf16"))
+            K[pos] = up(hist["k"])
+            V[pos] = up(hist["v"])
+            t_up = time.perf_counter() - t0
+            # the G query heads of a KV head attend over the same keys at the same cost:
+            # one is timed and counted G times
+            t1 = time.perf_counter()
+            h = g * w.group
+            OA.head_attention(OA.upcast(q[h], "bf16")[None], [t], K, V, bool(mask[g]), w.sink, w.recent)
+            elapsed += t_up + w.group * (time.perf_counter() - t1)
+            del K, V, hist
+    per_step = elapsed * w.n_layers / len(STACK_SAMPLE_LAYERS)
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    return {"value": round(1.0 / per_step, 6), "unit": "tok/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": (f"one decode token at position {t}: layers {list(STACK_SAMPLE_LAYERS)}, each KV head's history "
+                       f"upcast and one of its {w.group} query heads timed (x{w.group}), {elapsed:.1f}s of oracle time, "
+                       f"extrapolated x{w.n_layers / len(STACK_SAMPLE_LAYERS):.2f} to {w.n_layers} layers"),
+            "extrapolated": True, "host_cpus": os.cpu_count()}
 
 
 def cpu_baseline(w, total, budget_s):
@@ -903,7 +988,7 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] in ("--summarize-stats", "--summarize-traffic"):
         sp = argparse.ArgumentParser()
         sp.add_argument("dirs", nargs="+")
-        sp.add_argument("--workload", default="llama2_7b_mha_32k")
+        sp.add_argument("--workload", default=DEFAULT_WORKLOAD)
         sp.add_argument("--extras", action="store_true", help="the run was `bench.py --extras-only`")
         a = sp.parse_args(sys.argv[2:])
         if sys.argv[1] == "--summarize-stats":
@@ -915,7 +1000,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="llama2_7b_mha_32k")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-identification", action="store_true",
                     help="skip the timing of the head-identification pre-filling beside the step")
