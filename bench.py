@@ -870,6 +870,30 @@ PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4("
                     "prefill_chunk_tiles": ["k_chunk_tiles<false>"]}
 
 
+def streaming_only_grid(workload):
+    """Grid (threads) of the prefill launches that hold only streaming-head queries (the
+    queries of a chunk after its first 4096), or None when the workload has none; the
+    k_prefill_mfma launches of any other grid are the chunk's main launch (retrieval
+    heads plus the first 4096 streaming-head queries)."""
+    import math
+    from mixed_head_kv_amd import inputs as I
+    w = I.WORKLOADS[workload]
+    if not w.prefill_chunk or w.prefill_chunk <= STAGE_TOKENS:
+        return None
+    n_str = int((~w.mask(0)).sum()) * w.group
+    return n_str * math.ceil(min(STAGE_TOKENS, w.prefill_chunk - STAGE_TOKENS) / 128) * 256
+
+
+def launch_kind(name, grid, workload):
+    """The roofline entry a profiled dispatch belongs to (None: not a path kernel)."""
+    for k, pats in PROFILED_KERNELS.items():
+        if any(p in name for p in pats):
+            if k == "prefill_attention" and grid == streaming_only_grid(workload):
+                return "prefill_streaming_attention"
+            return k
+    return None
+
+
 def extra_kernels(workload):
     """Kernels of `bench.py --extras-only` (the projections and the identification
     pre-filling): label -> (name pattern, grid size in threads or None).  The projections'
@@ -942,11 +966,15 @@ def summarize_traffic(fetch_dir, write_dir, workload, extras=False):
         return per
 
     kmap = ({k: (pat, grid) for k, (pat, grid) in extra_kernels(workload).items()} if extras else
-            {k: (pats, None) for k, pats in PROFILED_KERNELS.items()})
+            {k: (None, None) for k in list(PROFILED_KERNELS) + ["prefill_streaming_attention"]})
 
     def match(name, grid, pat, want):
+        if pat is None:  # the path's kernels, by launch kind
+            return launch_kind(name, grid, workload) == k_now[0]
         pats = pat if isinstance(pat, list) else [pat]
         return any(p in name for p in pats) and (want is None or grid == want)
+
+    k_now = [None]
 
     out, lines = {}, []
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -957,6 +985,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, extras=False):
         lines.append(f"{counter}: the 1 GiB copy reads {ref:.0f} KiB -> scale factor {factor:.4f}")
         out[counter] = {"factor": factor}
         for k, (pat, grid) in kmap.items():
+            k_now[0] = k
             xs = [v for (_, n, g), v in vals.items() if match(n, g, pat, grid)]
             if xs:
                 out[counter][k] = (len(xs), sum(xs) / len(xs))
@@ -984,7 +1013,78 @@ def summarize_traffic(fetch_dir, write_dir, workload, extras=False):
     return "\n".join(lines)
 
 
+# Counters of the summary below, one rocprofv3 --pmc pass each (within the per-pass
+# hardware limits of 8 SQ counters).
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES",
+    "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_VMEM SQ_WAIT_INST_LDS",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_MISC",
+]
+
+
+def summarize_counters(dirs, workload, n_cu=256):
+    """MFMA utilisation and instruction mix of the prefill and decode launches from
+    `rocprofv3 --pmc` passes (COUNTER_PASSES, one directory each), per launch kind.
+    Normalisation: SQ_BUSY_CU_CYCLES sums busy cycles over the CUs, so per-CU cycles =
+    it / n_cu and the shader clock = per-CU cycles / kernel duration;
+    SQ_VALU_MFMA_BUSY_CYCLES sums matrix-core busy cycles over the SIMDs (32 per
+    32x32x16 bf16 MFMA), so the MFMA busy fraction = it / (4 * SQ_BUSY_CU_CYCLES);
+    SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_* count in the same (quad-cycle) unit, so
+    their ratios are fractions of wave time."""
+    import collections
+    import csv
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    n = collections.defaultdict(lambda: collections.defaultdict(int))
+    dur = collections.defaultdict(list)
+    for d in dirs:
+        for f in _csvs(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                k = launch_kind(r["Kernel_Name"], int(r["Grid_Size"]), workload)
+                if k is None:
+                    continue
+                c = r["Counter_Name"]
+                agg[k][c] += float(r["Counter_Value"])
+                n[k][c] += 1
+                if c in ("SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA"):
+                    dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = []
+    for k in sorted(agg):
+        v = {c: agg[k][c] / n[k][c] for c in agg[k]}  # per dispatch
+        t_ns = sum(dur[k]) / len(dur[k]) if dur[k] else float("nan")
+        lines.append(f"{k}: {max(n[k].values())} dispatches counted, mean duration {t_ns / 1e3:.2f} us (under counters)")
+        cu = v.get("SQ_BUSY_CU_CYCLES")
+        if cu:
+            lines.append(f"  shader clock        {cu / n_cu / t_ns:.3f} GHz (SQ_BUSY_CU_CYCLES / {n_cu} CUs / duration)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+                lines.append(f"  MFMA busy           {v['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cu):.3f} of SIMD cycles "
+                             f"(SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES))")
+        mf = v.get("SQ_INSTS_MFMA")
+        if mf:
+            valu = v.get("SQ_INSTS_VALU", 0) - mf
+            lines.append(f"  per MFMA            {valu / mf:.2f} other VALU (of which "
+                         f"{v.get('SQ_INSTS_VALU_TRANS_F32', 0) / mf:.2f} transcendental), "
+                         f"{v.get('SQ_INSTS_LDS', 0) / mf:.2f} LDS, {v.get('SQ_INSTS_SALU', 0) / mf:.2f} SALU, "
+                         f"{v.get('SQ_INSTS_VMEM', 0) / mf:.3f} VMEM instructions")
+        wc = v.get("SQ_WAVE_CYCLES")
+        if wc:
+            parts = [f"{name} {v[c] / wc:.2f}" for name, c in (("issuing any", "SQ_ACTIVE_INST_ANY"),
+                                                               ("issuing VALU+MFMA", "SQ_ACTIVE_INST_VALU"),
+                                                               ("waiting on dependencies", "SQ_WAIT_INST_ANY"),
+                                                               ("waiting at s_waitcnt", "SQ_WAIT_ANY"),
+                                                               ("waiting on LDS", "SQ_WAIT_INST_LDS")) if c in v]
+            lines.append("  of wave time        " + ", ".join(parts))
+    return "\n".join(lines)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        sp = argparse.ArgumentParser()
+        sp.add_argument("dirs", nargs="+")
+        sp.add_argument("--workload", default=DEFAULT_WORKLOAD)
+        a = sp.parse_args(sys.argv[2:])
+        print(summarize_counters(a.dirs, a.workload))
+        return
     if len(sys.argv) > 1 and sys.argv[1] in ("--summarize-stats", "--summarize-traffic"):
         sp = argparse.ArgumentParser()
         sp.add_argument("dirs", nargs="+")
