@@ -45,6 +45,7 @@ def log(*a):
 KERNEL_SOURCES = {
     "decode_attention": "mixed_head_kv_amd/csrc/decode_mfma.hip",
     "prefill_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
+    "prefill_streaming_attention": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "prefill_chunk_tiles": "mixed_head_kv_amd/csrc/prefill_mfma.hip",
     "qkv_rope_decode": "mixed_head_kv_amd/csrc/linear_w8.hip",
     "out_proj_decode": "mixed_head_kv_amd/csrc/linear_w8.hip",

@@ -351,6 +351,19 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   set_priority<0>();
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (id mod 8), each XCD with its own
+// L2.  The G query heads of a KV head (times the key splits) read the same K/V tiles: a
+// "unit" of U = G * nsplit logical ids.  This maps the dispatch id p so that the U ids of
+// a unit share an XCD and are dispatched together (ids u mod 8 + 8 j of a run of 8 units),
+// so the unit's tile reads after the first hit that XCD's L2; runs of 8 units keep the
+// longest-first order.  Ids past the last whole run map to themselves.
+__device__ inline int xcd_grouped(int p, int U, int n) {
+  const int run = 8 * U;
+  if (U <= 1 || p >= n / run * run) return p;
+  const int r = p % run;
+  return ((p / run) * 8 + r % 8) * U + r / 8;
+}
+
 // Retrieval workgroups (long) come first in the grid and streaming ones (short) after,
 // so the streaming work fills the CUs that the retrieval blocks' uneven lengths leave
 // idle towards the end of the launch.
@@ -368,7 +381,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   }
   const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
   const KindGrid& kg = streaming ? a.str : a.ret;
-  const int id = static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0);
+  const int id = xcd_grouped(static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0), a.g.G * kg.nsplit,
+                             kg.blocks);
   // Longest query blocks first; heads of one block adjacent.
   const int per_b = kg.n_heads * kg.n_qblocks * kg.nsplit;
   const int b = id / per_b;
