@@ -922,10 +922,11 @@ def _short(name):
     return name.split("(")[0]
 
 
-def summarize_stats(d, extras_workload=None):
+def summarize_stats(d, extras_workload=None, path_workload=None):
     """Text table of a `rocprofv3 --kernel-trace --stats` run: calls, mean and total time
-    per kernel, as the profiler reports them.  With extras_workload, also the launches of
-    the extras' kernels split by grid (from the kernel trace)."""
+    per kernel, as the profiler reports them.  With path_workload, also the path's
+    launches by roofline entry (the prefill kernel's two launch kinds apart); with
+    extras_workload, the extras' launches split by grid (both from the kernel trace)."""
     import csv
     rows = []
     for f in _csvs(d, "kernel_stats.csv"):
@@ -935,10 +936,21 @@ def summarize_stats(d, extras_workload=None):
     for r in rows:
         lines.append(f"{_short(r['Name'])[:58]:<58} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>10.3f} "
                      f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+    trace = []
+    for f in _csvs(d, "kernel_trace.csv"):
+        trace += list(csv.DictReader(open(f)))
+    if path_workload and trace:
+        by = {}
+        for r in trace:
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            k = launch_kind(r["Kernel_Name"], grid, path_workload)
+            if k:
+                by.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append("")
+        lines.append(f"{'launches by roofline entry':<40} {'calls':>7} {'avg_us':>10}")
+        for k, ds in sorted(by.items()):
+            lines.append(f"{k:<40} {len(ds):>7} {sum(ds) / len(ds):>10.3f}")
     if extras_workload:
-        trace = []
-        for f in _csvs(d, "kernel_trace.csv"):
-            trace += list(csv.DictReader(open(f)))
         lines.append("")
         lines.append(f"{'launches by grid':<40} {'grid':>9} {'calls':>7} {'avg_us':>10}")
         for label, (pat, grid) in extra_kernels(extras_workload).items():
@@ -1093,7 +1105,7 @@ def main():
         sp.add_argument("--extras", action="store_true", help="the run was `bench.py --extras-only`")
         a = sp.parse_args(sys.argv[2:])
         if sys.argv[1] == "--summarize-stats":
-            print(summarize_stats(a.dirs[0], a.workload if a.extras else None))
+            print(summarize_stats(a.dirs[0], a.workload if a.extras else None, None if a.extras else a.workload))
         else:
             print(summarize_traffic(a.dirs[0], a.dirs[1], a.workload, a.extras))
         return
