@@ -882,7 +882,8 @@ def streaming_only_grid(workload):
     if not w.prefill_chunk or w.prefill_chunk <= STAGE_TOKENS:
         return None
     n_str = int((~w.mask(0)).sum()) * w.group
-    return n_str * math.ceil(min(STAGE_TOKENS, w.prefill_chunk - STAGE_TOKENS) / 128) * 256
+    pack = 4 if w.group % 4 == 0 else (2 if w.group % 2 == 0 else 1)  # query heads per workgroup
+    return n_str // pack * math.ceil(min(STAGE_TOKENS, w.prefill_chunk - STAGE_TOKENS) / (128 // pack)) * 256
 
 
 def launch_kind(name, grid, workload):

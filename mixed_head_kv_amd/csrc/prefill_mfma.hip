@@ -12,7 +12,9 @@
 // approach section; cn.bg3.co article, 研究背景 section (pre-filling cost of full
 // attention grows quadratically with the context).
 //
-// Workgroup: 4 wavefronts x 32 queries of one query head.  Keys move HBM -> LDS with
+// Workgroup: 4 wavefronts x 32 queries; under GQA its wavefronts take up to 4 query
+// heads of one KV head (the same 32 queries, or two slices of 32 for 2 heads), so each
+// K/V tile in LDS serves every head of the group.  Keys move HBM -> LDS with
 // direct loads in 64-key tiles, double-buffered (K rows with their 16-byte chunks
 // XOR-swizzled by the row index so the permuted row reads hit distinct banks; V in
 // d-major 8-key blocks).  Per 32-key half tile each wavefront runs, with
@@ -38,7 +40,7 @@ constexpr int kTileKeys = 64;
 constexpr int kKBytes = kTileKeys * 256;           // K rows, 16-byte chunks XOR-swizzled by row
 constexpr int kVBytes = kTileKeys * 128 * 2;       // 16384
 constexpr int kStageRows = 64;
-constexpr int kQRows = 128;                        // queries per workgroup
+constexpr int kQRows = 128;                        // (query, head) rows per workgroup
 
 __device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -93,14 +95,19 @@ __device__ inline float max32(const f32x16& a, const f32x16& b) {
   return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
 }
 
-// Workgroups of one head kind in a prefill launch: (sequence, query head, 128-query
-// block, split), longest blocks first.
+// Workgroups of one head kind in a prefill launch: (sequence, head group, query block,
+// split), longest blocks first.  A head group is `pack` query heads of one KV head
+// (GQA: they read the same K/V tiles, so one tile in LDS serves them all); a query
+// block is 128 / pack queries, so a workgroup always holds 128 (query, head) rows, 32
+// per wavefront: wavefront w takes head w % pack and queries 32 (w / pack) .. +31.
 struct KindGrid {
   int n_heads;    // query heads of this kind per sequence
-  int n_qblocks;
+  int pack;       // query heads per workgroup: 4, 2 or 1, a divisor of G
+  int qrows;      // queries per workgroup: 128 / pack
+  int n_qblocks;  // ceil(nq / qrows)
   int nsplit;     // workgroups sharing one query block's key range (1 or 2; retrieval only)
   int q0, nq;     // queries: chunk rows [q0, q0 + nq)
-  int blocks;     // B * n_heads * n_qblocks * nsplit
+  int blocks;     // B * (n_heads / pack) * n_qblocks * nsplit
 };
 
 // The per-launch scalars of a chunk-tile pass (k_chunk_tiles below).
@@ -149,7 +156,8 @@ struct PrefillArgs {
   int upd_blocks;
 };
 
-// Partial of one split of one query block: O [128 queries][128 dims], then m[128], l[128].
+// Partial of one split of one workgroup's block: O [128 rows][128 dims], then m[128],
+// l[128]; row 32 w + c is wavefront w's query c (of its head).
 constexpr int kSlotFloats = kQRows * 128 + 2 * kQRows;
 
 // Split partials move with buffer instructions carrying the sc1 cache-policy bit
@@ -381,34 +389,37 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   }
   const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
   const KindGrid& kg = streaming ? a.str : a.ret;
-  const int id = xcd_grouped(static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0), a.g.G * kg.nsplit,
-                             kg.blocks);
-  // Longest query blocks first; heads of one block adjacent.
-  const int per_b = kg.n_heads * kg.n_qblocks * kg.nsplit;
+  const int n_groups = kg.n_heads / kg.pack;
+  const int id = xcd_grouped(static_cast<int>(blockIdx.x) - (streaming ? a.ret.blocks : 0),
+                             a.g.G / kg.pack * kg.nsplit, kg.blocks);
+  // Longest query blocks first; head groups of one block adjacent.
+  const int per_b = n_groups * kg.n_qblocks * kg.nsplit;
   const int b = id / per_b;
   const int rem = id % per_b;
   const int split = rem % kg.nsplit;
   const int hq = rem / kg.nsplit;
-  const int qb = kg.n_qblocks - 1 - hq / kg.n_heads;
-  const int head_idx = hq % kg.n_heads;
-  // With both outputs requested the second grid reads the retrieval caches directly (row
-  // = position) instead of staged streaming-cache keys.
-  const bool dual = a.out_lambda != nullptr;
-  const bool staged = streaming && !dual;
-  int kvh;
-  const int h = kind_head(a, staged, head_idx, &kvh);
-  const int64_t cache = int64_t(b) * (staged ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
+  const int qb = kg.n_qblocks - 1 - hq / n_groups;
+  const int group = hq % n_groups;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
-  const int q_first = kg.q0 + qb * kQRows;                // chunk-relative
-  const int q_last = min(q_first + kQRows, kg.q0 + kg.nq) - 1;
-  const int my_q = q_first + 32 * wave + col;             // this lane's query
+  const int wq = wave / kg.pack;                          // the wavefront's 32-query slice
+  // With both outputs requested the second grid reads the retrieval caches directly (row
+  // = position) instead of staged streaming-cache keys.
+  const bool dual = a.out_lambda != nullptr;
+  const bool staged = streaming && !dual;
+  int kvh;  // the same for every wavefront: pack divides G
+  const int h = kind_head(a, staged, group * kg.pack + wave % kg.pack, &kvh);
+  const int64_t cache = int64_t(b) * (staged ? a.lv.n_str : a.lv.n_ret) + a.lv.slot[kvh];
+
+  const int q_first = kg.q0 + qb * kg.qrows;              // chunk-relative
+  const int q_last = min(q_first + kg.qrows, kg.q0 + kg.nq) - 1;
+  const int my_q = q_first + 32 * wq + col;               // this lane's query
   const bool q_valid = my_q <= q_last;
   const int64_t i_pos = a.t0 + (q_valid ? my_q : q_last); // absolute position
-  const int64_t wave_q_hi = a.t0 + min(q_first + 32 * wave + 31, q_last);
-  const int64_t wave_q_lo = a.t0 + q_first + 32 * wave;
+  const int64_t wave_q_hi = a.t0 + min(q_first + 32 * wq + 31, q_last);
+  const int64_t wave_q_lo = a.t0 + q_first + 32 * wq;
 
   // Q^T operand: lane (col, half) holds dims 64*half + 8s .. +7 of its query, s = 0..7.
   u32x4 qop[8];
@@ -489,7 +500,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     auto tile_row = [&](int ti) -> int64_t {
       return ti < n_sink ? int64_t(ti) * kTileKeys : (w_first + (ti - n_sink)) * kTileKeys;
     };
-    const bool live = q_first + 32 * wave <= q_last;  // the wavefront has queries
+    const bool live = q_first + 32 * wq <= q_last;  // the wavefront has queries
     if (ntiles > 0) tile_dma(src, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
     __syncthreads();
     for (int ti = 0; ti < ntiles; ++ti) {
@@ -527,10 +538,10 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
   l += __shfl_xor(l, 32);
   if (kg.nsplit > 1) {
     // Every split publishes its partial; the last one to arrive merges them all.  A
-    // partial is O as float4 chunks [32 dim chunks][128 queries] (a wavefront's lanes
+    // partial is O as float4 chunks [32 dim chunks][128 rows] (a wavefront's lanes
     // cover 512 contiguous bytes per store), then m[128] and l[128], all moved with
     // 16-byte device-coherent buffer accesses.
-    const int pair = (b * kg.n_heads + head_idx) * kg.n_qblocks + qb;
+    const int pair = (b * n_groups + group) * kg.n_qblocks + qb;
     const int ql = 32 * wave + col;
     float* mine = a.scratch + (int64_t(pair) * kg.nsplit + split) * kSlotFloats;
     {
@@ -758,16 +769,24 @@ __device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const Cache
 
 }  // namespace
 
-// Streaming-head grid of the queries in chunk rows [q0, q0 + nq).
-static KindGrid streaming_grid(const Geom& g, const LayerView& lv, int q0, int nq) {
+// Grid of n_heads query heads (KV-head-major) over chunk rows [q0, q0 + nq): head groups
+// of the largest of 4, 2, 1 heads that divides G, query blocks of 128 / pack rows.
+static KindGrid kind_grid(const Geom& g, int n_heads, int q0, int nq, int nsplit) {
   KindGrid k = {};
-  k.n_heads = lv.n_str * g.G;
-  k.n_qblocks = (nq + kQRows - 1) / kQRows;
-  k.nsplit = 1;
+  k.n_heads = n_heads;
+  k.pack = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
+  k.qrows = kQRows / k.pack;
+  k.n_qblocks = (nq + k.qrows - 1) / k.qrows;
+  k.nsplit = nsplit;
   k.q0 = q0;
   k.nq = nq;
-  k.blocks = nq > 0 ? g.B * k.n_heads * k.n_qblocks : 0;
+  k.blocks = nq > 0 ? g.B * (n_heads / k.pack) * k.n_qblocks * nsplit : 0;
   return k;
+}
+
+// Streaming-head grid of the queries in chunk rows [q0, q0 + nq).
+static KindGrid streaming_grid(const Geom& g, const LayerView& lv, int q0, int nq) {
+  return kind_grid(g, lv.n_str * g.G, q0, nq, 1);
 }
 
 static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
@@ -781,7 +800,7 @@ static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheR
   a.t0 = t0;
   a.stage = stage;
   a.stage_sink_rows = stage_sink_rows(g.S);
-  a.ret.nsplit = a.str.nsplit = 1;
+  a.ret = a.str = kind_grid(g, 0, 0, 0, 1);
   return a;
 }
 
@@ -813,14 +832,11 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
     a.upd_blocks = a.upd.str_tiles * g.B * lv.n_str;
   }
   KindGrid& r = a.ret;
-  r.n_heads = lv.n_ret * g.G;
-  r.n_qblocks = (T + kQRows - 1) / kQRows;
-  r.q0 = 0;
-  r.nq = T;
+  r = kind_grid(g, lv.n_ret * g.G, 0, T, 1);
   // Split a query block's keys over two workgroups when the retrieval blocks alone would
   // leave fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own
   // MFMA, LDS and barrier latencies) and the keys and scratch allow it.
-  const int64_t pairs = int64_t(g.B) * r.n_heads * r.n_qblocks;
+  const int64_t pairs = int64_t(g.B) * (r.n_heads / r.pack) * r.n_qblocks;
   int nsplit = 1;
   if (pairs < 2 * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
       pairs * 2 * kSlotFloats <= scratch_floats)
@@ -834,13 +850,7 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
   a.scratch = scratch;
   a.counters = counters;
   if (out_lambda) {  // every head, every query of the chunk, over the retrieval caches
-    KindGrid& k = a.str;
-    k.n_heads = r.n_heads;
-    k.n_qblocks = r.n_qblocks;
-    k.nsplit = 1;
-    k.q0 = 0;
-    k.nq = T;
-    k.blocks = T > 0 ? g.B * k.n_heads * k.n_qblocks : 0;
+    a.str = kind_grid(g, r.n_heads, 0, T, 1);
   } else {
     a.str = streaming_grid(g, lv, 0, nq_streaming);
   }

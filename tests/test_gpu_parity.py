@@ -31,6 +31,10 @@ SMALL = {
     # a window longer than one decode split (2048 slots): streaming decode in two splits
     # with a merge, staged prefill over a 2304-row window, the ring wrapped
     "long_window_bf16": W("long_window_bf16", 19, 8, 4, 128, "bf16", 4, 2300, 3000, 12, 2),
+    # group sizes that pack 1 (G = 3) and 2 (G = 6: three workgroups per KV head) query
+    # heads into a prefill workgroup
+    "gqa3_bf16": W("gqa3_bf16", 24, 12, 4, 128, "bf16", 4, 64, 700, 6, 2),
+    "gqa6_bf16": W("gqa6_bf16", 25, 12, 2, 128, "bf16", 4, 64, 700, 6, 1),
 }
 CHUNKS = {
     "mha_bf16": [100, 156, 1, 300],
@@ -42,6 +46,8 @@ CHUNKS = {
     "all_retrieval_bf16": [400],
     "nosink_r1_bf16": [37, 263],
     "long_window_bf16": [1000, 1900, 100],
+    "gqa3_bf16": [129, 400, 71],
+    "gqa6_bf16": [300, 93, 1, 200],
 }
 
 
@@ -152,7 +158,7 @@ def test_poisoned_workspace_is_cleared_by_init(torch_cuda, name):
     compare(f"{name} decode (poisoned)", to_f64(dec), ref[L:], TOL[w.io_dtype])
 
 
-@pytest.mark.parametrize("name", ["mha_bf16", "gqa_bf16", "all_retrieval_bf16"])
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa_bf16", "all_retrieval_bf16", "gqa6_bf16"])
 def test_split_key_prefill_matches_oracle(torch_cuda, monkeypatch, name):
     """Query blocks whose key range is split over two workgroups (merged by the last to
     finish) give the same result; forced on small ragged chunks here."""
