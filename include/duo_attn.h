@@ -39,6 +39,13 @@
  * - Return codes: DUO_OK, or a negative DUO_E_* code with a message available from
  *   duo_last_error() (thread-local).
  * - A handle is not thread-safe.
+ * - Fault injection, for tests of error handling: when the environment variable
+ *   DUO_FAULT_INJECT holds "all" or a comma-separated list of entry-point names
+ *   (e.g. "duo_decode,duo_kv_append"), each named call of duo_kv_init, duo_prefill,
+ *   duo_prefill_seq, duo_prefill_dual, duo_kv_append, duo_kv_append_seq, duo_decode,
+ *   duo_decode_static, duo_kv_read and duo_kv_read_int4 returns DUO_E_HIP after its
+ *   argument checks, before any HIP call and without changing any state.  The
+ *   variable is read at every call; unset or empty, nothing changes.
  *
  * Tensor layouts (row-major, contiguous, batch B = cfg.batch):
  *   Q, O for prefill : [B, T, n_q_heads, head_dim]      (token-major, as a fused QKV
@@ -116,13 +123,25 @@ int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes);
  * slots) cache per streaming KV head, per layer and sequence: the two kinds of KV cache
  * each layer keeps (hotpaper.ai page "DuoAttention: Efficient Long-Context LLM
  * Inference with Retrieval and Streaming Heads", abstract and technical-approach
- * section; cn.bg3.co article, DuoAttention 的创新设计).  Clears the workspace (one fill
- * kernel on `stream`).  Every layer starts with length 0.  The workspace must not be
+ * section; cn.bg3.co article, DuoAttention 的创新设计).  Clears the workspace and fills
+ * its guard bands (fill kernels on `stream`).  Every layer starts with length 0.  The workspace must not be
  * used by anything else while the handle lives.  Errors: DUO_E_INVALID (bad config,
  * null or misaligned workspace), DUO_E_UNSUPPORTED, DUO_E_CAPACITY (bytes too small),
  * DUO_E_HIP (the fill kernel failed to launch; no handle is returned). */
 int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream,
                 duo_handle** out);
+
+/* Workspace guard bands, for checks that no kernel writes outside its region: every
+ * region of the workspace (each cache, the split scratch, the counters, the staging
+ * buffers) is followed by DUO_GUARD_BYTES bytes that duo_kv_init fills with the 32-bit
+ * word DUO_GUARD_WORD (little-endian, repeated) and that nothing else writes.
+ * Writes the byte offsets (from the workspace start) of the first `max` bands into the
+ * host array `offsets` and the number of bands into *n (the full count, also when max
+ * is smaller).  A caller compares the bands with the pattern after its work has run.
+ * Errors: DUO_E_INVALID (null handle or n, max < 0, null offsets with max > 0). */
+#define DUO_GUARD_BYTES 256u
+#define DUO_GUARD_WORD 0xD0A5C3E1u
+int duo_kv_guard_bands(const duo_handle* h, uint64_t* offsets, int32_t max, int32_t* n);
 
 /* Causal attention of n_tokens new tokens of `layer` (positions len .. len+T-1) and
  * append of their K/V (pre-filling; a prompt may be split into chunks, one call each,

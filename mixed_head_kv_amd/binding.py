@@ -28,12 +28,14 @@ DUO_KV_SAME_AS_IO = 0
 DUO_KV_INT4_G128 = 1
 DUO_SYNTH_INT8 = 2
 DUO_STATIC_SCRATCH_BYTES = 16 << 20
+DUO_GUARD_BYTES = 256
+DUO_GUARD_WORD = 0xD0A5C3E1
 
 EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_decode", "duo_decode_static",
            "duo_kv_length",
            "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_prefill_dual", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8",
-           "duo_profile_thread_enable", "duo_profile_thread_collect"]
+           "duo_profile_thread_enable", "duo_profile_thread_collect", "duo_kv_guard_bands"]
 KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage", "qkv_rope",
                   "linear"]
 
@@ -80,6 +82,7 @@ def lib():
         "duo_kv_append_seq": (ctypes.c_int, [vp, i32, i32, vp, vp, i32, vp]),
         "duo_kv_length_seq": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(i64)]),
         "duo_kv_free": (None, [vp]),
+        "duo_kv_guard_bands": (ctypes.c_int, [vp, ctypes.POINTER(u64), i32, ctypes.POINTER(i32)]),
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_kv_read": (ctypes.c_int, [vp, i32, i32, i32, i32, i64, i32, vp, vp]),
         "duo_kv_read_int4": (ctypes.c_int, [vp, i32, i32, i32, i32, i64, i32, vp, vp, vp]),
@@ -227,6 +230,15 @@ def qkv_rope_w8(x, positions, w, scale, n_q_heads, n_kv_heads, head_dim, rope_ba
 
 def duo_kv_free(h):
     lib().duo_kv_free(h)
+
+
+def duo_kv_guard_bands(h) -> list:
+    """Byte offsets of the workspace's guard bands (DUO_GUARD_BYTES each)."""
+    n = ctypes.c_int32()
+    _check(lib().duo_kv_guard_bands(h, None, 0, ctypes.byref(n)))
+    offs = (ctypes.c_uint64 * max(n.value, 1))()
+    _check(lib().duo_kv_guard_bands(h, offs, n.value, ctypes.byref(n)))
+    return list(offs[:n.value])
 
 
 def duo_last_error() -> str:

@@ -48,6 +48,18 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(DUO_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// DUO_FAULT_INJECT ("all" or a comma-separated list of entry-point names): the named
+// call fails with DUO_E_HIP here, after its argument checks and before any HIP call or
+// state change.
+int injected_fault(const char* call) {
+  const char* e = std::getenv("DUO_FAULT_INJECT");
+  if (!e || !*e) return DUO_OK;
+  if (std::strcmp(e, "all") != 0 &&
+      (std::string(",") + e + ",").find(std::string(",") + call + ",") == std::string::npos)
+    return DUO_OK;
+  return fail(DUO_E_HIP, std::string(call) + ": fault injected (DUO_FAULT_INJECT)");
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr uint64_t kAlign = 256;
@@ -69,6 +81,7 @@ struct Layout {
   int64_t stage_rows = 0;     // rows per streaming cache
   int stage_caches = 0;       // batch * most streaming heads of any layer
   uint64_t stage_k = 0, stage_v = 0;
+  std::vector<uint64_t> guards;  // offsets of the guard bands (one after every region)
 };
 
 int validate_config(const duo_config* c) {
@@ -115,6 +128,15 @@ bool make_layout(const duo_config* c, Layout* L) {
   const uint64_t meta = int4 ? 4 : 0;
   uint64_t off = 0;
   const long double limit = 1.0e18L;
+  L->guards.clear();
+  // A region of `bytes` bytes at the current offset, then its guard band.
+  auto region = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align_up(off + bytes, kAlign);
+    L->guards.push_back(off);
+    off += DUO_GUARD_BYTES;
+    return at;
+  };
   L->layers.assign(c->n_layers, LayerLayout());
   for (int l = 0; l < c->n_layers; ++l) {
     LayerLayout& y = L->layers[l];
@@ -125,23 +147,20 @@ bool make_layout(const duo_config* c, Layout* L) {
     if (ret_rows * vec * 2 + str_rows * vec * 2 + (ret_rows + str_rows) * meta * 2 + (long double)off > limit)
       return false;
     const uint64_t rr = B * y.n_ret * uint64_t(L->cap), sr = B * y.n_str * uint64_t(L->nslot);
-    y.ret_k = off; off = align_up(off + rr * vec, kAlign);
-    y.ret_v = off; off = align_up(off + rr * vec, kAlign);
-    y.str_k = off; off = align_up(off + sr * vec, kAlign);
-    y.str_v = off; off = align_up(off + sr * vec, kAlign);
+    y.ret_k = region(rr * vec);
+    y.ret_v = region(rr * vec);
+    y.str_k = region(sr * vec);
+    y.str_v = region(sr * vec);
     if (int4) {
-      y.ret_km = off; off = align_up(off + rr * meta, kAlign);
-      y.ret_vm = off; off = align_up(off + rr * meta, kAlign);
-      y.str_km = off; off = align_up(off + sr * meta, kAlign);
-      y.str_vm = off; off = align_up(off + sr * meta, kAlign);
+      y.ret_km = region(rr * meta);
+      y.ret_vm = region(rr * meta);
+      y.str_km = region(sr * meta);
+      y.str_vm = region(sr * meta);
     }
   }
-  L->partials = off;
-  off = align_up(off + B * c->n_q_heads * uint64_t(duo::kMaxSplits) * (D + 2) * 4, kAlign);
-  L->counters = off;
-  off = align_up(off + B * c->n_kv_heads * 4, kAlign);
-  L->prefill_counters = off;
-  off = align_up(off + uint64_t(duo::kPrefillCounters) * 4, kAlign);
+  L->partials = region(B * c->n_q_heads * uint64_t(duo::kMaxSplits) * (D + 2) * 4);
+  L->counters = region(B * c->n_kv_heads * 4);
+  L->prefill_counters = region(uint64_t(duo::kPrefillCounters) * 4);
   if (c->io_dtype == DUO_DTYPE_BF16 && D == 128 && !int4) {
     int n_str = 0;
     for (const LayerLayout& y : L->layers) n_str = y.n_str > n_str ? y.n_str : n_str;
@@ -149,8 +168,8 @@ bool make_layout(const duo_config* c, Layout* L) {
     L->stage_rows = duo::stage_sink_rows(c->sink) + duo::stage_window_rows(c->recent) + L->stage_tokens;
     L->stage_caches = int(B) * n_str;
     const uint64_t bytes = uint64_t(L->stage_caches) * uint64_t(L->stage_rows) * D * 2;
-    L->stage_k = off; off = align_up(off + bytes, kAlign);
-    L->stage_v = off; off = align_up(off + bytes, kAlign);
+    L->stage_k = region(bytes);
+    L->stage_v = region(bytes);
   }
   L->total = off;
   return true;
@@ -408,6 +427,7 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   Layout L;
   if (!make_layout(cfg, &L)) return fail(DUO_E_INVALID, "workspace size overflows");
   if (bytes < L.total) return fail(DUO_E_CAPACITY, "workspace smaller than duo_kv_bytes()");
+  if ((rc = injected_fault("duo_kv_init"))) return rc;
 
   duo_handle* h = new duo_handle();
   h->cfg = *cfg;
@@ -481,15 +501,29 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   hipError_t e = duo::launch_zero_bytes(h->ws, L.partials, as_stream(hip_stream));
   if (e == hipSuccess)
     e = duo::launch_zero_bytes(h->ws + L.counters, L.total - L.counters, as_stream(hip_stream));
+  if (e == hipSuccess)
+    e = duo::launch_guard_fill(h->ws, L.guards.data(), static_cast<int>(L.guards.size()), DUO_GUARD_WORD,
+                               as_stream(hip_stream));
   if (e != hipSuccess) {
     delete h;
-    return hip_fail(e, "clearing counters");
+    return hip_fail(e, "clearing the workspace");
   }
   *out = h;
   return ok();
 }
 
 void duo_kv_free(duo_handle* h) { delete h; }
+
+int duo_kv_guard_bands(const duo_handle* h, uint64_t* offsets, int32_t max, int32_t* n) {
+  if (!h) return fail(DUO_E_INVALID, "handle is NULL");
+  if (!n) return fail(DUO_E_INVALID, "n is NULL");
+  if (max < 0) return fail(DUO_E_INVALID, "max must be >= 0");
+  if (max > 0 && !offsets) return fail(DUO_E_INVALID, "offsets is NULL");
+  const std::vector<uint64_t>& g = h->layout.guards;
+  for (size_t i = 0; i < g.size() && i < size_t(max); ++i) offsets[i] = g[i];
+  *n = static_cast<int32_t>(g.size());
+  return ok();
+}
 
 static int64_t& seq_len(duo_handle* h, int32_t layer, int32_t seq) { return h->len[size_t(layer) * h->cfg.batch + seq]; }
 static int64_t seq_len(const duo_handle* h, int32_t layer, int32_t seq) {
@@ -619,6 +653,7 @@ int duo_prefill(duo_handle* h, int32_t layer, const void* q, const void* k, cons
   if (h->cfg.kv_format == DUO_KV_INT4_G128) return fail(DUO_E_UNSUPPORTED, "prefill with an int4 cache");
   int64_t t0 = 0;
   if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = injected_fault("duo_prefill"))) return rc;
   if ((rc = run_prefill(h, h->geom, h->views[layer], q, k, v, n_tokens, out, t0, as_stream(hip_stream)))) return rc;
   for (int32_t b = 0; b < h->cfg.batch; ++b) seq_len(h, layer, b) = t0 + n_tokens;
   return ok();
@@ -634,6 +669,7 @@ int duo_prefill_seq(duo_handle* h, int32_t layer, int32_t seq, const void* q, co
   if (h->cfg.kv_format == DUO_KV_INT4_G128) return fail(DUO_E_UNSUPPORTED, "prefill with an int4 cache");
   const int64_t t0 = seq_len(h, layer, seq);
   if ((rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = injected_fault("duo_prefill_seq"))) return rc;
   duo::Geom g;
   LayerView lv;
   one_sequence(h, layer, seq, &g, &lv);
@@ -654,6 +690,7 @@ int duo_prefill_dual(duo_handle* h, int32_t layer, const void* q, const void* k,
   if (lv.n_str != 0) return fail(DUO_E_STATE, "every KV head of the layer must be a retrieval head (full caches)");
   int64_t t0 = 0;
   if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = injected_fault("duo_prefill_dual"))) return rc;
   hipStream_t st = as_stream(hip_stream);
   hipError_t e;
   {
@@ -677,6 +714,7 @@ int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, in
   if ((rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
   int64_t t0 = 0;
   if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = injected_fault("duo_kv_append"))) return rc;
   hipError_t e;
   {
     KernelMark m(h, DUO_KERNEL_APPEND, as_stream(hip_stream));
@@ -695,6 +733,7 @@ int duo_kv_append_seq(duo_handle* h, int32_t layer, int32_t seq, const void* k, 
   if ((rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v"))) return rc;
   const int64_t t0 = seq_len(h, layer, seq);
   if ((rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
+  if ((rc = injected_fault("duo_kv_append_seq"))) return rc;
   duo::Geom g;
   LayerView lv;
   one_sequence(h, layer, seq, &g, &lv);
@@ -710,8 +749,9 @@ int duo_kv_append_seq(duo_handle* h, int32_t layer, int32_t seq, const void* k, 
 
 // One decoding step (duo_decode) with its split partials and arrival counters in the
 // given scratch (the workspace's, or the library's static array).
-static int run_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
-                      void* hip_stream, float* partials, int* counters, int max_splits) {
+static int run_decode(const char* call, duo_handle* h, int32_t layer, const void* q, const void* k_new,
+                      const void* v_new, void* out, void* hip_stream, float* partials, int* counters,
+                      int max_splits) {
   int rc = check_layer(h, layer);
   if (rc) return rc;
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(out, "out"))) return rc;
@@ -736,6 +776,7 @@ static int run_decode(duo_handle* h, int32_t layer, const void* q, const void* k
   hipError_t e;
   duo::DecodePlan p;
   if (!make_plan(h, layer, tmax, partials, counters, max_splits, &p)) return DUO_E_UNSUPPORTED;
+  if ((rc = injected_fault(call))) return rc;
   if (!uniform) {
     p.varlen = 1;
     for (int32_t b = 0; b < B; ++b) p.t_seq[b] = seq_len(h, layer, b) - (append ? 0 : 1);
@@ -776,7 +817,8 @@ static int run_decode(duo_handle* h, int32_t layer, const void* q, const void* k
 int duo_decode(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
                void* hip_stream) {
   if (!h) return fail(DUO_E_INVALID, "handle is NULL");
-  return run_decode(h, layer, q, k_new, v_new, out, hip_stream, h->partials, h->counters, duo::kMaxSplits);
+  return run_decode("duo_decode", h, layer, q, k_new, v_new, out, hip_stream, h->partials, h->counters,
+                    duo::kMaxSplits);
 }
 
 int duo_decode_static(duo_handle* h, int32_t layer, const void* q, const void* k_new, const void* v_new, void* out,
@@ -785,7 +827,8 @@ int duo_decode_static(duo_handle* h, int32_t layer, const void* q, const void* k
   StaticScratch sc;
   int rc = static_scratch(h, &sc);
   if (rc) return rc;
-  return run_decode(h, layer, q, k_new, v_new, out, hip_stream, sc.partials, sc.counters, sc.max_splits);
+  return run_decode("duo_decode_static", h, layer, q, k_new, v_new, out, hip_stream, sc.partials, sc.counters,
+                    sc.max_splits);
 }
 
 static int check_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, int32_t which, int64_t pos0,
@@ -817,6 +860,7 @@ int duo_kv_read(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_head, 
   int rc = check_read(h, layer, b, kv_head, which, pos0, n, &streaming, &cache);
   if (rc) return rc;
   if ((rc = check_ptr(d_out, "out"))) return rc;
+  if ((rc = injected_fault("duo_kv_read"))) return rc;
   if (n == 0) return ok();
   const LayerView& lv = h->views[layer];
   hipError_t e = duo::launch_read(h->geom, streaming ? lv.str : lv.ret, cache, streaming, pos0, n, which, d_out,
@@ -833,6 +877,7 @@ int duo_kv_read_int4(const duo_handle* h, int32_t layer, int32_t b, int32_t kv_h
   if (rc) return rc;
   if (h->cfg.kv_format != DUO_KV_INT4_G128) return fail(DUO_E_STATE, "cache is not int4");
   if ((rc = check_ptr(d_codes, "codes")) || (rc = check_ptr(d_meta, "meta"))) return rc;
+  if ((rc = injected_fault("duo_kv_read_int4"))) return rc;
   if (n == 0) return ok();
   const LayerView& lv = h->views[layer];
   hipError_t e = duo::launch_read_int4(h->geom, streaming ? lv.str : lv.ret, cache, streaming, pos0, n, which,

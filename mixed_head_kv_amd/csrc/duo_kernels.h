@@ -140,6 +140,9 @@ hipError_t launch_read_int4(const Geom& g, const CacheRegion& c, int64_t cache, 
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st);
 // Clears n_bytes (a multiple of 16, 16-byte aligned) with a fill kernel.
 hipError_t launch_zero_bytes(void* p, uint64_t n_bytes, hipStream_t st);
+// Fills the n guard bands (DUO_GUARD_BYTES each) at byte offsets `offsets` (host array)
+// from `base` with the 32-bit `word`.
+hipError_t launch_guard_fill(char* base, const uint64_t* offsets, int n, uint32_t word, hipStream_t st);
 hipError_t launch_synth(void* out, int dtype, uint64_t seed, uint32_t stream, uint64_t c0, uint64_t n,
                         hipStream_t st);
 

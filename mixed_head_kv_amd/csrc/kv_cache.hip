@@ -360,6 +360,30 @@ hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Guard bands of the workspace: up to 64 per launch, one workgroup per band, each of its
+// DUO_GUARD_BYTES / 4 threads writing one 32-bit word.
+struct GuardList {
+  uint64_t off[64];
+  int n;
+};
+
+__global__ void k_guard_fill(char* base, GuardList g, uint32_t word) {
+  if (static_cast<int>(blockIdx.x) < g.n && threadIdx.x < DUO_GUARD_BYTES / 4)
+    reinterpret_cast<uint32_t*>(base + g.off[blockIdx.x])[threadIdx.x] = word;
+}
+
+hipError_t launch_guard_fill(char* base, const uint64_t* offsets, int n, uint32_t word, hipStream_t st) {
+  for (int i = 0; i < n; i += 64) {
+    GuardList g = {};
+    g.n = n - i < 64 ? n - i : 64;
+    for (int j = 0; j < g.n; ++j) g.off[j] = offsets[i + j];
+    launch(k_guard_fill, dim3(static_cast<unsigned>(g.n)), dim3(DUO_GUARD_BYTES / 4), 0, st, base, g, word);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_zero_bytes(void* p, uint64_t n_bytes, hipStream_t st) {
   const uint64_t n = n_bytes / 16;
   if (n == 0) return hipSuccess;

@@ -4,6 +4,7 @@
 // any sanitizer report or an unexpected return code fails the run.
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -102,6 +103,13 @@ int main() {
     expect(duo_kv_init(&k.c, reinterpret_cast<void*>(4096 + 16), need, nullptr, &h), DUO_E_INVALID, "misaligned ws");
     expect(duo_kv_init(&k.c, nullptr, need, nullptr, &h), DUO_E_INVALID, "null ws");
     expect(duo_kv_init(&k.c, reinterpret_cast<void*>(4096), need, nullptr, nullptr), DUO_E_INVALID, "null out");
+    // an injected fault fails the call after validation, before any HIP call
+    setenv("DUO_FAULT_INJECT", "duo_prefill,duo_kv_init", 1);
+    expect(duo_kv_init(&k.c, reinterpret_cast<void*>(4096), need, nullptr, &h), DUO_E_HIP, "injected init fault");
+    if (h) { std::printf("FAIL injected init fault: handle returned\n"); ++g_fail; }
+    expect(duo_kv_init(&k.c, reinterpret_cast<void*>(4096), need - 1, nullptr, &h), DUO_E_CAPACITY,
+           "validation before the injected fault");
+    unsetenv("DUO_FAULT_INJECT");
   }
   // calls on a NULL handle
   void* p = reinterpret_cast<void*>(4096);
@@ -120,6 +128,8 @@ int main() {
   expect(duo_kv_read_int4(nullptr, 0, 0, 0, 0, 0, 1, reinterpret_cast<uint8_t*>(4096),
                           reinterpret_cast<uint16_t*>(4096), nullptr),
          DUO_E_INVALID, "read_int4 null handle");
+  int32_t nb = 0;
+  expect(duo_kv_guard_bands(nullptr, nullptr, 0, &nb), DUO_E_INVALID, "guard_bands null handle");
   expect(duo_profile_enable(nullptr, 1), DUO_E_INVALID, "profile_enable null handle");
   double ms[DUO_KERNEL_CLASSES];
   int64_t cnt[DUO_KERNEL_CLASSES];

@@ -159,6 +159,24 @@ def fill_stack(w: I.Workload, kv, chunk: int = 65536):
     torch.cuda.synchronize()
 
 
+def guard_violations(kv) -> list:
+    """Byte offsets of the guard bands of a DuoKV's workspace that no longer hold the
+    pattern duo_kv_init wrote there (a kernel wrote outside its region)."""
+    import struct
+    import torch
+    from mixed_head_kv_amd import binding as B
+    offs = B.duo_kv_guard_bands(kv.h)
+    if not offs:
+        return []
+    ws = kv.workspace
+    idx = (torch.tensor(offs, dtype=torch.int64, device=ws.device)[:, None] +
+           torch.arange(B.DUO_GUARD_BYTES, dtype=torch.int64, device=ws.device)[None, :])
+    pat = torch.tensor(list(struct.pack("<I", B.DUO_GUARD_WORD)) * (B.DUO_GUARD_BYTES // 4), dtype=torch.uint8,
+                       device=ws.device)
+    bad = (ws[idx] != pat[None, :]).any(dim=1).cpu().numpy()
+    return [o for o, b in zip(offs, bad) if b]
+
+
 def to_f64(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 

@@ -61,6 +61,7 @@ def _bytes(cfg):
 
 def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask):
     al = lambda x, a: (x + a - 1) // a * a
+    reg = lambda off, size: al(off + size, 256) + B.DUO_GUARD_BYTES  # a region, then its guard band
     cap, nslot = al(max_ctx, 64), al(S + R, 64)
     vec = D // 2 if int4 else D * esize
     off = 0
@@ -68,18 +69,18 @@ def expected_bytes(n_layers, batch, hq, hkv, D, S, R, max_ctx, esize, int4, mask
         nr = int(mask[l].sum())
         ns = hkv - nr
         for rows in (batch * nr * cap, batch * nr * cap, batch * ns * nslot, batch * ns * nslot):
-            off = al(off + rows * vec, 256)
+            off = reg(off, rows * vec)
         if int4:
             for rows in (batch * nr * cap, batch * nr * cap, batch * ns * nslot, batch * ns * nslot):
-                off = al(off + rows * 4, 256)
-    off = al(off + batch * hq * 2048 * (D + 2) * 4, 256)
-    off = al(off + batch * hkv * 4, 256)
-    off = al(off + 65536 * 4, 256)
+                off = reg(off, rows * 4)
+    off = reg(off, batch * hq * 2048 * (D + 2) * 4)
+    off = reg(off, batch * hkv * 4)
+    off = reg(off, 65536 * 4)
     if esize == 2 and D == 128 and not int4:  # streaming-head prefill staging, K then V
         stage_rows = al(S, 64) + al(R - 1, 64) + min(cap, 4096)
         n_str = max(hkv - int(mask[l].sum()) for l in range(n_layers))
         for _ in range(2):
-            off = al(off + batch * n_str * stage_rows * D * 2, 256)
+            off = reg(off, batch * n_str * stage_rows * D * 2)
     return off
 
 
@@ -205,3 +206,47 @@ def test_capacity_arithmetic_orders_the_layouts():
     cfg = B.make_config(w.n_layers, 1, w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink, w.recent,
                         c["int4_duo"] + 1, B.DUO_DTYPE_BF16, B.DUO_KV_INT4_G128, w.masks().astype(np.uint8))
     assert r["int4_duo"]["bytes"] <= 288e9 < B.duo_kv_bytes(cfg)
+
+
+class _FakeWorkspace:
+    """Stands in for a workspace tensor in calls that must fail before using it."""
+
+    def __init__(self, nbytes):
+        self.nbytes = nbytes
+
+    def data_ptr(self):
+        return 1 << 20  # 256-byte aligned, never dereferenced
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def test_fault_injection_fails_init_after_validation(monkeypatch):
+    """DUO_FAULT_INJECT naming duo_kv_init makes it return DUO_E_HIP after its argument
+    checks and before any HIP call (no handle is returned); the binding raises it as a
+    DuoError with that code.  Validation errors still take precedence."""
+    _lib_or_skip()
+    cfg = _cfg()
+    rc, nbytes = _bytes(cfg)
+    assert rc == B.DUO_OK
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)
+    for value in ("duo_decode,duo_kv_init", "all", "duo_kv_init"):
+        monkeypatch.setenv("DUO_FAULT_INJECT", value)
+        rc = B.lib().duo_kv_init(ctypes.byref(cfg), fake, nbytes, None, ctypes.byref(h))
+        assert rc == B.DUO_E_HIP and not h.value
+        assert "fault injected" in B.duo_last_error() and "duo_kv_init" in B.duo_last_error()
+        rc = B.lib().duo_kv_init(ctypes.byref(cfg), fake, nbytes - 1, None, ctypes.byref(h))
+        assert rc == B.DUO_E_CAPACITY and not h.value
+        with pytest.raises(B.DuoError) as ei:
+            B.duo_kv_init(cfg, _FakeWorkspace(nbytes), stream=0)
+        assert ei.value.code == B.DUO_E_HIP
+
+
+def test_guard_band_call_rejects_bad_arguments():
+    _lib_or_skip()
+    n = ctypes.c_int32()
+    assert B.lib().duo_kv_guard_bands(None, None, 0, ctypes.byref(n)) == B.DUO_E_INVALID

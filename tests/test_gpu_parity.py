@@ -9,7 +9,8 @@ from mixed_head_kv_amd import inputs as I
 from oracle import attention as OA
 from oracle import int4 as OQ
 
-from parity_util import (TOL, compare, device_synth, fill_stack, host_history, oracle_decode_steps, oracle_rows,
+from parity_util import (TOL, compare, device_synth, fill_stack, guard_violations, host_history, oracle_decode_steps,
+                         oracle_rows,
                          oracle_rows_threaded, q_rows, run_layer, say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -249,6 +250,67 @@ def test_failed_calls_leave_state_unchanged(torch_cuda):
     assert e.value.code == B.DUO_E_INVALID
     kv.prefill(0, q[60:64], k[60:64], v[60:64])
     assert kv.length(0) == 64
+
+
+def test_injected_faults_leave_state_unchanged(torch_cuda, monkeypatch):
+    """DUO_FAULT_INJECT makes each named call fail with DUO_E_HIP after validation and
+    before any launch: the binding raises it, lengths and caches are unchanged, and the
+    same calls succeed once the variable is cleared (outputs against the oracle)."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    w = SMALL["gqa_bf16"].scaled(context=300, decode_steps=3)
+    say("injected faults")
+    kv = B.DuoKV.for_workload(w)
+    total = 300 + 3
+    q = device_synth(w, 0, "q", 0, total)
+    k = device_synth(w, 0, "k", 0, total)
+    v = device_synth(w, 0, "v", 0, total)
+    pre = [kv.prefill(0, q[:200], k[:200], v[:200])]
+    snap = kv.workspace.clone()
+    monkeypatch.setenv("DUO_FAULT_INJECT", "duo_prefill,duo_kv_append,duo_decode,duo_decode_static,duo_kv_read,"
+                                           "duo_prefill_seq,duo_kv_append_seq")
+    out = torch.zeros_like(q[:100])
+    calls = [lambda: B.duo_prefill(kv.h, 0, q[200:], k[200:], v[200:], 100, out),
+             lambda: B.duo_prefill_seq(kv.h, 0, 0, q[200:], k[200:], v[200:], 100, out),
+             lambda: B.duo_kv_append(kv.h, 0, k[200:], v[200:], 100),
+             lambda: B.duo_kv_append_seq(kv.h, 0, 0, k[200:], v[200:], 100),
+             lambda: B.duo_decode(kv.h, 0, q[200], k[200], v[200], out[0]),
+             lambda: B.duo_decode_static(kv.h, 0, q[200], k[200], v[200], out[0]),
+             lambda: kv.read(0, int(np.nonzero(w.mask(0))[0][0]), 0, 0, 10)]  # a retrieval head
+    for call in calls:
+        with pytest.raises(B.DuoError) as e:
+            call()
+        assert e.value.code == B.DUO_E_HIP and "fault injected" in str(e.value)
+    torch.cuda.synchronize()
+    assert kv.length(0) == 200 and torch.equal(kv.workspace, snap) and not out.any()
+    monkeypatch.delenv("DUO_FAULT_INJECT")
+    pre.append(kv.prefill(0, q[200:300], k[200:300], v[200:300]))
+    dec = torch.stack([kv.decode(0, q[t], k[t], v[t]) for t in range(300, total)])
+    torch.cuda.synchronize()
+    ref = oracle_rows(w, 0, np.arange(total), total)
+    compare("after injected faults, prefill", to_f64(torch.cat(pre)), ref[:300], TOL["bf16"])
+    compare("after injected faults, decode", to_f64(dec), ref[300:], TOL["bf16"])
+
+
+def test_guard_band_check_sees_a_stray_write(torch_cuda):
+    """The guard bands sit between the workspace's regions and hold the pattern after
+    init and after work; a byte written into one (here from the host side, the way a
+    kernel writing past its region would) is reported."""
+    from mixed_head_kv_amd import binding as B
+    w = SMALL["gqa_bf16"].scaled(context=200, decode_steps=2)
+    say("guard bands")
+    kv, _, _, _ = run_layer(w, [198], 2)
+    offs = B.duo_kv_guard_bands(kv.h)
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    assert all(o % 256 == 0 and o + B.DUO_GUARD_BYTES <= kv.nbytes for o in offs)
+    assert len(offs) == 4 * w.n_layers + 5  # K and V of both cache kinds per layer; scratch, counters, staging
+    assert guard_violations(kv) == []
+    o = offs[len(offs) // 2] + 77
+    saved = int(kv.workspace[o])
+    kv.workspace[o] = saved ^ 0x40
+    assert guard_violations(kv) == [o - 77]
+    kv.workspace[o] = saved
+    assert guard_violations(kv) == []
 
 
 def test_llama2_7b_mha_32k_layer(torch_cuda):
