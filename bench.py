@@ -867,7 +867,7 @@ def cpu_baseline(w, total, budget_s):
 # --- rocprofv3 output summaries (host only; no GPU) ---------------------------------
 
 PROFILED_KERNELS = {"decode_attention": ["k_decode_mfma(", "k_decode_mfma_int4(", "k_decode_mfma<", "k_decode_valu"],
-                    "prefill_attention": ["k_prefill_mfma(", "k_prefill_valu"],
+                    "prefill_attention": ["k_prefill_mfma<", "k_prefill_valu"],
                     "prefill_chunk_tiles": ["k_chunk_tiles<false>"]}
 
 
@@ -883,7 +883,8 @@ def streaming_only_grid(workload):
         return None
     n_str = int((~w.mask(0)).sum()) * w.group
     pack = 4 if w.group % 4 == 0 else (2 if w.group % 2 == 0 else 1)  # query heads per workgroup
-    return n_str // pack * math.ceil(min(STAGE_TOKENS, w.prefill_chunk - STAGE_TOKENS) / (128 // pack)) * 256
+    rows = 128 // pack                       # queries per 4-wavefront workgroup (these launches' shape)
+    return n_str // pack * math.ceil(min(STAGE_TOKENS, w.prefill_chunk - STAGE_TOKENS) / rows) * 256
 
 
 def launch_kind(name, grid, workload):
@@ -909,7 +910,7 @@ def extra_kernels(workload):
         tm = math.ceil(w.prefill_chunk / 256)
         out["qkv_rope_prefill"] = ("k_w8_gemm<", tm * nqkv // 256 * 512)
         out["out_proj_prefill"] = ("k_w8_gemm<", tm * hidden // 256 * 512)
-        out["prefill_dual_attention"] = ("k_prefill_mfma(", None)
+        out["prefill_dual_attention"] = ("k_prefill_mfma<", None)
     return out
 
 

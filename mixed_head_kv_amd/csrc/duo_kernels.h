@@ -77,6 +77,11 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
 // Streaming-head (sink + window) prefill on bf16 MFMA (D = 128) of the queries in chunk
 // rows [q0, q0 + nq) (at most kStageTokens), over the keys staged by launch_chunk_tiles;
 // for the queries after the first kStageTokens of a chunk.
+// Wavefronts per MFMA prefill workgroup for a layer shape (4 or 8), and whether the
+// streaming caches' update can join the prefill launch (upd_k / upd_v above).
+int prefill_waves(const Geom& g);
+bool prefill_fuses_update(const Geom& g);
+
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);
 

@@ -40,7 +40,15 @@ constexpr int kTileKeys = 64;
 constexpr int kKBytes = kTileKeys * 256;           // K rows, 16-byte chunks XOR-swizzled by row
 constexpr int kVBytes = kTileKeys * 128 * 2;       // 16384
 constexpr int kStageRows = 64;
-constexpr int kQRows = 128;                        // (query, head) rows per workgroup
+// Workgroup shape, by wavefront count W (4 or 8): 32 (query, head) rows per wavefront,
+// and each wavefront moves 16 / W of the tile's 16 K and 16 V kilobytes into LDS.
+template <int W>
+struct Shape {
+  static constexpr int kRows = 32 * W;                      // (query, head) rows per workgroup
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kDma = 16 / W;                       // 1 KB loads per wavefront, K and V each
+  static constexpr int kSlotFloats = kRows * 128 + 2 * kRows;  // one split's partial (below)
+};
 
 __device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -140,7 +148,7 @@ struct PrefillArgs {
   int64_t t0;           // position of chunk row 0
   KindGrid ret;         // blocks [0, ret.blocks): retrieval heads
   KindGrid str;         // blocks [ret.blocks, ret.blocks + str.blocks): streaming heads
-  float* scratch;       // split retrieval blocks: per (block, split) fp32 partial, kSlotFloats each
+  float* scratch;       // split retrieval blocks: per (block, split) fp32 partial, Shape<W>::kSlotFloats each
   int* counters;        // split retrieval blocks: arrival counter per query block
   CacheRegion stage;    // streaming heads: the staged keys, one region per streaming cache
   int stage_sink_rows;  // streaming heads: staged sink rows (before the window rows)
@@ -156,20 +164,21 @@ struct PrefillArgs {
   int upd_blocks;
 };
 
-// Partial of one split of one workgroup's block: O [128 rows][128 dims], then m[128],
-// l[128]; row 32 w + c is wavefront w's query c (of its head).
-constexpr int kSlotFloats = kQRows * 128 + 2 * kQRows;
+// Partial of one split of one workgroup's block: O [rows][128 dims], then m[rows],
+// l[rows] (rows = 32 W); row 32 w + c is wavefront w's query c (of its head).
 
 // Split partials move with buffer instructions carrying the sc1 cache-policy bit
 // (device-coherent: written through / read past the XCD-local L2), so a partial written
 // on one XCD is read correctly on another.  0x00020000 is the gfx9 buffer-descriptor
 // word 3 for raw (untyped) dword access; num_records bounds every access to the slot.
 constexpr int kCoherent = 16;  // sc1
+template <int W>
 __device__ inline __amdgpu_buffer_rsrc_t slot_rsrc(float* slot) {
-  return __builtin_amdgcn_make_buffer_rsrc(slot, 0, kSlotFloats * 4, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(slot, 0, Shape<W>::kSlotFloats * 4, 0x00020000);
 }
-// Byte offset of float4 chunk `c` (dims 4c .. 4c + 3) of query `ql` in a partial.
-__device__ inline int o_chunk_offset(int c, int ql) { return (c * kQRows + ql) * 16; }
+// Byte offset of float4 chunk `c` (dims 4c .. 4c + 3) of row `ql` in a partial.
+template <int W>
+__device__ inline int o_chunk_offset(int c, int ql) { return (c * Shape<W>::kRows + ql) * 16; }
 
 // Query head (of this kind) with index `idx`: the idx-th query head whose KV head has
 // this kind, in KV-head-major order.
@@ -189,15 +198,17 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // chunk L mod 16), gathered from the cache's MFMA-ordered 32-key tiles; V's d-major
 // 8-key blocks are copied as they are.  `wave` is uniform; the caller waits (vmcnt)
 // and synchronises before reading.
+template <int W>
 __device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb, char* ldsK, char* ldsV, int wave,
-                                int lane, const int (&koff)[4]) {
+                                int lane, const int (&koff)[Shape<W>::kDma]) {
+  constexpr int kDma = Shape<W>::kDma;
   // kb and the cache's first row are multiples of 32: the tile's 32-key cache tiles are
   // whole, and each lane's element offset inside them is loop-invariant (koff)
   const uint16_t* Kt = reinterpret_cast<const uint16_t*>(c.k) + ((cache * c.rows + kb) >> 5) * 4096;
-  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2 + wave * 4096 + lane * 16;
+  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2 + wave * (kDma * 1024) + lane * 16;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int inst = wave * 4 + u;
+  for (int u = 0; u < kDma; ++u) {
+    const int inst = wave * kDma + u;
     __builtin_amdgcn_global_load_lds(Kt + koff[u], (lds_void_ptr)(ldsK + inst * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(V + u * 1024, (lds_void_ptr)(ldsV + inst * 1024), 16, 0, 0);
   }
@@ -205,11 +216,12 @@ __device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb,
 
 // Element offsets (inside a 64-key tile of the MFMA-ordered K cache) of the chunks lane
 // `lane` of wavefront `wave` moves: LDS row 4 inst + L/16, physical chunk L mod 16 of the
-// swizzled tile, inst = 4 wave + u.
-__device__ inline void tile_dma_offsets(int wave, int lane, int (&koff)[4]) {
+// swizzled tile, inst = kDma wave + u.
+template <int W>
+__device__ inline void tile_dma_offsets(int wave, int lane, int (&koff)[Shape<W>::kDma]) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = (wave * 4 + u) * 4 + (lane >> 4);
+  for (int u = 0; u < Shape<W>::kDma; ++u) {
+    const int row = (wave * Shape<W>::kDma + u) * 4 + (lane >> 4);
     const int col16 = (lane & 15) ^ (row & 15);
     koff[u] = static_cast<int>(k_chunk_tiled(row, col16));
   }
@@ -374,18 +386,25 @@ __device__ inline int xcd_grouped(int p, int U, int n) {
 
 // Retrieval workgroups (long) come first in the grid and streaming ones (short) after,
 // so the streaming work fills the CUs that the retrieval blocks' uneven lengths leave
-// idle towards the end of the launch.
-__global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
+// idle towards the end of the launch.  W wavefronts per workgroup: 4 (two workgroups
+// per CU) or 8 (one per CU, each tile shared by twice the rows: half the LDS fill per
+// flop).
+template <int W>
+__global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];  // two tile buffers
+  constexpr int kRows = Shape<W>::kRows;
+  constexpr int kSlotFloats = Shape<W>::kSlotFloats;
 
   const Geom& g = a.g;
-  const int upd0 = a.ret.blocks + a.str.blocks;
-  if (static_cast<int>(blockIdx.x) >= upd0) {  // uniform: a streaming cache update block
-    const int id = static_cast<int>(blockIdx.x) - upd0;
-    chunk_tiles_body<true>(g, a.lv, a.stage, a.upd, id % a.upd.str_tiles, id / a.upd.str_tiles,
-                           reinterpret_cast<uint4(*)[16]>(lds),
-                           reinterpret_cast<uint16_t(*)[128]>(lds + kStageRows * 16 * 16));
-    return;
+  if constexpr (W == 4) {  // (the update blocks are 256-thread blocks)
+    const int upd0 = a.ret.blocks + a.str.blocks;
+    if (static_cast<int>(blockIdx.x) >= upd0) {  // uniform: a streaming cache update block
+      const int id = static_cast<int>(blockIdx.x) - upd0;
+      chunk_tiles_body<true>(g, a.lv, a.stage, a.upd, id % a.upd.str_tiles, id / a.upd.str_tiles,
+                             reinterpret_cast<uint4(*)[16]>(lds),
+                             reinterpret_cast<uint16_t(*)[128]>(lds + kStageRows * 16 * 16));
+      return;
+    }
   }
   const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
   const KindGrid& kg = streaming ? a.str : a.ret;
@@ -439,8 +458,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
 
   const float sl2 = g.scale_log2;
-  int koff[4];
-  tile_dma_offsets(wave, lane, koff);
+  int koff[Shape<W>::kDma];
+  tile_dma_offsets<W>(wave, lane, koff);
 
   if (!streaming) {
     // Retrieval: keys [0, t0 + q_last] of the cache, 64 per tile; a split takes a
@@ -454,12 +473,12 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     const int64_t first_q = a.t0 + q_first;
     int64_t n_inner = first_q >= kb_first + kTileKeys - 1 ? (first_q - (kb_first + kTileKeys - 1)) / kTileKeys + 1 : 0;
     if (n_inner > ntiles) n_inner = ntiles;
-    if (ntiles > 0) tile_dma(a.lv.ret, cache, kb_first, lds, lds + kKBytes, wave, lane, koff);
+    if (ntiles > 0) tile_dma<W>(a.lv.ret, cache, kb_first, lds, lds + kKBytes, wave, lane, koff);
     __syncthreads();
     auto prefetch = [&](int64_t ti) {  // the next tile is in flight during the compute
       if (ti + 1 < ntiles) {
         char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-        tile_dma(a.lv.ret, cache, kb_first + (ti + 1) * kTileKeys, nK, nK + kKBytes, wave, lane, koff);
+        tile_dma<W>(a.lv.ret, cache, kb_first + (ti + 1) * kTileKeys, nK, nK + kKBytes, wave, lane, koff);
       }
     };
     auto no_mask = [](f32x16&, int) {};
@@ -501,13 +520,13 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
       return ti < n_sink ? int64_t(ti) * kTileKeys : (w_first + (ti - n_sink)) * kTileKeys;
     };
     const bool live = q_first + 32 * wq <= q_last;  // the wavefront has queries
-    if (ntiles > 0) tile_dma(src, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
+    if (ntiles > 0) tile_dma<W>(src, cache, tile_row(0), lds, lds + kKBytes, wave, lane, koff);
     __syncthreads();
     for (int ti = 0; ti < ntiles; ++ti) {
       const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
       if (ti + 1 < ntiles) {  // the next tile is in flight during the compute
         char* nK = lds + ((ti + 1) & 1) * (kKBytes + kVBytes);
-        tile_dma(src, cache, tile_row(ti + 1), nK, nK + kKBytes, wave, lane, koff);
+        tile_dma<W>(src, cache, tile_row(ti + 1), nK, nK + kKBytes, wave, lane, koff);
       }
       // (a window tile may cover sink rows too when S is not a multiple of 64: its mask
       // keeps keys >= S only, the sink tile's keys < S, so no key counts twice)
@@ -545,18 +564,18 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     const int ql = 32 * wave + col;
     float* mine = a.scratch + (int64_t(pair) * kg.nsplit + split) * kSlotFloats;
     {
-      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(mine);
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc<W>(mine);
 #pragma unroll
       for (int jd = 0; jd < 4; ++jd)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const u32x4 v = {__float_as_uint(o[jd][4 * j + 0]), __float_as_uint(o[jd][4 * j + 1]),
                            __float_as_uint(o[jd][4 * j + 2]), __float_as_uint(o[jd][4 * j + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o_chunk_offset(8 * jd + 2 * j + half, ql), 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o_chunk_offset<W>(8 * jd + 2 * j + half, ql), 0, kCoherent);
         }
       if (half == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, (kQRows * 128 + ql) * 4, 0, kCoherent);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, (kQRows * 128 + kQRows + ql) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, (kRows * 128 + ql) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, (kRows * 128 + kRows + ql) * 4, 0, kCoherent);
       }
     }
     if (!last_arrival(a.counters + pair, kg.nsplit)) return;
@@ -566,8 +585,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
     float M = m;
     for (int s2 = 0; s2 < kg.nsplit; ++s2) {
       if (s2 == split) continue;
-      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
-      M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)));
+      const __amdgpu_buffer_rsrc_t rs = slot_rsrc<W>(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
+      M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kRows * 128 + ql) * 4, 0, kCoherent)));
     }
     float L = 0.0f;
     f32x16 acc[4];
@@ -580,15 +599,15 @@ __global__ void __launch_bounds__(256, 2) k_prefill_mfma(PrefillArgs a) {
 #pragma unroll
         for (int jd = 0; jd < 4; ++jd) os[jd] = o[jd];
       } else {
-        const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
+        const __amdgpu_buffer_rsrc_t rs = slot_rsrc<W>(a.scratch + (int64_t(pair) * kg.nsplit + s2) * kSlotFloats);
         ws = __builtin_amdgcn_exp2f(
-            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + ql) * 4, 0, kCoherent)) - M);
-        ls = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kQRows * 128 + kQRows + ql) * 4, 0, kCoherent));
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kRows * 128 + ql) * 4, 0, kCoherent)) - M);
+        ls = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (kRows * 128 + kRows + ql) * 4, 0, kCoherent));
 #pragma unroll
         for (int jd = 0; jd < 4; ++jd)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o_chunk_offset(8 * jd + 2 * j + half, ql), 0, kCoherent);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o_chunk_offset<W>(8 * jd + 2 * j + half, ql), 0, kCoherent);
 #pragma unroll
             for (int i = 0; i < 4; ++i) os[jd][4 * j + i] = __uint_as_float(v[i]);
           }
@@ -769,13 +788,20 @@ __device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const Cache
 
 }  // namespace
 
-// Grid of n_heads query heads (KV-head-major) over chunk rows [q0, q0 + nq): head groups
-// of the largest of 4, 2, 1 heads that divides G, query blocks of 128 / pack rows.
-static KindGrid kind_grid(const Geom& g, int n_heads, int q0, int nq, int nsplit) {
+// Wavefronts per prefill workgroup: 8 when G is a multiple of 4 (four heads of a KV head
+// in every workgroup, two 32-query slices each), else 4.  The streaming caches' update
+// joins the prefill launch only with 4 (its blocks have 256 threads).
+int prefill_waves(const Geom& g) { return g.G % 4 == 0 ? 8 : 4; }
+bool prefill_fuses_update(const Geom& g) { return prefill_waves(g) == 4; }
+
+// Grid of n_heads query heads (KV-head-major) over chunk rows [q0, q0 + nq) for
+// workgroups of W wavefronts: head groups of the largest of 4, 2, 1 heads that divides
+// G, query blocks of 32 W / pack rows.
+static KindGrid kind_grid(const Geom& g, int W, int n_heads, int q0, int nq, int nsplit) {
   KindGrid k = {};
   k.n_heads = n_heads;
   k.pack = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
-  k.qrows = kQRows / k.pack;
+  k.qrows = 32 * W / k.pack;
   k.n_qblocks = (nq + k.qrows - 1) / k.qrows;
   k.nsplit = nsplit;
   k.q0 = q0;
@@ -785,8 +811,8 @@ static KindGrid kind_grid(const Geom& g, int n_heads, int q0, int nq, int nsplit
 }
 
 // Streaming-head grid of the queries in chunk rows [q0, q0 + nq).
-static KindGrid streaming_grid(const Geom& g, const LayerView& lv, int q0, int nq) {
-  return kind_grid(g, lv.n_str * g.G, q0, nq, 1);
+static KindGrid streaming_grid(const Geom& g, int W, const LayerView& lv, int q0, int nq) {
+  return kind_grid(g, W, lv.n_str * g.G, q0, nq, 1);
 }
 
 static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
@@ -800,7 +826,7 @@ static PrefillArgs prefill_args(const Geom& g, const LayerView& lv, const CacheR
   a.t0 = t0;
   a.stage = stage;
   a.stage_sink_rows = stage_sink_rows(g.S);
-  a.ret = a.str = kind_grid(g, 0, 0, 0, 1);
+  a.ret = a.str = kind_grid(g, 4, 0, 0, 0, 1);
   return a;
 }
 
@@ -827,37 +853,44 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
                                const void* upd_v) {
   PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
   a.out_lambda = static_cast<uint16_t*>(out_lambda);
-  if (upd_k && g.B * lv.n_str > 0) {  // the streaming caches' update joins the launch
+  const int W = prefill_waves(g);
+  const int64_t slot_floats = W == 8 ? Shape<8>::kSlotFloats : Shape<4>::kSlotFloats;
+  if (W == 4 && upd_k && g.B * lv.n_str > 0) {  // the streaming caches' update joins the launch
     a.upd = update_scalars(g, lv, upd_k, upd_v, T, t0);
     a.upd_blocks = a.upd.str_tiles * g.B * lv.n_str;
   }
   KindGrid& r = a.ret;
-  r = kind_grid(g, lv.n_ret * g.G, 0, T, 1);
+  r = kind_grid(g, W, lv.n_ret * g.G, 0, T, 1);
   // Split a query block's keys over two workgroups when the retrieval blocks alone would
-  // leave fewer than two workgroups per CU (one wavefront per SIMD cannot hide its own
+  // leave fewer than eight wavefronts per CU (one wavefront per SIMD cannot hide its own
   // MFMA, LDS and barrier latencies) and the keys and scratch allow it.
   const int64_t pairs = int64_t(g.B) * (r.n_heads / r.pack) * r.n_qblocks;
   int nsplit = 1;
-  if (pairs < 2 * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
-      pairs * 2 * kSlotFloats <= scratch_floats)
+  if (pairs < 8 / W * int64_t(num_cu) && t0 + T >= 2048 && pairs <= kPrefillCounters &&
+      pairs * 2 * slot_floats <= scratch_floats)
     nsplit = 2;
   if (const char* e = std::getenv("DUO_PREFILL_SPLIT")) {
     const int f = std::atoi(e);
-    if (f == 1 || (f == 2 && pairs <= kPrefillCounters && pairs * 2 * kSlotFloats <= scratch_floats)) nsplit = f;
+    if (f == 1 || (f == 2 && pairs <= kPrefillCounters && pairs * 2 * slot_floats <= scratch_floats)) nsplit = f;
   }
   r.nsplit = nsplit;
   r.blocks = static_cast<int>(pairs * nsplit);
   a.scratch = scratch;
   a.counters = counters;
   if (out_lambda) {  // every head, every query of the chunk, over the retrieval caches
-    a.str = kind_grid(g, r.n_heads, 0, T, 1);
+    a.str = kind_grid(g, W, r.n_heads, 0, T, 1);
   } else {
-    a.str = streaming_grid(g, lv, 0, nq_streaming);
+    a.str = streaming_grid(g, W, lv, 0, nq_streaming);
   }
   a.stage_p0 = t0 - stage_window_rows(g.R);
   const int64_t blocks = int64_t(r.blocks) + a.str.blocks + a.upd_blocks;
   if (blocks == 0) return hipSuccess;
-  launch(k_prefill_mfma, dim3(static_cast<unsigned>(blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  if (W == 8)
+    launch(k_prefill_mfma<8>, dim3(static_cast<unsigned>(blocks)), dim3(Shape<8>::kThreads), 2 * (kKBytes + kVBytes),
+           st, a);
+  else
+    launch(k_prefill_mfma<4>, dim3(static_cast<unsigned>(blocks)), dim3(Shape<4>::kThreads), 2 * (kKBytes + kVBytes),
+           st, a);
   return hipGetLastError();
 }
 
@@ -902,11 +935,14 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
 
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st) {
+  // (streaming heads only: short blocks, for which 4-wavefront workgroups, two per CU,
+  // measured faster than the shared tiles of 8)
   PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
-  a.str = streaming_grid(g, lv, q0, nq);
+  a.str = streaming_grid(g, 4, lv, q0, nq);
   a.stage_p0 = t0 + q0 - stage_window_rows(g.R);
   if (a.str.blocks == 0) return hipSuccess;
-  launch(k_prefill_mfma, dim3(static_cast<unsigned>(a.str.blocks)), dim3(256), 2 * (kKBytes + kVBytes), st, a);
+  launch(k_prefill_mfma<4>, dim3(static_cast<unsigned>(a.str.blocks)), dim3(Shape<4>::kThreads),
+         2 * (kKBytes + kVBytes), st, a);
   return hipGetLastError();
 }
 
