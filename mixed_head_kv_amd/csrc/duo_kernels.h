@@ -45,11 +45,13 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
 // keys [0, t0 + T) read from the retrieval caches, so the chunk must have been appended
 // there first) and the streaming-head queries of chunk rows [0, nq_streaming) over the
 // keys staged by launch_chunk_tiles.  When the retrieval blocks alone are few (under
-// two workgroups per CU) each block's key range is split over two workgroups that merge
-// through `scratch` (fp32 partials, coherent) and `counters` (kPrefillCounters ints,
-// zero between calls).
+// eight wavefronts per CU) each block's key range is split over two workgroups that
+// merge through `scratch` (fp32 partials, coherent) and `counters` (kPrefillCounters
+// ints, zero between calls).
 // upd_k / upd_v != null: the streaming caches' update with the chunk (K/V inputs) runs
-// in the same launch (valid when no later staging reads the caches as they stood).
+// in the same launch (valid when no later staging reads the caches as they stood); only
+// when prefill_fuses_update(g), else they are ignored and the caller updates the caches
+// with launch_stream_cache_update.
 // out_lambda != null (every KV head a retrieval head): the second grid computes every
 // head's sink + window attention over the retrieval caches for all T queries and writes
 // it there, beside the full causal output in `out`.

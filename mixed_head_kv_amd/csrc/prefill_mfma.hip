@@ -12,8 +12,8 @@
 // approach section; cn.bg3.co article, 研究背景 section (pre-filling cost of full
 // attention grows quadratically with the context).
 //
-// Workgroup: 4 wavefronts x 32 queries; under GQA its wavefronts take up to 4 query
-// heads of one KV head (the same 32 queries, or two slices of 32 for 2 heads), so each
+// Workgroup: 4 or 8 wavefronts x 32 queries; under GQA its wavefronts take up to 4 query
+// heads of one KV head (each head's query slices spread over the wavefronts), so each
 // K/V tile in LDS serves every head of the group.  Keys move HBM -> LDS with
 // direct loads in 64-key tiles, double-buffered (K rows with their 16-byte chunks
 // XOR-swizzled by the row index so the permuted row reads hit distinct banks; V in
