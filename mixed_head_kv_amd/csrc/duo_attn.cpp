@@ -601,7 +601,7 @@ static int run_prefill(duo_handle* h, const duo::Geom& g, const LayerView& lv, c
     if (e != hipSuccess) return hip_fail(e, "prefill append and staging");
     // When every streaming-head query was staged above, the streaming caches' update
     // (nothing later reads them as they stood) joins the attention launch.
-    const bool fuse_update = duo::prefill_fuses_update(g) && n_tokens <= h->stage_tokens;
+    const bool fuse_update = n_tokens <= h->stage_tokens;
     {  // retrieval heads and the first staged streaming-head queries, one launch
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
       e = duo::launch_prefill_mfma(g, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,

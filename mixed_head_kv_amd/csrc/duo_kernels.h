@@ -49,9 +49,7 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
 // merge through `scratch` (fp32 partials, coherent) and `counters` (kPrefillCounters
 // ints, zero between calls).
 // upd_k / upd_v != null: the streaming caches' update with the chunk (K/V inputs) runs
-// in the same launch (valid when no later staging reads the caches as they stood); only
-// when prefill_fuses_update(g), else they are ignored and the caller updates the caches
-// with launch_stream_cache_update.
+// in the same launch (valid when no later staging reads the caches as they stood).
 // out_lambda != null (every KV head a retrieval head): the second grid computes every
 // head's sink + window attention over the retrieval caches for all T queries and writes
 // it there, beside the full causal output in `out`.
@@ -79,10 +77,8 @@ hipError_t launch_stream_cache_update(const Geom& g, const LayerView& lv, const 
 // Streaming-head (sink + window) prefill on bf16 MFMA (D = 128) of the queries in chunk
 // rows [q0, q0 + nq) (at most kStageTokens), over the keys staged by launch_chunk_tiles;
 // for the queries after the first kStageTokens of a chunk.
-// Wavefronts per MFMA prefill workgroup for a layer shape (4 or 8), and whether the
-// streaming caches' update can join the prefill launch (upd_k / upd_v above).
+// Wavefronts per MFMA prefill workgroup for a layer shape (4 or 8).
 int prefill_waves(const Geom& g);
-bool prefill_fuses_update(const Geom& g);
 
 hipError_t launch_prefill_stream_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q,
                                       void* out, int T, int64_t t0, int q0, int nq, hipStream_t st);

@@ -137,7 +137,7 @@ struct ChunkScalars {
 
 template <bool UPDATE>
 __device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const CacheRegion& stage, const ChunkScalars& a,
-                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128]);
+                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128], int tid, bool active);
 
 struct PrefillArgs {
   Geom g;
@@ -161,7 +161,8 @@ struct PrefillArgs {
   // chunk (the k_chunk_tiles<true> pass), run in the same launch when every streaming
   // query of the chunk was staged before it (nothing later reads the cache as it stood).
   ChunkScalars upd;
-  int upd_blocks;
+  int upd_tiles;        // 64-row update tiles (str_tiles per streaming cache)
+  int upd_blocks;       // workgroups running them, W / 4 tiles each
 };
 
 // Partial of one split of one workgroup's block: O [rows][128 dims], then m[rows],
@@ -396,15 +397,18 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
   constexpr int kSlotFloats = Shape<W>::kSlotFloats;
 
   const Geom& g = a.g;
-  if constexpr (W == 4) {  // (the update blocks are 256-thread blocks)
-    const int upd0 = a.ret.blocks + a.str.blocks;
-    if (static_cast<int>(blockIdx.x) >= upd0) {  // uniform: a streaming cache update block
-      const int id = static_cast<int>(blockIdx.x) - upd0;
-      chunk_tiles_body<true>(g, a.lv, a.stage, a.upd, id % a.upd.str_tiles, id / a.upd.str_tiles,
-                             reinterpret_cast<uint4(*)[16]>(lds),
-                             reinterpret_cast<uint16_t(*)[128]>(lds + kStageRows * 16 * 16));
-      return;
-    }
+  const int upd0 = a.ret.blocks + a.str.blocks;
+  if (static_cast<int>(blockIdx.x) >= upd0) {  // uniform: streaming cache update tiles
+    // (256-thread tiles: a workgroup of W wavefronts runs W / 4 of them, each with its
+    // own 32 KB of the LDS; a part past the last tile still takes the tile's barrier)
+    const int part = static_cast<int>(threadIdx.x) >> 8;
+    const int id = (static_cast<int>(blockIdx.x) - upd0) * (W / 4) + part;
+    char* mine = lds + part * (kStageRows * 16 * 16 + kStageRows * 128 * 2);
+    chunk_tiles_body<true>(g, a.lv, a.stage, a.upd, id % a.upd.str_tiles, id / a.upd.str_tiles,
+                           reinterpret_cast<uint4(*)[16]>(mine),
+                           reinterpret_cast<uint16_t(*)[128]>(mine + kStageRows * 16 * 16),
+                           static_cast<int>(threadIdx.x) & 255, id < a.upd_tiles);
+    return;
   }
   const bool streaming = static_cast<int>(blockIdx.x) >= a.ret.blocks;  // uniform
   const KindGrid& kg = streaming ? a.str : a.ret;
@@ -683,18 +687,22 @@ __global__ void __launch_bounds__(256) k_chunk_tiles(ChunkTileArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_k[kStageRows][16];  // chunk c of row r at [r][c ^ (r & 15)]
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kStageRows][128];
   chunk_tiles_body<UPDATE>(a.g, a.lv, a.stage, a.s, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), s_k,
-                           s_v);
+                           s_v, static_cast<int>(threadIdx.x), true);
 }
 
-// One 64-row tile (bx) of one cache (by) of a chunk-tile pass; s_k, s_v: this workgroup's
-// LDS (s_k: chunk c of row r at [r][c ^ (r & 15)]).
+// One 64-row tile (bx) of one cache (by) of a chunk-tile pass, run by 256 threads (tid
+// 0..255); s_k, s_v: their LDS (s_k: chunk c of row r at [r][c ^ (r & 15)]).  Inactive
+// (or past the last tile), the threads only take the one barrier the tile's threads
+// take, so 256-thread parts of a larger workgroup stay in step.
 template <bool UPDATE>
 __device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const CacheRegion& stage, const ChunkScalars& a,
-                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128]) {
-  const bool ret = by < a.ret_caches;
-  if (bx >= (ret ? a.ret_tiles : a.str_tiles)) return;  // uniform
+                                 int bx, int by, uint4 (*s_k)[16], uint16_t (*s_v)[128], int tid, bool active) {
+  const bool ret = active && by < a.ret_caches;
+  if (!active || bx >= (ret ? a.ret_tiles : a.str_tiles)) {  // uniform over the 256 threads
+    __syncthreads();
+    return;
+  }
   const bool update = UPDATE && !ret;
-  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cache = ret ? by : by - a.ret_caches;  // b * n_kind + index
   const int n_kind = ret ? lv.n_ret : lv.n_str;
@@ -788,11 +796,10 @@ __device__ void chunk_tiles_body(const Geom& g, const LayerView& lv, const Cache
 
 }  // namespace
 
-// Wavefronts per prefill workgroup: 8 when G is a multiple of 4 (four heads of a KV head
-// in every workgroup, two 32-query slices each), else 4.  The streaming caches' update
-// joins the prefill launch only with 4 (its blocks have 256 threads).
+// Wavefronts per prefill workgroup for a chunk's attention: 8 when G is a multiple of 4
+// (four heads of a KV head in every workgroup, two 32-query slices each), else 4 (MHA:
+// 256-query blocks measured slower than 128).  The streaming-only launches use 4.
 int prefill_waves(const Geom& g) { return g.G % 4 == 0 ? 8 : 4; }
-bool prefill_fuses_update(const Geom& g) { return prefill_waves(g) == 4; }
 
 // Grid of n_heads query heads (KV-head-major) over chunk rows [q0, q0 + nq) for
 // workgroups of W wavefronts: head groups of the largest of 4, 2, 1 heads that divides
@@ -855,9 +862,10 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
   a.out_lambda = static_cast<uint16_t*>(out_lambda);
   const int W = prefill_waves(g);
   const int64_t slot_floats = W == 8 ? Shape<8>::kSlotFloats : Shape<4>::kSlotFloats;
-  if (W == 4 && upd_k && g.B * lv.n_str > 0) {  // the streaming caches' update joins the launch
+  if (upd_k && g.B * lv.n_str > 0) {  // the streaming caches' update joins the launch
     a.upd = update_scalars(g, lv, upd_k, upd_v, T, t0);
-    a.upd_blocks = a.upd.str_tiles * g.B * lv.n_str;
+    a.upd_tiles = a.upd.str_tiles * g.B * lv.n_str;
+    a.upd_blocks = (a.upd_tiles + W / 4 - 1) / (W / 4);
   }
   KindGrid& r = a.ret;
   r = kind_grid(g, W, lv.n_ret * g.G, 0, T, 1);
