@@ -350,6 +350,33 @@ def test_llama3_8b_gqa_128k_layer(torch_cuda):
     assert np.isfinite(to_f64(dec)).all() and np.isfinite(to_f64(pre)).all()
 
 
+@pytest.mark.parametrize("name", ["mha", "gqa"])
+def test_one_call_prefill_of_a_long_prompt(torch_cuda, name):
+    """A whole prompt in one prefill call: 32768 tokens of the 32K MHA layer (8 of 32 heads
+    retrieval; 256 query blocks per head, the streaming heads' keys staged in 8 passes
+    inside the call) or 16384 tokens of a GQA layer with 4 query heads per KV head
+    (8-wavefront workgroups), then 4 decode steps.  Checked, all heads: every decode step;
+    prefill rows: the first and last 256, +-R rows around every 4096-row staging pass, and
+    512 seeded rows."""
+    w = {
+        "mha": W("oneshot_mha", 81, 32, 32, 128, "bf16", 64, 256, 32768 + 4, 4, 8),
+        "gqa": W("oneshot_gqa", 82, 32, 8, 128, "bf16", 64, 256, 16384 + 4, 4, 4),
+    }[name]
+    L = w.context - w.decode_steps
+    say(f"one-call prefill {name}: {L} tokens")
+    kv, pre, dec, total = run_layer(w, [L], w.decode_steps)
+    rng = np.random.default_rng(7)
+    rows = set(range(256)) | set(range(L - 256, L)) | set(rng.integers(0, L, 512).tolist())
+    for a in range(4096, L, 4096):
+        rows |= set(range(a - w.recent, min(L, a + w.recent)))
+    rows = np.array(sorted(rows))
+    say(f"  oracle: {len(rows)} prefill rows and {w.decode_steps} decode steps, all heads")
+    ref = oracle_rows_threaded(w, 0, np.concatenate([rows, np.arange(L, total)]), total)
+    compare(f"one-call {name} decode", to_f64(dec), ref[len(rows):], TOL["bf16"])
+    compare(f"one-call {name} prefill (sampled rows)", to_f64(pre[rows]), ref[:len(rows)], TOL["bf16"])
+    assert np.isfinite(to_f64(pre)).all()
+
+
 STACK_LAYERS = (0, 15, 31)
 
 
