@@ -208,14 +208,16 @@ def test_tiny_workload_exact_config(torch_cuda):
 
 
 @pytest.mark.parametrize("split", [None, "2"])
-def test_outputs_are_bitwise_repeatable(torch_cuda, monkeypatch, split):
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16"])
+def test_outputs_are_bitwise_repeatable(torch_cuda, monkeypatch, name, split):
     """Same inputs, same bits, including when query blocks are split over two workgroups
-    (merged in split order whichever finishes last)."""
+    (merged in split order whichever finishes last); 8-wavefront (GQA) and 4-wavefront
+    (MHA) prefill workgroups."""
     if split:
         monkeypatch.setenv("DUO_PREFILL_SPLIT", split)
-    w = SMALL["gqa_bf16"]
-    say(f"repeatability split={split}")
-    runs = [run_layer(w, CHUNKS["gqa_bf16"], 5) for _ in range(3)]
+    w = SMALL[name]
+    say(f"repeatability {name} split={split}")
+    runs = [run_layer(w, CHUNKS[name], 5) for _ in range(3)]
     for _, p, d, _ in runs[1:]:
         assert torch_cuda.equal(runs[0][1], p) and torch_cuda.equal(runs[0][2], d)
 
