@@ -41,9 +41,9 @@
  * - A handle is not thread-safe.
  * - Fault injection, for tests of error handling: when the environment variable
  *   DUO_FAULT_INJECT holds "all" or a comma-separated list of entry-point names
- *   (e.g. "duo_decode,duo_kv_append"), each named call of duo_kv_init, duo_prefill,
- *   duo_prefill_seq, duo_prefill_dual, duo_kv_append, duo_kv_append_seq, duo_decode,
- *   duo_decode_static, duo_kv_read and duo_kv_read_int4 returns DUO_E_HIP after its
+ *   (e.g. "duo_decode,duo_kv_append"), each named call of duo_kv_init, duo_kv_attach,
+ *   duo_prefill, duo_prefill_seq, duo_prefill_dual, duo_kv_append, duo_kv_append_seq,
+ *   duo_decode, duo_decode_static, duo_kv_read and duo_kv_read_int4 returns DUO_E_HIP after its
  *   argument checks, before any HIP call and without changing any state.  The
  *   variable is read at every call; unset or empty, nothing changes.
  *
@@ -130,6 +130,18 @@ int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes);
  * DUO_E_HIP (the fill kernel failed to launch; no handle is returned). */
 int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream,
                 duo_handle** out);
+
+/* Resume from a saved state: a handle over a workspace that holds what an earlier handle
+ * with the same config left in it between calls (its bytes saved and copied back, or
+ * the same memory), with the tokens held per layer and sequence given in the host array
+ * lengths[n_layers * batch] (layer-major; duo_kv_length_seq of the earlier handle).
+ * Nothing in the workspace is cleared or written (the first handle on a device still
+ * sets up that device's static scratch once).  Resuming this way and re-creating the
+ * state with duo_kv_init plus duo_kv_append of the same tokens give the same caches, so
+ * the same outputs.  Errors: as duo_kv_init, and DUO_E_INVALID for a null lengths array
+ * or a length outside 0..max_context. */
+int duo_kv_attach(const duo_config* cfg, void* d_workspace, uint64_t bytes, const int64_t* lengths,
+                  duo_handle** out);
 
 /* Workspace guard bands, for checks that no kernel writes outside its region: every
  * region of the workspace (each cache, the split scratch, the counters, the staging

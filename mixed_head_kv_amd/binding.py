@@ -35,7 +35,7 @@ EXPORTS = ["duo_kv_bytes", "duo_kv_init", "duo_prefill", "duo_kv_append", "duo_d
            "duo_kv_length",
            "duo_prefill_seq", "duo_kv_append_seq", "duo_kv_length_seq", "duo_prefill_dual", "duo_kv_free", "duo_last_error", "duo_kv_read", "duo_kv_read_int4", "duo_synth_fill",
            "duo_profile_enable", "duo_profile_collect", "duo_linear_w8", "duo_qkv_rope_w8",
-           "duo_profile_thread_enable", "duo_profile_thread_collect", "duo_kv_guard_bands"]
+           "duo_profile_thread_enable", "duo_profile_thread_collect", "duo_kv_guard_bands", "duo_kv_attach"]
 KERNEL_CLASSES = ["append", "prefill_retrieval", "prefill_streaming", "decode", "prefill_stage", "qkv_rope",
                   "linear"]
 
@@ -72,6 +72,7 @@ def lib():
     sig = {
         "duo_kv_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(u64)]),
         "duo_kv_init": (ctypes.c_int, [cfgp, vp, u64, vp, ctypes.POINTER(vp)]),
+        "duo_kv_attach": (ctypes.c_int, [cfgp, vp, u64, ctypes.POINTER(i64), ctypes.POINTER(vp)]),
         "duo_prefill": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp]),
         "duo_kv_append": (ctypes.c_int, [vp, i32, vp, vp, i32, vp]),
         "duo_decode": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
@@ -152,6 +153,16 @@ def duo_kv_init(cfg, workspace, stream=None):
     h = ctypes.c_void_p()
     _check(lib().duo_kv_init(ctypes.byref(cfg), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def duo_kv_attach(cfg, workspace, lengths):
+    """A handle over a workspace holding an earlier handle's state; lengths: the tokens
+    held per (layer, sequence), layer-major."""
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * max(len(lengths), 1))(*[int(x) for x in lengths])
+    _check(lib().duo_kv_attach(ctypes.byref(cfg), _ptr(workspace), workspace.numel() * workspace.element_size(), arr,
+                               ctypes.byref(h)))
     return h
 
 
@@ -332,6 +343,22 @@ class DuoKV:
 
     def length_seq(self, layer, seq):
         return duo_kv_length_seq(self.h, layer, seq)
+
+    def lengths(self):
+        """Tokens held per (layer, sequence), layer-major (what duo_kv_attach takes)."""
+        return [duo_kv_length_seq(self.h, layer, b) for layer in range(self.cfg.n_layers) for b in range(self.B)]
+
+    @classmethod
+    def attach(cls, like, workspace, lengths):
+        """A handle with `like`'s config over `workspace`, a saved copy of a workspace of
+        that config taken between calls, holding `lengths` tokens (duo_kv_attach)."""
+        self = cls.__new__(cls)
+        self.io, self.torch_dtype, self.cfg, self.nbytes = like.io, like.torch_dtype, like.cfg, like.nbytes
+        self.B, self.Hq, self.Hkv, self.D = like.B, like.Hq, like.Hkv, like.D
+        self.workspace = workspace
+        self.h = None
+        self.h = duo_kv_attach(self.cfg, workspace, lengths)
+        return self
 
     def prefill_seq(self, layer, seq, q, k, v, out=None):
         """One sequence's chunk: q, k, v of shape [1, T, heads, D] (or [T, heads, D])."""

@@ -418,17 +418,22 @@ int duo_kv_bytes(const duo_config* cfg, uint64_t* out_bytes) {
   return ok();
 }
 
-int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream, duo_handle** out) {
+// Checks shared by duo_kv_init and duo_kv_attach (config, workspace pointer and size);
+// fills the layout.
+static int check_workspace(const duo_config* cfg, void* d_workspace, uint64_t bytes, duo_handle** out, Layout* L) {
   int rc = validate_config(cfg);
   if (rc) return rc;
   if (!out) return fail(DUO_E_INVALID, "out is NULL");
   if (!d_workspace) return fail(DUO_E_INVALID, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign) return fail(DUO_E_INVALID, "workspace is not 256-byte aligned");
-  Layout L;
-  if (!make_layout(cfg, &L)) return fail(DUO_E_INVALID, "workspace size overflows");
-  if (bytes < L.total) return fail(DUO_E_CAPACITY, "workspace smaller than duo_kv_bytes()");
-  if ((rc = injected_fault("duo_kv_init"))) return rc;
+  if (!make_layout(cfg, L)) return fail(DUO_E_INVALID, "workspace size overflows");
+  if (bytes < L->total) return fail(DUO_E_CAPACITY, "workspace smaller than duo_kv_bytes()");
+  return DUO_OK;
+}
 
+// A handle over the workspace with every length 0 (host state only, apart from the
+// once-per-device set-up of the static scratch).
+static duo_handle* new_handle(const duo_config* cfg, void* d_workspace, uint64_t bytes, const Layout& L) {
   duo_handle* h = new duo_handle();
   h->cfg = *cfg;
   h->mask.assign(cfg->retrieval_mask, cfg->retrieval_mask + size_t(cfg->n_layers) * cfg->n_kv_heads);
@@ -495,6 +500,15 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   // I/O and head_dim 64 on the vector-ALU kernels.
   h->use_mfma = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128 && cfg->kv_format == DUO_KV_SAME_AS_IO;
   h->use_mfma_decode = cfg->io_dtype == DUO_DTYPE_BF16 && cfg->head_dim == 128;
+  return h;
+}
+
+int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* hip_stream, duo_handle** out) {
+  Layout L;
+  int rc = check_workspace(cfg, d_workspace, bytes, out, &L);
+  if (rc) return rc;
+  if ((rc = injected_fault("duo_kv_init"))) return rc;
+  duo_handle* h = new_handle(cfg, d_workspace, bytes, L);
   // Clear every cache and the counters.  The MFMA kernels read whole 32/64-row tiles
   // and weight rows past the valid length by exactly zero, which needs those rows
   // finite; cleared memory guarantees it.
@@ -508,6 +522,23 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
     delete h;
     return hip_fail(e, "clearing the workspace");
   }
+  *out = h;
+  return ok();
+}
+
+int duo_kv_attach(const duo_config* cfg, void* d_workspace, uint64_t bytes, const int64_t* lengths,
+                  duo_handle** out) {
+  Layout L;
+  int rc = check_workspace(cfg, d_workspace, bytes, out, &L);
+  if (rc) return rc;
+  if (!lengths) return fail(DUO_E_INVALID, "lengths is NULL");
+  const size_t n = size_t(cfg->n_layers) * cfg->batch;
+  for (size_t i = 0; i < n; ++i)
+    if (lengths[i] < 0 || lengths[i] > cfg->max_context)
+      return fail(DUO_E_INVALID, "lengths must be in 0..max_context");
+  if ((rc = injected_fault("duo_kv_attach"))) return rc;
+  duo_handle* h = new_handle(cfg, d_workspace, bytes, L);
+  h->len.assign(lengths, lengths + n);
   *out = h;
   return ok();
 }

@@ -110,6 +110,16 @@ int main() {
     expect(duo_kv_init(&k.c, reinterpret_cast<void*>(4096), need - 1, nullptr, &h), DUO_E_CAPACITY,
            "validation before the injected fault");
     unsetenv("DUO_FAULT_INJECT");
+    // resume over a saved workspace: lengths are checked before anything else happens
+    std::vector<int64_t> lens(size_t(k.c.n_layers) * k.c.batch, 3);
+    expect(duo_kv_attach(&k.c, reinterpret_cast<void*>(4096), need, nullptr, &h), DUO_E_INVALID, "attach null lengths");
+    lens[1] = k.c.max_context + 1;
+    expect(duo_kv_attach(&k.c, reinterpret_cast<void*>(4096), need, lens.data(), &h), DUO_E_INVALID,
+           "attach length past max_context");
+    lens[1] = 3;
+    expect(duo_kv_attach(&k.c, reinterpret_cast<void*>(4096), need - 1, lens.data(), &h), DUO_E_CAPACITY,
+           "attach small ws");
+    if (h) { std::printf("FAIL attach: handle returned\n"); ++g_fail; }
   }
   // calls on a NULL handle
   void* p = reinterpret_cast<void*>(4096);

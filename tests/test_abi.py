@@ -250,3 +250,28 @@ def test_guard_band_call_rejects_bad_arguments():
     _lib_or_skip()
     n = ctypes.c_int32()
     assert B.lib().duo_kv_guard_bands(None, None, 0, ctypes.byref(n)) == B.DUO_E_INVALID
+
+
+def test_attach_rejects_bad_arguments_before_any_hip_call(monkeypatch):
+    """duo_kv_attach (resume over a saved workspace) validates the config, the workspace and
+    every length before touching the device; an injected fault comes after that."""
+    _lib_or_skip()
+    cfg = _cfg()
+    rc, nbytes = _bytes(cfg)
+    assert rc == B.DUO_OK
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)
+    n = cfg.n_layers * cfg.batch
+    ok = (ctypes.c_int64 * n)(*([5] * n))
+    cases = [
+        (None, nbytes, B.DUO_E_INVALID),                                          # null lengths
+        ((ctypes.c_int64 * n)(*([-1] + [0] * (n - 1))), nbytes, B.DUO_E_INVALID),  # negative
+        ((ctypes.c_int64 * n)(*([cfg.max_context + 1] * n)), nbytes, B.DUO_E_INVALID),
+        (ok, nbytes - 1, B.DUO_E_CAPACITY),
+    ]
+    for lengths, size, want in cases:
+        rc = B.lib().duo_kv_attach(ctypes.byref(cfg), fake, size, lengths, ctypes.byref(h))
+        assert rc == want and not h.value, (rc, want)
+    monkeypatch.setenv("DUO_FAULT_INJECT", "duo_kv_attach")
+    rc = B.lib().duo_kv_attach(ctypes.byref(cfg), fake, nbytes, ok, ctypes.byref(h))
+    assert rc == B.DUO_E_HIP and not h.value and "fault injected" in B.duo_last_error()

@@ -294,6 +294,56 @@ def test_injected_faults_leave_state_unchanged(torch_cuda, monkeypatch):
     compare("after injected faults, decode", to_f64(dec), ref[300:], TOL["bf16"])
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16", "int4"])
+def test_resume_from_a_saved_workspace_or_replayed_appends(torch_cuda, name):
+    """Checkpoint and resume: after the prefill (int4: appends) and two decode steps the
+    state is saved (workspace bytes and the per-sequence lengths).  The next decode steps
+    on the original handle, on a handle attached to a copy of the saved bytes
+    (duo_kv_attach), and on a fresh handle refilled by appending the same tokens are
+    bitwise equal, and match the oracle."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    if name == "int4":
+        w = W("int4_resume", 26, 8, 4, 128, "bf16", 4, 32, 394, 6, 2, fmt="int4")
+        chunks, append_only = [150, 244], True
+    else:
+        w, chunks, append_only = SMALL[name], CHUNKS[name], False
+    L = sum(chunks)
+    total = L + w.decode_steps
+    say(f"resume {name}: {L} tokens, {w.decode_steps} decode steps")
+    kv = B.DuoKV.for_workload(w)
+    Q, K, V = (device_synth(w, 0, kind, 0, total) for kind in ("q", "k", "v"))
+    t = 0
+    for T in chunks:
+        if append_only:
+            kv.append(0, K[t:t + T], V[t:t + T])
+        else:
+            kv.prefill(0, Q[t:t + T], K[t:t + T], V[t:t + T])
+        t += T
+    for t in range(L, L + 2):
+        kv.decode(0, Q[t], K[t], V[t])
+    torch.cuda.synchronize()
+    saved, lengths = kv.workspace.clone(), kv.lengths()
+    assert lengths == [L + 2]
+
+    def rest(h):
+        return torch.stack([h.decode(0, Q[t], K[t], V[t]) for t in range(L + 2, total)])
+
+    out_a = rest(kv)
+    resumed = B.DuoKV.attach(kv, saved.clone(), lengths)
+    out_b = rest(resumed)
+    replayed = B.DuoKV.for_workload(w)
+    replayed.append(0, K[:L + 2], V[:L + 2])
+    out_c = rest(replayed)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b), "attached handle differs"
+    assert torch.equal(out_a, out_c), "replayed appends differ"
+    assert resumed.lengths() == replayed.lengths() == [total]
+    compare(f"resume {name}", to_f64(out_a), oracle_rows(w, 0, np.arange(L + 2, total), total), TOL["bf16"])
+    resumed.close()
+    replayed.close()
+
+
 def test_guard_band_check_sees_a_stray_write(torch_cuda):
     """The guard bands sit between the workspace's regions and hold the pattern after
     init and after work; a byte written into one (here from the host side, the way a
