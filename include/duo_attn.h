@@ -46,6 +46,10 @@
  *   duo_decode, duo_decode_static, duo_kv_read and duo_kv_read_int4 returns DUO_E_HIP after its
  *   argument checks, before any HIP call and without changing any state.  The
  *   variable is read at every call; unset or empty, nothing changes.
+ * - Launch log, for debugging: with the environment variable DUO_LOG set (non-empty, not
+ *   "0"), duo_kv_init, duo_kv_append, duo_prefill (bf16 head_dim 128 caches) and the
+ *   decode calls write one line each to stderr with their launch parameters (workspace
+ *   size; workgroup shape, splits and grid sizes).  Nothing else changes.
  *
  * Tensor layouts (row-major, contiguous, batch B = cfg.batch):
  *   Q, O for prefill : [B, T, n_q_heads, head_dim]      (token-major, as a fused QKV

@@ -48,6 +48,13 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(DUO_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// DUO_LOG set (non-empty, not "0"): every compute call writes one line of its launch
+// parameters to stderr.  Read at every call; changes nothing else.
+bool log_enabled() {
+  const char* e = std::getenv("DUO_LOG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
 // DUO_FAULT_INJECT ("all" or a comma-separated list of entry-point names): the named
 // call fails with DUO_E_HIP here, after its argument checks and before any HIP call or
 // state change.
@@ -509,6 +516,11 @@ int duo_kv_init(const duo_config* cfg, void* d_workspace, uint64_t bytes, void* 
   if (rc) return rc;
   if ((rc = injected_fault("duo_kv_init"))) return rc;
   duo_handle* h = new_handle(cfg, d_workspace, bytes, L);
+  if (log_enabled())
+    std::fprintf(stderr, "duo: init layers=%d batch=%d heads=%d/%d head_dim=%d workspace=%llu bytes (%zu guard bands) "
+                 "kernels=%s\n", cfg->n_layers, cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
+                 static_cast<unsigned long long>(L.total), L.guards.size(),
+                 h->use_mfma ? "mfma" : (h->use_mfma_decode ? "mfma decode, valu prefill" : "valu"));
   // Clear every cache and the counters.  The MFMA kernels read whole 32/64-row tiles
   // and weight rows past the valid length by exactly zero, which needs those rows
   // finite; cleared memory guarantees it.
@@ -633,13 +645,23 @@ static int run_prefill(duo_handle* h, const duo::Geom& g, const LayerView& lv, c
     // When every streaming-head query was staged above, the streaming caches' update
     // (nothing later reads them as they stood) joins the attention launch.
     const bool fuse_update = n_tokens <= h->stage_tokens;
+    duo::PrefillLaunchInfo info{};
     {  // retrieval heads and the first staged streaming-head queries, one launch
       KernelMark m(h, DUO_KERNEL_PREFILL_RETRIEVAL, st);
       e = duo::launch_prefill_mfma(g, lv, h->stage, q, out, n_tokens, t0, nq0, h->partials, h->partial_floats,
                                    h->prefill_counters, h->num_cu, st, nullptr, fuse_update ? k : nullptr,
-                                   fuse_update ? v : nullptr);
+                                   fuse_update ? v : nullptr, &info);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill attention");
+    if (log_enabled())
+      std::fprintf(stderr,
+                   "duo: prefill t0=%lld tokens=%d batch=%d workgroups of %d wavefronts (%d heads x %d queries) "
+                   "retrieval=%d (key splits %d) streaming=%d (first %d queries, staged passes %d) "
+                   "cache update=%s\n",
+                   static_cast<long long>(t0), n_tokens, g.B, info.waves, info.pack, info.qrows, info.ret_blocks,
+                   info.nsplit, info.str_blocks, nq0,
+                   nq0 > 0 ? (n_tokens + h->stage_tokens - 1) / h->stage_tokens : 0,
+                   fuse_update ? "in the launch" : "own launch");
     // further streaming-head queries, at most stage_tokens per launch pair (the staging
     // capacity)
     for (int q0 = h->stage_tokens; q0 < n_tokens && nq0 > 0; q0 += h->stage_tokens) {
@@ -746,6 +768,9 @@ int duo_kv_append(duo_handle* h, int32_t layer, const void* k, const void* v, in
   int64_t t0 = 0;
   if ((rc = batch_len(h, layer, &t0)) || (rc = check_tokens(t0, h->cfg.max_context, n_tokens))) return rc;
   if ((rc = injected_fault("duo_kv_append"))) return rc;
+  if (log_enabled())
+    std::fprintf(stderr, "duo: append layer=%d t0=%lld tokens=%d batch=%d\n", layer, static_cast<long long>(t0),
+                 n_tokens, h->cfg.batch);
   hipError_t e;
   {
     KernelMark m(h, DUO_KERNEL_APPEND, as_stream(hip_stream));
@@ -808,6 +833,12 @@ static int run_decode(const char* call, duo_handle* h, int32_t layer, const void
   duo::DecodePlan p;
   if (!make_plan(h, layer, tmax, partials, counters, max_splits, &p)) return DUO_E_UNSUPPORTED;
   if ((rc = injected_fault(call))) return rc;
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "duo: %s layer=%d t=%lld batch=%d varlen=%d retrieval=%d splits x %d keys streaming=%d splits x %d "
+                 "slots max_splits=%d append=%d kernel=%s\n",
+                 call, layer, static_cast<long long>(tmax), B, uniform ? 0 : 1, p.nsplit_r, p.chunk_r, p.nsplit_s,
+                 p.chunk_s, p.max_splits, append ? 1 : 0, h->use_mfma_decode ? "mfma" : "valu");
   if (!uniform) {
     p.varlen = 1;
     for (int32_t b = 0; b < B; ++b) p.t_seq[b] = seq_len(h, layer, b) - (append ? 0 : 1);

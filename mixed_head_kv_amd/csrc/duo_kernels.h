@@ -53,10 +53,16 @@ hipError_t launch_prefill_valu(const Geom& g, const LayerView& lv, const void* q
 // out_lambda != null (every KV head a retrieval head): the second grid computes every
 // head's sink + window attention over the retrieval caches for all T queries and writes
 // it there, beside the full causal output in `out`.
+// What a prefill launch was (filled when `info` is given): workgroup shape and grid.
+struct PrefillLaunchInfo {
+  int waves, pack, qrows, nsplit;
+  int ret_blocks, str_blocks, upd_blocks;
+};
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
                                int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
                                int* counters, int num_cu, hipStream_t st, void* out_lambda = nullptr,
-                               const void* upd_k = nullptr, const void* upd_v = nullptr);
+                               const void* upd_k = nullptr, const void* upd_v = nullptr,
+                               PrefillLaunchInfo* info = nullptr);
 
 // Chunk keys into the layouts the MFMA prefill loads directly (bf16, D = 128), one
 // launch: with `retrieval`, rows [t0, t0 + T) of every retrieval cache (the append);

@@ -857,7 +857,7 @@ static ChunkScalars update_scalars(const Geom& g, const LayerView& lv, const voi
 hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRegion& stage, const void* q, void* out,
                                int T, int64_t t0, int nq_streaming, float* scratch, int64_t scratch_floats,
                                int* counters, int num_cu, hipStream_t st, void* out_lambda, const void* upd_k,
-                               const void* upd_v) {
+                               const void* upd_v, PrefillLaunchInfo* info) {
   PrefillArgs a = prefill_args(g, lv, stage, q, out, T, t0);
   a.out_lambda = static_cast<uint16_t*>(out_lambda);
   const int W = prefill_waves(g);
@@ -892,6 +892,7 @@ hipError_t launch_prefill_mfma(const Geom& g, const LayerView& lv, const CacheRe
   }
   a.stage_p0 = t0 - stage_window_rows(g.R);
   const int64_t blocks = int64_t(r.blocks) + a.str.blocks + a.upd_blocks;
+  if (info) *info = PrefillLaunchInfo{W, r.pack, r.qrows, r.nsplit, r.blocks, a.str.blocks, a.upd_blocks};
   if (blocks == 0) return hipSuccess;
   if (W == 8)
     launch(k_prefill_mfma<8>, dim3(static_cast<unsigned>(blocks)), dim3(Shape<8>::kThreads), 2 * (kKBytes + kVBytes),

@@ -344,6 +344,26 @@ def test_resume_from_a_saved_workspace_or_replayed_appends(torch_cuda, name):
     replayed.close()
 
 
+def test_launch_log_reports_the_plan_and_changes_nothing(torch_cuda, monkeypatch, capfd):
+    """DUO_LOG=1: init, prefill and every decode step write one line of launch parameters
+    to stderr (here 8-wavefront workgroups of 4 heads x 64 queries); the outputs are the
+    unlogged run's, bit for bit."""
+    w = SMALL["gqa_bf16"]
+    say("launch log")
+    _, pre0, dec0, _ = run_layer(w, [300], 2)
+    torch_cuda.cuda.synchronize()
+    capfd.readouterr()
+    monkeypatch.setenv("DUO_LOG", "1")
+    _, pre1, dec1, _ = run_layer(w, [300], 2)
+    torch_cuda.cuda.synchronize()
+    lines = [ln for ln in capfd.readouterr().err.splitlines() if ln.startswith("duo: ")]
+    assert sum(ln.startswith("duo: init") for ln in lines) == 1, lines
+    pre_lines = [ln for ln in lines if ln.startswith("duo: prefill t0=0 tokens=300")]
+    assert len(pre_lines) == 1 and "workgroups of 8 wavefronts (4 heads x 64 queries)" in pre_lines[0], lines
+    assert sum(ln.startswith("duo: duo_decode layer=0 t=30") for ln in lines) == 2, lines
+    assert torch_cuda.equal(pre0, pre1) and torch_cuda.equal(dec0, dec1)
+
+
 def test_guard_band_check_sees_a_stray_write(torch_cuda):
     """The guard bands sit between the workspace's regions and hold the pattern after
     init and after work; a byte written into one (here from the host side, the way a
