@@ -344,6 +344,41 @@ def test_resume_from_a_saved_workspace_or_replayed_appends(torch_cuda, name):
     replayed.close()
 
 
+@pytest.mark.parametrize("hq", [16, 4])
+def test_planted_needles_dominate_like_the_oracle(torch_cuda, hq):
+    """Planted needles: queries share one direction u; two retrieval-cache keys (positions
+    123 and 517) and one sink key (position 2) are large multiples of u, so once visible
+    they outweigh every other key by ~40-60 in log2 units.  The running maximum must jump
+    far past its slack mid-sequence (prefill and decode), and the outputs must match the
+    oracle on every row and head (hq = 16: 8-wavefront prefill workgroups; 4: MHA)."""
+    import torch
+    from mixed_head_kv_amd import binding as B
+    from oracle import attention as OA
+    hkv, D, S, R, L, steps = 4, 128, 4, 64, 700, 4
+    total = L + steps
+    g = torch.Generator().manual_seed(5)
+    u = torch.randn(D, generator=g)
+    q = (u + 0.1 * torch.randn(total, hq, D, generator=g)).to(torch.bfloat16)
+    k = torch.randn(total, hkv, D, generator=g)
+    v = torch.randn(total, hkv, D, generator=g)
+    unit = u / u.norm()
+    for pos, alpha in ((2, 40.0), (123, 40.0), (517, 60.0)):
+        k[pos] = alpha * unit
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    mask = np.array([[1, 0, 1, 0]], dtype=np.uint8)
+    say(f"needles hq={hq}")
+    kv = B.DuoKV(1, hq, hkv, D, S, R, total, mask)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    pre = [kv.prefill(0, qd[a:b], kd[a:b], vd[a:b]) for a, b in ((0, 300), (300, L))]
+    dec = [kv.decode(0, qd[t], kd[t], vd[t]) for t in range(L, total)]
+    torch.cuda.synchronize()
+    got = np.concatenate([to_f64(torch.cat(pre)), to_f64(torch.stack(dec))])
+    ref = OA.layer_attention(q.double().numpy(), np.arange(total), k.double().numpy(), v.double().numpy(),
+                             mask[0].astype(bool), S, R)
+    compare(f"needles hq={hq}", got, ref, TOL["bf16"])
+    kv.close()
+
+
 def test_launch_log_reports_the_plan_and_changes_nothing(torch_cuda, monkeypatch, capfd):
     """DUO_LOG=1: init, prefill and every decode step write one line of launch parameters
     to stderr (here 8-wavefront workgroups of 4 heads x 64 queries); the outputs are the
