@@ -807,6 +807,8 @@ DUAL = {
     "mha_sink64": (W("dual_mha", 42, 8, 8, 128, "bf16", 64, 256, 1700, 3, 8), [700, 1000]),
     "nosink": (W("dual_nosink", 43, 4, 2, 128, "bf16", 0, 8, 300, 2, 2), [37, 263]),
     "long_chunk": (W("dual_long", 44, 4, 2, 128, "bf16", 16, 128, 4700, 2, 2), [4600, 100]),
+    # the 128K layer's shape and chunk (4 query heads per KV head: 8-wavefront workgroups)
+    "gqa_8192": (W("dual_gqa_8192", 45, 32, 8, 128, "bf16", 64, 256, 8292, 2, 8), [8192, 100]),
 }
 
 
