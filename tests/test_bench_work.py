@@ -55,3 +55,19 @@ def test_extras_grids_match_the_launch_shapes():
     assert k["out_proj_prefill"] == ("k_w8_gemm<", 16 * 16 * 512)
     k3 = bench.extra_kernels("llama3_8b_gqa_32layer_1m")
     assert k3["qkv_rope_decode"][1] == 6144 // 16 * 512 and "qkv_rope_prefill" not in k3
+
+
+def test_launch_kinds_follow_the_prefill_grid_rules():
+    """The prefill launches are told apart by grid in the profile summaries: the chunk's
+    streaming-only launches use 4-wavefront workgroups of 128 / pack queries x pack heads
+    (pack = 4 for the 128K GQA layer: 4 head groups x 128 blocks x 256 threads), every
+    other k_prefill_mfma launch is the chunk's main launch; a 4096-token chunk (32K MHA
+    layer) has no streaming-only launch."""
+    assert bench.streaming_only_grid("llama3_8b_gqa_128k") == 4 * (4096 // 32) * 256
+    assert bench.streaming_only_grid("llama2_7b_mha_32k") is None
+    name = "duo::(anonymous namespace)::k_prefill_mfma<4>(duo::(anonymous namespace)::PrefillArgs)"
+    assert bench.launch_kind(name, 131072, "llama3_8b_gqa_128k") == "prefill_streaming_attention"
+    main = name.replace("<4>", "<8>")
+    assert bench.launch_kind(main, (512 + 256) * 512, "llama3_8b_gqa_128k") == "prefill_attention"
+    assert bench.launch_kind("duo::k_decode_mfma(args)", 1, "llama3_8b_gqa_128k") == "decode_attention"
+    assert bench.launch_kind("duo::k_synth<1>(args)", 1, "llama3_8b_gqa_128k") is None
