@@ -670,6 +670,24 @@ def test_batched_sequences_match_oracle(torch_cuda, name):
             assert np.array_equal(got, hist[:, g]), (name, b, "retrieval K cache")
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_bf16"])
+def test_batched_split_key_prefill_matches_oracle(torch_cuda, monkeypatch, name):
+    """Three sequences with every query block's keys split over two workgroups (forced):
+    the split partials and arrival counters of each sequence's blocks are kept apart, on
+    8-wavefront (GQA) and 4-wavefront (MHA) workgroups."""
+    monkeypatch.setenv("DUO_PREFILL_SPLIT", "2")
+    base = SMALL[name]
+    w = base.scaled(fixed_retrieval=tuple(int(g) for g in np.flatnonzero(base.mask(0))))
+    chunks = CHUNKS[name]
+    say(f"batched split {name}")
+    ws, kv, pre, dec, total = _batched_run(w, 3, chunks, 2)
+    L = sum(chunks)
+    for b, wb in enumerate(ws):
+        ref = oracle_rows(wb, 0, np.arange(total), total)
+        compare(f"batched split {name} seq {b} prefill", to_f64(pre[b]), ref[:L], TOL["bf16"])
+        compare(f"batched split {name} seq {b} decode", to_f64(dec[b]), ref[L:], TOL["bf16"])
+
+
 def test_llama2_7b_mha_32k_full_attention_layer(torch_cuda):
     """The full-attention baseline on the same kernels (all 32 heads retrieval) at the 32K
     shape: 8 prefill chunks of 4096 and 16 decode steps.  Every decode output is checked;
