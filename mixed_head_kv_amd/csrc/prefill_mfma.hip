@@ -191,14 +191,19 @@ __device__ inline int kind_head(const PrefillArgs& a, bool streaming, int idx, i
 }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+constexpr int kTileBytes = 64 * 128 * 2;   // one 64-key tile of K or of V
+constexpr int kRsrcWord3 = 0x00020000;    // buffer descriptor word 3: 32-bit data format
 
-// Retrieval tiles go HBM -> LDS directly (global_load_lds_dwordx4): each wavefront
+// Retrieval tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds): each wavefront
 // instruction fills one contiguous KB of LDS, lane L writing bytes 16L .. 16L + 15, so
 // no registers hold the tile in flight.  The K KB `inst` holds rows 4 inst .. 4 inst + 3
 // of the swizzled row-major tile, its lane L the chunk (row 4 inst + L/16, physical
 // chunk L mod 16), gathered from the cache's MFMA-ordered 32-key tiles; V's d-major
 // 8-key blocks are copied as they are.  `wave` is uniform; the caller waits (vmcnt)
-// and synchronises before reading.
+// and synchronises before reading.  The buffer form (one descriptor per 16 KB tile)
+// rather than the global one: the compiler counts a global load into LDS as an LDS
+// access as well, and while one is in flight it waits for every outstanding LDS read
+// before each product instead of for the one operand the product needs.
 template <int W>
 __device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb, char* ldsK, char* ldsV, int wave,
                                 int lane, const int (&koff)[Shape<W>::kDma]) {
@@ -206,12 +211,14 @@ __device__ inline void tile_dma(const CacheRegion& c, int64_t cache, int64_t kb,
   // kb and the cache's first row are multiples of 32: the tile's 32-key cache tiles are
   // whole, and each lane's element offset inside them is loop-invariant (koff)
   const uint16_t* Kt = reinterpret_cast<const uint16_t*>(c.k) + ((cache * c.rows + kb) >> 5) * 4096;
-  const char* V = c.v + ((cache * c.rows + kb) * 128) * 2 + wave * (kDma * 1024) + lane * 16;
+  const char* Vt = c.v + ((cache * c.rows + kb) * 128) * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kt), 0, kTileBytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vt), 0, kTileBytes, kRsrcWord3);
 #pragma unroll
   for (int u = 0; u < kDma; ++u) {
     const int inst = wave * kDma + u;
-    __builtin_amdgcn_global_load_lds(Kt + koff[u], (lds_void_ptr)(ldsK + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(V + u * 1024, (lds_void_ptr)(ldsV + inst * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(ldsK + inst * 1024), 16, koff[u] * 2, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(ldsV + inst * 1024), 16, inst * 1024 + lane * 16, 0, 0, 0);
   }
 }
 
