@@ -493,13 +493,21 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
       }
     };
     auto no_mask = [](f32x16&, int) {};
-    int64_t ti = 0;
-    for (; ti < n_inner; ++ti) {
-      const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
-      prefetch(ti);
+    // Tile ti sits in buffer ti & 1.  The unmasked loop takes two tiles per trip with the
+    // buffer a compile-time constant, so each LDS read's buffer offset is an immediate of
+    // the instruction and the per-lane read addresses stay in registers across tiles.
+    auto inner = [&](int64_t t, auto buf) {
+      const char* ldsK = lds + decltype(buf)::value * (kKBytes + kVBytes);
+      prefetch(t);
       tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask);
       __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
+    };
+    int64_t ti = 0;
+    for (; ti + 1 < n_inner; ti += 2) {
+      inner(ti, std::integral_constant<int, 0>());
+      inner(ti + 1, std::integral_constant<int, 1>());
     }
+    if (ti < n_inner) inner(ti++, std::integral_constant<int, 0>());
     for (; ti < ntiles; ++ti) {
       const char* ldsK = lds + (ti & 1) * (kKBytes + kVBytes);
       const int64_t kb = kb_first + ti * kTileKeys;
