@@ -57,9 +57,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest(kernel):
+    """The kernel's source file and the hipcc flags it builds with."""
     import hashlib
+    from mixed_head_kv_amd import build
     path = os.path.join(ROOT, KERNEL_SOURCES[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    flags = " ".join(build.flags_for(os.path.basename(path))).encode()
+    return hashlib.sha256(open(path, "rb").read() + b"\0" + flags).hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):

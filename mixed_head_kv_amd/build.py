@@ -35,6 +35,19 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source additions.  The pre-filling kernel computes with finite values or -inf only
+# (scores, running maxima, weights), so it builds without NaN semantics: its maxima then
+# need no quieting of their inputs (5 fewer VALU instructions per 64-key tile).
+FILE_FLAGS = {
+    "prefill_mfma.hip": ["-fno-honor-nans"],
+}
+
+
+def flags_for(src: str) -> list:
+    """hipcc flags for one source file."""
+    return HIP_FLAGS + FILE_FLAGS.get(src, [])
+
+
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     return p
@@ -50,7 +63,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags_for(src), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

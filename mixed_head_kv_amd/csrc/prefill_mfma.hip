@@ -279,6 +279,13 @@ __device__ inline void mask_block(f32x16& s, int64_t base, int64_t i_pos, int ha
     }
 }
 
+// Work a tile routine issues right after its first K reads (the next tile's loads into
+// LDS in the unmasked loop, whose ~30 issue instructions then cover the reads' latency
+// instead of delaying them).
+struct NoIssue {
+  __device__ void operator()() const {}
+};
+
 // One 64-key tile for the wavefront's 32 queries.  Both 32-key score blocks are formed
 // first (the second block's MFMAs run while the first block's maximum is taken), the
 // scores outside the mask are set to -inf in place when the tile needs it (`mask`, a uniform
@@ -288,16 +295,20 @@ __device__ inline void mask_block(f32x16& s, int64_t base, int64_t i_pos, int ha
 // cores work at the same time.  The running max m may lag the true one by up to kSlack
 // (log2 units): weights are then at most 2^kSlack, harmless in fp32 and bf16, and the
 // rescale (which touches all of O) runs only when some lane's max outgrows m + kSlack.
-template <typename MaskFn>
+// `issue` runs once the K reads of the first score block are issued.
+template <typename MaskFn, typename IssueFn = NoIssue>
 __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
                                              f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half,
-                                             bool masked, const MaskFn& mask) {
+                                             bool masked, const MaskFn& mask, const IssueFn& issue = IssueFn()) {
   const int pk = k_perm(col);
   const int sw = pk & 15;  // row swizzle (rows pk and 32 + pk share it)
   u32x4 kop[8];
 #pragma unroll
   for (int st = 0; st < 8; ++st)
     kop[st] = *reinterpret_cast<const u32x4*>(ldsK + pk * 256 + (((8 * half + st) ^ sw) * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  issue();
+  __builtin_amdgcn_sched_barrier(0);
   set_priority<1>();
   f32x16 s0 = {}, s1 = {};
 #pragma unroll
@@ -498,8 +509,7 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
     // the instruction and the per-lane read addresses stay in registers across tiles.
     auto inner = [&](int64_t t, auto buf) {
       const char* ldsK = lds + decltype(buf)::value * (kKBytes + kVBytes);
-      prefetch(t);
-      tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask);
+      tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask, [&] { prefetch(t); });
       __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
     };
     int64_t ti = 0;
