@@ -34,6 +34,16 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Largest x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows holding one
+// query's scores), by two register swaps (v_permlane16_swap: rows 0 <-> 1 and 2 <-> 3;
+// v_permlane32_swap: the wavefront's halves) instead of two LDS permutes and their waits.
+__device__ inline float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Two floats to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
@@ -251,8 +261,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma(Geom g, LayerView lv, Decod
       float mx = sc[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      mx = max_over_rows(mx) * sl2;
       const float mn = fmaxf(m, mx);
       const float mref = mn == kNegInf ? 0.0f : mn;
       if (__ballot(mn > m)) {  // some lane's max moved: rescale (alpha is exactly 1 elsewhere)
@@ -496,8 +505,7 @@ __global__ void __launch_bounds__(512) k_decode_mfma_int4(Geom g, LayerView lv, 
       float mx = sc[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      mx = max_over_rows(mx) * sl2;
       const float mn = fmaxf(m, mx);
       const float mref = mn == kNegInf ? 0.0f : mn;
       if (__ballot(mn > m)) {
