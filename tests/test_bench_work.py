@@ -71,3 +71,17 @@ def test_launch_kinds_follow_the_prefill_grid_rules():
     assert bench.launch_kind(main, (512 + 256) * 512, "llama3_8b_gqa_128k") == "prefill_attention"
     assert bench.launch_kind("duo::k_decode_mfma(args)", 1, "llama3_8b_gqa_128k") == "decode_attention"
     assert bench.launch_kind("duo::k_synth<1>(args)", 1, "llama3_8b_gqa_128k") is None
+
+
+def test_traffic_digest_covers_source_and_build_flags(monkeypatch):
+    """Stored HBM traffic counts for a kernel only while both its source file and the hipcc
+    flags that file builds with are unchanged."""
+    from mixed_head_kv_amd import build
+    before = bench.source_digest("prefill_attention")
+    assert before == bench.source_digest("prefill_attention")
+    assert "-fno-honor-nans" in build.flags_for("prefill_mfma.hip")
+    assert "-fno-honor-nans" not in build.flags_for("decode_mfma.hip")
+    monkeypatch.setitem(build.FILE_FLAGS, "prefill_mfma.hip", [])
+    assert bench.source_digest("prefill_attention") != before
+    monkeypatch.undo()
+    assert bench.source_digest("prefill_attention") == before
