@@ -71,16 +71,20 @@ __device__ inline float sum_bf16_pair(uint32_t pair, float acc) {
 
 constexpr float kSlack = 8.0f;  // log2 units
 
-// Wavefront issue priority (s_setprio) around the MFMA sections of the tile routine: of
-// the two wavefronts sharing a SIMD, the one with matrix work ready issues it first and
-// the other fills the cycles between with its softmax, so the matrix pipe idles less
-// (measured 7-10% off the retrieval prefill).  The scheduling barriers keep the compiler
-// from moving instructions across the change.
-template <int P>
+// Wavefront issue priority (s_setprio) around the MFMA sections of the tile routine, in
+// 4-wavefront workgroups (two per CU): of the two wavefronts sharing a SIMD, the one with
+// matrix work ready issues it first and the other fills the cycles between with its
+// softmax, so the matrix pipe idles less (measured 7-10% off the retrieval prefill).  The
+// scheduling barriers keep the compiler from moving instructions across the change.  In
+// 8-wavefront workgroups the two wavefronts of a SIMD meet at every tile's barrier and
+// the raise, with the scheduling fences it needs, measured ~1% slower: none there.
+template <int P, bool kOn>
 __device__ inline void set_priority() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(P);
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kOn) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(P);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // max(x of this lane, x of lane ^ 32): one v_permlane32_swap instead of an LDS permute.
@@ -295,8 +299,9 @@ struct NoIssue {
 // cores work at the same time.  The running max m may lag the true one by up to kSlack
 // (log2 units): weights are then at most 2^kSlack, harmless in fp32 and bf16, and the
 // rescale (which touches all of O) runs only when some lane's max outgrows m + kSlack.
-// `issue` runs once the K reads of the first score block are issued.
-template <typename MaskFn, typename IssueFn = NoIssue>
+// `issue` runs once the K reads of the first score block are issued; kPrio selects the
+// issue-priority raises around the MFMA sections.
+template <bool kPrio, typename MaskFn, typename IssueFn = NoIssue>
 __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV, const u32x4 (&qop)[8],
                                              f32x16 (&o)[4], float& m, float& l, float sl2, int col, int half,
                                              bool masked, const MaskFn& mask, const IssueFn& issue = IssueFn()) {
@@ -309,7 +314,7 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   __builtin_amdgcn_sched_barrier(0);
   issue();
   __builtin_amdgcn_sched_barrier(0);
-  set_priority<1>();
+  set_priority<1, kPrio>();
   f32x16 s0 = {}, s1 = {};
 #pragma unroll
   for (int st = 0; st < 8; ++st) s0 = mfma32(kop[st], qop[st], s0);
@@ -324,7 +329,7 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < 8; ++st) s1 = mfma32(kop[st], qop[st], s1);
-  set_priority<0>();
+  set_priority<0, kPrio>();
   if (masked) {  // mask(s, off): scores of the 32-key block at tile offset off
     mask(s0, 0);
     mask(s1, 32);
@@ -351,7 +356,7 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
     for (int w = 0; w < 4; ++w) l = sum_bf16_pair(out[w], l);
   };
   probs(s0, 0, pb[0]);
-  set_priority<1>();
+  set_priority<1, kPrio>();
 #pragma unroll
   for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[jd], pb[0], o[jd]);
   probs(s0, 1, pb[1]);
@@ -387,7 +392,7 @@ __device__ __forceinline__ void tile_compute(const char* ldsK, const char* ldsV,
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int jd = 0; jd < 4; ++jd) o[jd] = mfma32(v0[4 + jd], pb[3], o[jd]);
-  set_priority<0>();
+  set_priority<0, kPrio>();
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (id mod 8), each XCD with its own
@@ -509,7 +514,7 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
     // the instruction and the per-lane read addresses stay in registers across tiles.
     auto inner = [&](int64_t t, auto buf) {
       const char* ldsK = lds + decltype(buf)::value * (kKBytes + kVBytes);
-      tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask, [&] { prefetch(t); });
+      tile_compute<W == 4>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, false, no_mask, [&] { prefetch(t); });
       __syncthreads();  // (waits for this wavefront's tile loads, LDS ones included)
     };
     int64_t ti = 0;
@@ -524,7 +529,7 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
       prefetch(ti);
       if (kb <= wave_q_hi) {  // (a tile wholly after the wavefront's queries is skipped)
         const bool inside = kb + kTileKeys - 1 <= wave_q_lo;  // every key visible to every query
-        tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !inside, [&](f32x16& sc, int off) {
+        tile_compute<W == 4>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !inside, [&](f32x16& sc, int off) {
           mask_block<kMaskCausal>(sc, kb + off, i_pos, half, 0, 0);
         });
       }
@@ -572,7 +577,7 @@ __global__ void __launch_bounds__(Shape<W>::kThreads, 8 / W) k_prefill_mfma(Pref
         full = p >= S && p_last <= wave_q_lo && p > wave_q_hi - R;
       }
       if (live && any)
-        tile_compute(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !full, [&](f32x16& sc, int off) {
+        tile_compute<W == 4>(ldsK, ldsK + kKBytes, qop, o, m, l, sl2, col, half, !full, [&](f32x16& sc, int off) {
           if (sink)
             mask_block<kMaskSink>(sc, p + off, i_pos, half, S, R);
           else
