@@ -291,12 +291,12 @@ struct NoIssue {
 };
 
 // One 64-key tile for the wavefront's 32 queries.  Both 32-key score blocks are formed
-// first (the second block's MFMAs run while the first block's maximum is taken), the
-// scores outside the mask are set to -inf in place when the tile needs it (`mask`, a uniform
-// branch that touches only the score registers, so O stays in one register set), one
-// running-max update serves the tile, and the exponentials of the second block are
-// issued between the MFMAs of the first block's P*V, so the vector ALU and the matrix
-// cores work at the same time.  The running max m may lag the true one by up to kSlack
+// first (16 MFMAs, the second block's K operands read while the first block's products
+// run), the scores outside the mask are set to -inf in place when the tile needs it
+// (`mask`, a uniform branch that touches only the score registers, so O stays in one
+// register set), one running-max update serves the tile, and the probabilities are formed
+// in four quarter steps of 8 keys per lane, each issued between the P*V MFMAs of the
+// quarter before, so the vector ALU and the matrix cores work at the same time.  The running max m may lag the true one by up to kSlack
 // (log2 units): weights are then at most 2^kSlack, harmless in fp32 and bf16, and the
 // rescale (which touches all of O) runs only when some lane's max outgrows m + kSlack.
 // `issue` runs once the K reads of the first score block are issued; kPrio selects the
