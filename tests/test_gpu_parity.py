@@ -965,6 +965,21 @@ def test_wide_query_groups_match_oracle(torch_cuda, G):
             compare(f"G={G} {fmt} decode", to_f64(dec), ref, TOL["bf16"])
 
 
+def test_wide_query_groups_over_long_split_chunks(torch_cuda):
+    """8 query heads per KV head (two 4-head groups per KV head in 8-wavefront prefill
+    workgroups, both groups' blocks dispatched to one XCD) over chunks of 4096 and 2048
+    tokens, whose query blocks split their keys over two workgroups: every prefill row and
+    decode step of every head against the oracle."""
+    w = W("group8_long", 68, 16, 2, 128, "bf16", 64, 256, 6144 + 4, 4, 1, fixed=(0,))
+    chunks = [4096, 2048]
+    say("group 8 long split chunks")
+    kv, pre, dec, total = run_layer(w, chunks, w.decode_steps)
+    L = sum(chunks)
+    ref = oracle_rows_threaded(w, 0, np.arange(total), total)
+    compare("G=8 long prefill (every row)", to_f64(pre), ref[:L], TOL["bf16"])
+    compare("G=8 long decode", to_f64(dec), ref[L:], TOL["bf16"])
+
+
 @pytest.mark.parametrize("name", ["mha64_bf16", "gqa64x2_f32_d64"])
 def test_most_kv_heads_match_oracle(torch_cuda, name):
     """The largest head count the library accepts (64 KV heads): a bf16 MHA layer whose
